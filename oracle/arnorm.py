@@ -70,13 +70,19 @@ def rms_norm(x, gamma, eps):
     """x * w / sqrt(mean(x^2) + eps) per row, float64, one BF16 rounding at the end.
 
     x: uint16 [M, 7168]; gamma: uint16 [7168]; eps: the FP32 value of the argument.
+    The page accumulates the sum of squares in FP32, so a total beyond the FP32 range
+    is +inf there (rstd = 0: out is +-0, or NaN where x is infinite); the float64 total
+    is taken through float32 to keep that range, which changes no finite total by more
+    than half an FP32 ulp.
     """
     v = widen(x).astype(np.float64)
     g = widen(gamma).astype(np.float64)
     e = float(np.float32(eps))
-    total = np.sum(v * v, axis=-1, keepdims=True)  # squares of BF16 values are exact
-    rstd = 1.0 / np.sqrt(total / HIDDEN + e)
-    return round_to_bf16(v * rstd * g)
+    with np.errstate(over="ignore", invalid="ignore"):
+        total = np.sum(v * v, axis=-1, keepdims=True)  # squares of BF16 values are exact
+        total = total.astype(np.float32).astype(np.float64)  # the FP32 range of the page's sum
+        rstd = 1.0 / np.sqrt(total / HIDDEN + e)
+        return round_to_bf16(v * rstd * g)
 
 
 def arnorm_rows(slot_words, residual, gamma, eps):

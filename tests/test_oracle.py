@@ -250,6 +250,24 @@ def check_norm_closed_forms(norm_fn):
     assert np.all(got == want), (hex(int(got[0])), hex(want))
 
 
+def check_norm_fp32_range(norm_fn):
+    """The page's FP32 sum of squares: a row whose total exceeds the FP32 range has
+    rstd = 0, so finite values give +-0 and infinite values NaN."""
+    one = np.full(W, 0x3F80, dtype=np.uint16)
+    big = np.full((1, W), 0x7F00, dtype=np.uint16)  # 2^127: squares overflow FP32
+    big[0, 1::2] = 0xFF00  # -2^127
+    got = np.asarray(norm_fn(big, one, 1e-6))[0]
+    assert np.all((got & 0x7FFF) == 0), hex(int(got[0]))
+    assert np.all(got[1::2] == 0x8000) and np.all(got[0::2] == 0x0000)
+    inf = big.copy()
+    inf[0, 5] = 0x7F80
+    got = np.asarray(norm_fn(inf, one, 1e-6))[0]
+    assert (int(got[5]) & 0x7F80) == 0x7F80 and (int(got[5]) & 0x7F) != 0  # NaN
+    # inside the range nothing changes: 2^50 everywhere (total 7168 * 2^100) gives 1.0
+    mid = np.full((1, W), 0x5880, dtype=np.uint16)
+    assert np.all(np.asarray(norm_fn(mid, one, 1e-6)) == 0x3F80)
+
+
 def check_norm_random_rows(norm_fn):
     rng = np.random.default_rng(16)
     for sigma in (1.0, 0.02):
@@ -351,6 +369,10 @@ def test_residual_add():
 
 def test_norm_closed_forms():
     check_norm_closed_forms(oar.rms_norm)
+
+
+def test_norm_fp32_range():
+    check_norm_fp32_range(oar.rms_norm)
 
 
 def test_norm_random_rows():
@@ -460,6 +482,13 @@ def _mut_norm_wrong_width(x, gamma, eps):
     return obf.round_to_bf16(v * rstd * g)
 
 
+def _mut_norm_f64_range(x, gamma, eps):
+    v = obf.widen(x).astype(np.float64)
+    g = obf.widen(gamma).astype(np.float64)
+    rstd = 1.0 / np.sqrt(np.sum(v * v, axis=-1, keepdims=True) / 7168 + float(np.float32(eps)))
+    return obf.round_to_bf16(v * rstd * g)
+
+
 def _mut_residual_double_round(r, c):
     if c is None:
         return np.asarray(r).copy()
@@ -530,6 +559,7 @@ MUTANTS = {
     "norm sum not mean": lambda: check_norm_closed_forms(_mut_norm_sum_not_mean),
     "norm without gamma": lambda: check_norm_random_rows(_mut_norm_no_gamma),
     "norm over 7167": lambda: check_norm_random_rows(_mut_norm_wrong_width),
+    "norm sum in float64 range": lambda: check_norm_fp32_range(_mut_norm_f64_range),
     "residual truncated": lambda: check_residual_add(_mut_residual_double_round),
     "gather keeps rows": lambda: check_gather(oga.gather_push, _gather_poll_no_rearm),
     "gather no clean": lambda: check_gather(_gather_push_no_clean, oga.gather_poll),
