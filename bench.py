@@ -1,0 +1,267 @@
+#!/usr/bin/env python3
+"""Benchmark of the Lamport-mailbox ArNorm on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+One step = one ArNorm call of the one-GPU stand-in at TP=8, M=4 (the embedding
+call: residual = AR(x)): arnorm_push of the 8 ranks' partial rows, then
+arnorm_reduce_norm (poll, re-arm, rank-order sum, RMSNorm), alternating the two
+layer parities.  The calls are captured in HIP graphs and replayed; K steps are timed
+between two device synchronizations, inputs already resident in HBM.
+
+The same JSON line carries:
+  roofline      the consumer kernel at TP=8, M=4096 with residual (the HBM-bound
+                workload): algorithmic bytes per launch / its average duration, HIP
+                events around each launch on the stream it runs on, against 8 TB/s
+  push          the producer kernel at the same size, same method
+  cpu_baseline  the CPU oracle timed on the same TP=8, M=4 call on this host
+Prints exactly one JSON line (rank 0, one GPU).
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HIDDEN = 7168
+ROW_BYTES = HIDDEN * 2
+PEAK_HBM_GBPS = 8000.0
+EPS = 1e-6
+METRIC = "ArNorm µs/call at TP=8 M=4; HBM GB/s (fraction of peak) at M=4096"
+
+
+def reduce_bytes(tp, m, residual):
+    """Algorithmic bytes of one arnorm_reduce_norm launch: TP slot reads, residual,
+    gamma, out + residual_out, TP slot re-arm writes."""
+    return tp * m * ROW_BYTES + (m * ROW_BYTES if residual else 0) + ROW_BYTES + 2 * m * ROW_BYTES \
+        + tp * m * ROW_BYTES
+
+
+def push_bytes(nslots, m):
+    return 2 * nslots * m * ROW_BYTES
+
+
+def kernel_sources_hash():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "tp_all_reduce_arnorm_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + f.read())
+    return h.hexdigest()[:16]
+
+
+def committed_traffic(kernel_key):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or None when
+    there is none or the kernel sources changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    entry = rec.get(kernel_key)
+    if not entry or entry.get("sources_sha") != kernel_sources_hash():
+        return None
+    return entry.get("bytes_per_launch")
+
+
+def time_latency(lib, torch, steps, warmup, chunk=50):
+    """µs per stand-in call at TP=8, M=4 (no residual), graph-replayed."""
+    from tp_all_reduce_arnorm_amd import workloads as wl
+
+    cfg = wl.CONFIGS["c2"]
+    src = wl.ArNormInputs(cfg)
+    box = torch.empty((2, cfg.tp, cfg.cap, HIDDEN // 2), dtype=torch.int32, device="cuda")
+    assert lib.lamport_arm(box) is True
+    parts = [torch.from_numpy(src.partials().view(np.int16)).cuda() for _ in range(2)]
+    gamma = torch.from_numpy(src.gamma.view(np.int16)).cuda()
+    outs = [(torch.empty((cfg.m, HIDDEN), dtype=torch.int16, device="cuda"),
+             torch.empty((cfg.m, HIDDEN), dtype=torch.int16, device="cuda")) for _ in range(2)]
+
+    def call(i):
+        parity = i % 2
+        assert lib.arnorm_push(parts[parity], box, parity, 0) is True
+        assert lib.arnorm_reduce_norm(None, gamma, box, parity, EPS, outs[parity][0], outs[parity][1]) is True
+
+    def capture(n):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(n):
+                call(i)
+        return g
+
+    # eager warmup (also loads the kernels), then graphs of `chunk` calls (even: parities alternate)
+    for i in range(4):
+        call(i)
+    torch.cuda.synchronize()
+    chunk = max(2, min(chunk, steps) // 2 * 2)
+    g_main = capture(chunk)
+    rem = steps % chunk
+    g_rem = capture(rem) if rem else None
+    for _ in range(max(1, warmup // chunk)):
+        g_main.replay()
+    torch.cuda.synchronize()
+    reps = steps // chunk
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        g_main.replay()
+    if g_rem is not None:
+        g_rem.replay()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    assert lib.status() == lib.OK
+
+    # the consumer kernel alone at this size: events around eager launches
+    evs = []
+    for i in range(200):
+        parity = i % 2
+        assert lib.arnorm_push(parts[parity], box, parity, 0) is True
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        assert lib.arnorm_reduce_norm(None, gamma, box, parity, EPS, outs[parity][0], outs[parity][1]) is True
+        e1.record()
+        evs.append((e0, e1))
+    torch.cuda.synchronize()
+    kern_us = float(np.median([a.elapsed_time(b) for a, b in evs[20:]])) * 1e3
+    return elapsed, kern_us
+
+
+def time_roofline(lib, torch, launches=20):
+    """Consumer and producer kernels at TP=8, M=4096 with residual."""
+    from tp_all_reduce_arnorm_amd import workloads as wl
+
+    cfg = wl.CONFIGS["c5"]
+    src = wl.ArNormInputs(cfg)
+    p, r = src.call()
+    box = torch.empty((1, cfg.tp, cfg.cap, HIDDEN // 2), dtype=torch.int32, device="cuda")
+    assert lib.lamport_arm(box) is True
+    p_d = torch.from_numpy(p.view(np.int16)).cuda()
+    r_d = torch.from_numpy(r.view(np.int16)).cuda()
+    g_d = torch.from_numpy(src.gamma.view(np.int16)).cuda()
+    del p, r
+    out = torch.empty((cfg.m, HIDDEN), dtype=torch.int16, device="cuda")
+    rout = torch.empty((cfg.m, HIDDEN), dtype=torch.int16, device="cuda")
+    red, push = [], []
+    for i in range(launches + 3):
+        a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        b0, b1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a0.record()
+        assert lib.arnorm_push(p_d, box, 0, 0) is True
+        a1.record()
+        b0.record()
+        assert lib.arnorm_reduce_norm(r_d, g_d, box, 0, EPS, out, rout) is True
+        b1.record()
+        if i >= 3:
+            push.append((a0, a1))
+            red.append((b0, b1))
+    torch.cuda.synchronize()
+    assert lib.status() == lib.OK
+    red_us = float(np.mean([a.elapsed_time(b) for a, b in red])) * 1e3
+    push_us = float(np.mean([a.elapsed_time(b) for a, b in push])) * 1e3
+    return cfg, red_us, push_us
+
+
+def cpu_baseline(budget_s=10.0):
+    """The oracle (numpy, one thread) on the TP=8, M=4 stand-in call: push of 8 slots +
+    poll / re-arm / reduce / norm, fresh partials each call."""
+    import oracle
+    from tp_all_reduce_arnorm_amd import workloads as wl
+
+    cfg = wl.CONFIGS["c2"]
+    src = wl.ArNormInputs(cfg)
+    box = oracle.arm(np.empty((2, cfg.tp, cfg.cap, HIDDEN // 2), dtype=np.uint32))
+    inputs = [src.partials() for _ in range(8)]
+    times = []
+    start = time.perf_counter()
+    i = 0
+    while time.perf_counter() - start < budget_s:
+        p = inputs[i % len(inputs)]
+        parity = i % 2
+        t0 = time.perf_counter()
+        oracle.arnorm_push(box, p, parity, 0)
+        oracle.arnorm_reduce_norm(box, parity, cfg.m, None, src.gamma, EPS)
+        times.append(time.perf_counter() - t0)
+        i += 1
+    return float(np.median(times)) * 1e6, len(times)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--warmup", type=int, default=200)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this benchmark runs on one GPU; the TP ranks are mailbox slots of "
+              f"one MI355X (--gpus {args.gpus} is not supported)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from tp_all_reduce_arnorm_amd import _lib as lib
+
+    torch.cuda.set_device(0)
+    elapsed, kern_us = time_latency(lib, torch, args.steps, args.warmup)
+    cfg5, red_us, push_us = time_roofline(lib, torch)
+    rb = reduce_bytes(cfg5.tp, cfg5.m, True)
+    pb = push_bytes(cfg5.tp, cfg5.m)
+    achieved = rb / (red_us * 1e-6) / 1e9
+    traffic = committed_traffic("reduce_norm_tp8_m4096_res")
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu_us, n = cpu_baseline(args.cpu_seconds)
+        cpu = {"value": round(cpu_us, 1), "unit": "µs/call", "cores": 1, "kind": "oracle",
+               "sample": f"{n} oracle calls (push of 8 slots + reduce_norm) at TP=8, M=4, no residual; "
+                         f"median; {os.cpu_count()} host CPUs visible, numpy on one thread"}
+    us_per_call = elapsed / args.steps * 1e6
+    rec = {
+        "metric": METRIC,
+        "value": round(us_per_call, 3),
+        "unit": "µs/call",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(elapsed / args.steps * 1e3, 6),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "ArNorm TP=8 M=4 width 7168, residual=False, 2 parities alternating "
+                        "(arnorm_push of 8 slots + arnorm_reduce_norm per call, HIP-graph replay)",
+            "tp": 8, "m": 4, "hidden": HIDDEN, "parities": 2, "residual": False,
+            "reduce_norm_kernel_us": round(kern_us, 3),
+        },
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": PEAK_HBM_GBPS,
+            "unit": "GB/s",
+            "frac": round(achieved / PEAK_HBM_GBPS, 4),
+            "traffic": traffic,
+            "kernel": "arnorm_reduce_norm",
+            "workload": "ArNorm TP=8 M=4096 width 7168, residual=True",
+            "algorithmic_bytes": rb,
+            "kernel_us": round(red_us, 2),
+        },
+        "push": {
+            "kernel": "arnorm_push", "workload": "8 slots, M=4096", "algorithmic_bytes": pb,
+            "kernel_us": round(push_us, 2), "achieved_gbps": round(pb / (push_us * 1e-6) / 1e9, 1),
+            "frac": round(pb / (push_us * 1e-6) / 1e9 / PEAK_HBM_GBPS, 4),
+        },
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

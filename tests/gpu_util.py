@@ -1,0 +1,77 @@
+"""Helpers for the GPU parity tests: host <-> device copies of bit patterns and the
+comparison contract (bit-exact words; `out` within one BF16 ulp of the oracle)."""
+
+import sys
+
+import numpy as np
+
+import oracle
+
+S0 = 0x80000000
+W = 7168
+
+
+def say(*a):
+    """Name the case before a GPU step (flushed, so a fault still leaves the name)."""
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def dev16(a):
+    import torch
+
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.uint16).view(np.int16)).to("cuda")
+
+
+def dev32(a):
+    import torch
+
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.uint32).view(np.int32)).to("cuda")
+
+
+def host16(t):
+    return t.cpu().numpy().view(np.uint16)
+
+
+def host32(t):
+    return t.cpu().numpy().view(np.uint32)
+
+
+def empty16(shape):
+    import torch
+
+    return torch.empty(shape, dtype=torch.int16, device="cuda")
+
+
+def armed_box(shape):
+    """A device mailbox filled with the sentinel by the library's own lamport_arm."""
+    import torch
+    from tp_all_reduce_arnorm_amd import _lib
+
+    box = torch.empty(shape, dtype=torch.int32, device="cuda")
+    assert _lib.lamport_arm(box) is True
+    return box
+
+
+def assert_bits_equal(got, want, what):
+    got = np.asarray(got)
+    want = np.asarray(want)
+    assert got.shape == want.shape, (what, got.shape, want.shape)
+    bad = np.argwhere(got != want)
+    if bad.size:
+        i = tuple(bad[0])
+        raise AssertionError(f"{what}: {len(bad)} mismatches, first at {i}: got {int(got[i]):#x}, "
+                             f"want {int(want[i]):#x}")
+
+
+def assert_out_close(got, want, what="out"):
+    """|gpu - oracle| <= 2^-7 |oracle| elementwise (<= 1 BF16 ulp); zero exactly zero;
+    infinities equal; NaN where the oracle has NaN (any NaN pattern)."""
+    g = oracle.widen(got).astype(np.float64)
+    w = oracle.widen(want).astype(np.float64)
+    with np.errstate(invalid="ignore"):
+        ok = (np.abs(g - w) <= 2.0**-7 * np.abs(w)) | (g == w) | (np.isnan(g) & np.isnan(w))
+    if not ok.all():
+        i = tuple(np.argwhere(~ok)[0])
+        raise AssertionError(f"{what}: {(~ok).sum()} outside 1 ulp, first at {i}: got {g[i]!r} "
+                             f"({int(np.asarray(got)[i]):#06x}), want {w[i]!r} ({int(np.asarray(want)[i]):#06x})")

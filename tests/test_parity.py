@@ -1,0 +1,296 @@
+"""GPU parity: the HIP path, called through the C ABI, against the CPU oracle on the
+same seeded inputs.  Bit-exact: residual_out (the all-reduced row when there is no
+residual), every gathered word, and the mailbox after every call.  out: within one
+BF16 ulp.  Sizes: the five workloads (c1..c5, c5 on sampled rows), plus edge cases."""
+
+import numpy as np
+import pytest
+
+import oracle
+from tests.gpu_util import (S0, W, armed_box, assert_bits_equal, assert_out_close, dev16, dev32, empty16,
+                            host16, host32, say)
+from tp_all_reduce_arnorm_amd import workloads as wl
+
+pytestmark = pytest.mark.gpu
+EPS = 1e-6
+
+
+@pytest.fixture(autouse=True)
+def _defaults(lib):
+    lib.set_reduce_threads(0)
+    yield
+    lib.set_reduce_threads(0)
+
+
+def run_call(lib, box_d, box_h, partials, residual, gamma_d, gamma, parity, eps=EPS, pushes=None,
+             fused_rank=None):
+    """One ArNorm call on both sides: pushes (list of (rank, nslots)), then the
+    consumer; returns after comparing outputs and the whole mailbox."""
+    tp = partials.shape[0]
+    m = partials.shape[1]
+    pushes = pushes or [(0, tp)]
+    for rank, n in pushes:
+        assert lib.arnorm_push(dev16(partials[rank:rank + n]), box_d, parity, rank) is True
+        oracle.arnorm_push(box_h, partials[rank:rank + n], parity, rank)
+    out_d, rout_d = empty16((m, W)), empty16((m, W))
+    res_d = dev16(residual) if residual is not None else None
+    part_d = dev16(partials[fused_rank]) if fused_rank is not None else None
+    assert lib.arnorm_reduce_norm(res_d, gamma_d, box_d, parity, eps, out_d, rout_d, partial=part_d,
+                                  rank=fused_rank or 0) is True
+    want_out, want_res = oracle.arnorm_reduce_norm(
+        box_h, parity, m, residual, gamma, eps,
+        partial=partials[fused_rank] if fused_rank is not None else None, rank=fused_rank or 0)
+    got_res = host16(rout_d)
+    assert_bits_equal(got_res, want_res, "residual_out")
+    assert_out_close(host16(out_d), want_out)
+    assert_bits_equal(host32(box_d), box_h, "mailbox")
+    assert lib.status() == lib.OK
+    return got_res
+
+
+def run_config(lib, name, calls=None, threads=0):
+    cfg = wl.CONFIGS[name]
+    say(f"[parity] {name} threads={threads}")
+    lib.set_reduce_threads(threads)
+    src = wl.ArNormInputs(cfg)
+    shape = (cfg.parities, cfg.tp, cfg.cap, W // 2)
+    box_d = armed_box(shape)
+    box_h = oracle.arm(np.empty(shape, dtype=np.uint32))
+    gamma_d = dev16(src.gamma)
+    for call in range(calls or cfg.calls):
+        p, r = src.call()
+        run_call(lib, box_d, box_h, p, r, gamma_d, src.gamma, call % cfg.parities)
+
+
+def test_c1(lib):
+    run_config(lib, "c1")
+
+
+def test_c2(lib):
+    run_config(lib, "c2")
+
+
+def test_c3(lib):
+    run_config(lib, "c3")
+
+
+@pytest.mark.parametrize("threads", [448, 256])
+def test_c3_other_workgroup_sizes(lib, threads):
+    run_config(lib, "c3", calls=4, threads=threads)
+
+
+def test_c3_per_rank_pushes_and_chained_residual(lib):
+    """Ranks push one by one (and in groups), and each call's residual is the previous
+    call's residual_out, as consecutive layers use it."""
+    cfg = wl.CONFIGS["c3"]
+    say("[parity] c3 per-rank pushes, chained residual")
+    src = wl.ArNormInputs(cfg)
+    shape = (2, 8, 64, W // 2)
+    box_d, box_h = armed_box(shape), oracle.arm(np.empty(shape, dtype=np.uint32))
+    gamma_d = dev16(src.gamma)
+    residual = src.residual()
+    groupings = [[(k, 1) for k in range(8)], [(0, 3), (3, 5)], [(7, 1), (0, 7)], [(4, 4), (0, 4)]]
+    for call in range(8):
+        p = src.partials()
+        residual = run_call(lib, box_d, box_h, p, residual, gamma_d, src.gamma, call % 2,
+                            pushes=groupings[call % len(groupings)])
+
+
+def test_c4_gather(lib):
+    cfg = wl.CONFIGS["c4"]
+    say("[parity] c4 gather copy / no-copy")
+    shards = wl.gather_shards(cfg)
+    gshape = (cfg.cap, cfg.tp * cfg.s)
+    gbox_d = armed_box(gshape)
+    gbox_h = oracle.arm(np.empty(gshape, dtype=np.uint32))
+    import torch
+
+    for round_ in range(3):
+        # ranks push one by one (round 0), all at once (1), in two groups (2)
+        groups = [[(k, 1) for k in range(8)], [(0, 8)], [(0, 5), (5, 3)]][round_]
+        for rank, n in groups:
+            assert lib.gather_push(dev32(shards[rank:rank + n]), gbox_d, cfg.tp, rank) is True
+            oracle.gather_push(gbox_h, shards[rank:rank + n], rank)
+        assert_bits_equal(host32(gbox_d), gbox_h, "gather mailbox after push")
+        if round_ == 1:
+            # no copy: rows stay published for a later reader, which copies and re-arms
+            assert lib.gather_poll(gbox_d, cfg.tp, cfg.m, copy=False) is True
+            assert oracle.gather_poll(gbox_h, cfg.m, False) is None
+            assert_bits_equal(host32(gbox_d), gbox_h, "gather mailbox after no-copy poll")
+        out_d = torch.empty((cfg.m, cfg.tp * cfg.s), dtype=torch.int32, device="cuda")
+        assert lib.gather_poll(gbox_d, cfg.tp, cfg.m, out=out_d, copy=True) is True
+        want = oracle.gather_poll(gbox_h, cfg.m, True)
+        assert_bits_equal(host32(out_d), want, "gathered words")
+        assert_bits_equal(host32(gbox_d), gbox_h, "gather mailbox after copy")
+        assert lib.status() == lib.OK
+        # the words moved are the shards with only the sentinel pair changed
+        for r in range(cfg.tp):
+            blk = want[:, r * cfg.s:(r + 1) * cfg.s]
+            src = shards[r]
+            assert np.array_equal(blk[src != S0], src[src != S0]) and np.all(blk[src == S0] == 0)
+
+
+def test_c5_full_size_sampled_rows(lib):
+    """M = 4096, TP = 8, in the launch configuration the benchmark times; the oracle
+    checks a sample of rows one by one (rows are independent), and the whole mailbox
+    must be re-armed."""
+    import torch
+
+    cfg = wl.CONFIGS["c5"]
+    say("[parity] c5 full size")
+    src = wl.ArNormInputs(cfg)
+    p, r = src.call()
+    shape = (1, 8, cfg.cap, W // 2)
+    box_d = armed_box(shape)
+    p_d, r_d, g_d = dev16(p), dev16(r), dev16(src.gamma)
+    out_d, rout_d = empty16((cfg.m, W)), empty16((cfg.m, W))
+    assert lib.arnorm_push(p_d, box_d, 0, 0) is True
+    assert lib.arnorm_reduce_norm(r_d, g_d, box_d, 0, EPS, out_d, rout_d) is True
+    assert lib.status() == lib.OK
+    assert bool((box_d == torch.tensor(-(1 << 31), dtype=torch.int32, device="cuda")).all())
+    rng = np.random.default_rng(99)
+    rows = np.unique(np.concatenate([[0, 1, cfg.m - 1], rng.choice(cfg.m, 61, replace=False)]))
+    box_h = oracle.arm(np.empty((1, 8, len(rows), W // 2), dtype=np.uint32))
+    oracle.arnorm_push(box_h, p[:, rows], 0, 0)
+    want_out, want_res = oracle.arnorm_reduce_norm(box_h, 0, len(rows), r[rows], src.gamma, EPS)
+    got_out, got_res = host16(out_d)[rows], host16(rout_d)[rows]
+    assert_bits_equal(got_res, want_res, "residual_out (sampled rows)")
+    assert_out_close(got_out, want_out, "out (sampled rows)")
+    # the same rows through the oracle's stateless path
+    o2, r2 = oracle.arnorm_rows(oracle.clean(oracle.pack_pairs(p[:, rows])), r[rows], src.gamma, EPS)
+    assert np.array_equal(r2, want_res) and np.array_equal(o2, want_out)
+
+
+# -- edge cases ------------------------------------------------------------------
+
+
+def torture_partials(rng, tp, m):
+    """Rows built to hit the rounding and sign corner cases: ties to even, carries into
+    the next binade, cancellation to +-0, BF16 subnormals, overflow to inf, the
+    sentinel pair and other -0 words."""
+    p = np.zeros((tp, m, W), dtype=np.uint16)
+    for r in range(m):
+        kind = r % 6
+        if kind == 0:  # random patterns over a wide exponent range
+            e = rng.integers(-20, 20, size=(tp, W)) + 127
+            p[:, r] = ((rng.integers(0, 2, (tp, W)) << 15) | (e << 7) | rng.integers(0, 128, (tp, W))).astype(np.uint16)
+        elif kind == 1:  # subnormals and signed zeros
+            p[:, r] = ((rng.integers(0, 2, (tp, W)) << 15) | rng.integers(0, 128, (tp, W))).astype(np.uint16)
+        elif kind == 2:  # near-overflow values: sums overflow to +-inf
+            p[:, r] = ((rng.integers(0, 2, (tp, W)) << 15) | (254 << 7) | rng.integers(100, 128, (tp, W))).astype(np.uint16)
+        elif kind == 3:  # exact cancellation: slot 1 = -slot 0, the rest -0
+            x = rng.integers(0, 1 << 15, W).astype(np.uint16) & np.uint16(0x7F7F)
+            p[0, r] = x
+            p[1, r] = x ^ np.uint16(0x8000)
+            p[2:, r] = 0x8000
+        elif kind == 4:  # ties: 1.0 + k * 2^-8 style values per column
+            p[0, r] = 0x3F80
+            p[1, r] = rng.choice([0x3B80, 0x3C40, 0x3BC0, 0x3C00], W)
+            p[2:, r] = rng.choice([0x0000, 0x8000, 0x3300], (tp - 2, W))
+        else:  # the sentinel pair everywhere in some slots, -0 words in others
+            p[:, r] = rng.integers(0, 1 << 16, (tp, W)).astype(np.uint16) & np.uint16(0xBF7F)
+            p[: tp // 2, r, 0::2] = 0x0000
+            p[: tp // 2, r, 1::2] = 0x8000
+            p[tp // 2:, r, 0::4] = 0x8000
+    return p
+
+
+@pytest.mark.parametrize("tp", [2, 3, 4, 5, 6, 7, 8])
+@pytest.mark.parametrize("residual", [False, True])
+def test_all_tp_torture_rows(lib, tp, residual):
+    say(f"[parity] torture tp={tp} residual={residual}")
+    rng = np.random.default_rng(100 + tp)
+    m, cap = 13, 17  # ragged: rows 13..16 of the cap stay untouched
+    shape = (2, tp, cap, W // 2)
+    box_d, box_h = armed_box(shape), oracle.arm(np.empty(shape, dtype=np.uint32))
+    gamma = (rng.integers(0, 2, W) << 15 | (rng.integers(120, 132, W) << 7) | rng.integers(0, 128, W)).astype(np.uint16)
+    g_d = dev16(gamma)
+    # leave the other parity published and unread: it must survive untouched
+    other = torture_partials(rng, tp, m)
+    assert lib.arnorm_push(dev16(other), box_d, 1, 0) is True
+    oracle.arnorm_push(box_h, other, 1, 0)
+    for call in range(2):
+        p = torture_partials(rng, tp, m)
+        res = torture_partials(rng, 1, m)[0] if residual else None
+        run_call(lib, box_d, box_h, p, res, g_d, gamma, 0)
+
+
+@pytest.mark.parametrize("threads", [896, 448, 256])
+def test_norm_closed_form_rows(lib, threads):
+    """All-zero row, one-hot row, constant row, an eps-dominated row and a row whose
+    residual cancels the all-reduced value; tp=4, M=5."""
+    say(f"[parity] closed-form rows threads={threads}")
+    lib.set_reduce_threads(threads)
+    tp, m = 4, 5
+    p = np.zeros((tp, m, W), dtype=np.uint16)
+    p[:, 0] = 0x0000                      # zero row
+    p[0, 1, 123] = 0x3F80                 # one-hot 1.0
+    p[:, 2] = 0x3E80                      # 4 x 0.25 = 1.0 everywhere
+    p[0, 3] = 0x3A80                      # 2^-10 everywhere: mean ~ eps
+    p[:, 4] = 0x3F80                      # 4.0, cancelled by residual -4.0
+    res = np.zeros((m, W), dtype=np.uint16)
+    res[4] = 0xC080
+    gamma = np.full(W, 0x3F80, dtype=np.uint16)
+    shape = (1, tp, m, W // 2)
+    box_d, box_h = armed_box(shape), oracle.arm(np.empty(shape, dtype=np.uint32))
+    got_res = run_call(lib, box_d, box_h, p, res, dev16(gamma), gamma, 0)
+    assert np.all(got_res[4] == 0)
+
+
+@pytest.mark.parametrize("rank", [0, 3, 7])
+def test_fused_own_push(lib, rank):
+    """The one-kernel form: the consumer brings rank `rank`'s row itself."""
+    say(f"[parity] fused own push rank={rank}")
+    cfg = wl.CONFIGS["c3"]
+    src = wl.ArNormInputs(cfg)
+    shape = (2, 8, 64, W // 2)
+    box_d, box_h = armed_box(shape), oracle.arm(np.empty(shape, dtype=np.uint32))
+    g_d = dev16(src.gamma)
+    for call in range(3):
+        p, r = src.call()
+        pushes = [(k, 1) for k in range(8) if k != rank]
+        run_call(lib, box_d, box_h, p, r, g_d, src.gamma, call % 2, pushes=pushes, fused_rank=rank)
+
+
+def test_max_rows_and_single_row(lib):
+    say("[parity] M = cap = 512 and M = 1")
+    rng = np.random.default_rng(5)
+    for m, cap in ((512, 512), (1, 512)):
+        tp = 8
+        p = (rng.standard_normal((tp, m, W), dtype=np.float32).view(np.uint32) >> 16).astype(np.uint16)
+        res = (rng.standard_normal((m, W), dtype=np.float32).view(np.uint32) >> 16).astype(np.uint16)
+        gamma = np.full(W, 0x3F80, dtype=np.uint16)
+        shape = (1, tp, cap, W // 2)
+        box_d, box_h = armed_box(shape), oracle.arm(np.empty(shape, dtype=np.uint32))
+        run_call(lib, box_d, box_h, p, res, dev16(gamma), gamma, 0)
+
+
+def test_in_place_residual(lib):
+    say("[parity] residual_out == residual")
+    cfg = wl.CONFIGS["c3"]
+    src = wl.ArNormInputs(cfg)
+    p, r = src.call()
+    box_d = armed_box((2, 8, 64, W // 2))
+    box_h = oracle.arm(np.empty((2, 8, 64, W // 2), dtype=np.uint32))
+    assert lib.arnorm_push(dev16(p), box_d, 1, 0) is True
+    oracle.arnorm_push(box_h, p, 1, 0)
+    res_d = dev16(r)
+    out_d = empty16((64, W))
+    assert lib.arnorm_reduce_norm(res_d, dev16(src.gamma), box_d, 1, EPS, out_d, res_d) is True
+    want_out, want_res = oracle.arnorm_reduce_norm(box_h, 1, 64, r, src.gamma, EPS)
+    assert_bits_equal(host16(res_d), want_res, "in-place residual_out")
+    assert_out_close(host16(out_d), want_out)
+
+
+def test_not_served_shapes(lib):
+    import torch
+
+    box = armed_box((1, 8, 4, W // 2))
+    p = torch.zeros((8, 5, W), dtype=torch.int16, device="cuda")
+    assert lib.arnorm_push(p, box, 0, 0) is None  # M = 5 > cap = 4
+    box1 = armed_box((1, 1, 4, W // 2))
+    assert lib.arnorm_push(torch.zeros((1, 2, W), dtype=torch.int16, device="cuda"), box1, 0, 0) is None
+    g = armed_box((4, 8 * 6))
+    assert lib.gather_push(torch.zeros((1, 2, 6), dtype=torch.int32, device="cuda"), g, 8, 0) is None
+    with pytest.raises(lib.ArnormError):
+        lib.arnorm_push(torch.zeros((2, 2, W), dtype=torch.int16, device="cuda"), box, 0, 7)

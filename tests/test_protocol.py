@@ -1,0 +1,114 @@
+"""Mailbox protocol on the GPU: bounded polls (a missing push is forced from the host
+with a tiny spin limit, so every kernel still ends), recovery with lamport_arm, and
+the stand-in call sequence captured in a HIP graph and replayed."""
+
+import numpy as np
+import pytest
+
+import oracle
+from tests.gpu_util import (W, armed_box, assert_bits_equal, assert_out_close, dev16, dev32, empty16, host16,
+                            host32, say)
+from tp_all_reduce_arnorm_amd import workloads as wl
+
+pytestmark = pytest.mark.gpu
+EPS = 1e-6
+
+
+@pytest.fixture
+def small_spin(lib):
+    old = lib.get_spin_limit()
+    lib.set_spin_limit(64)
+    yield
+    lib.set_spin_limit(old)
+
+
+def test_missing_push_times_out_and_recovers(lib, small_spin):
+    say("[protocol] arnorm missing push -> timeout -> lamport_arm -> exact")
+    cfg = wl.CONFIGS["c2"]
+    src = wl.ArNormInputs(cfg)
+    shape = (2, 8, 64, W // 2)
+    box_d = armed_box(shape)
+    p, _ = src.call()
+    assert lib.status() == lib.OK
+    assert lib.arnorm_push(dev16(p[:7]), box_d, 0, 0) is True  # rank 7 never pushes
+    out_d, rout_d = empty16((4, W)), empty16((4, W))
+    g_d = dev16(src.gamma)
+    assert lib.arnorm_reduce_norm(None, g_d, box_d, 0, EPS, out_d, rout_d) is True
+    assert lib.status() == lib.TIMEOUT
+    assert lib.status() == lib.OK  # read and cleared
+    # timed-out fragments were not re-armed: slots 0..6 of rows < 4 still hold data
+    assert not np.any(host32(box_d)[0, :7, :4] == 0x80000000)
+    # recovery: re-arm the whole mailbox, then a normal call is exact
+    assert lib.lamport_arm(box_d) is True
+    box_h = oracle.arm(np.empty(shape, dtype=np.uint32))
+    p, _ = src.call()
+    assert lib.arnorm_push(dev16(p), box_d, 1, 0) is True
+    oracle.arnorm_push(box_h, p, 1, 0)
+    assert lib.arnorm_reduce_norm(None, g_d, box_d, 1, EPS, out_d, rout_d) is True
+    want_out, want_res = oracle.arnorm_reduce_norm(box_h, 1, 4, None, src.gamma, EPS)
+    assert lib.status() == lib.OK
+    assert_bits_equal(host16(rout_d), want_res, "residual_out after recovery")
+    assert_out_close(host16(out_d), want_out)
+    assert_bits_equal(host32(box_d), box_h, "mailbox after recovery")
+
+
+def test_gather_missing_push_times_out(lib, small_spin):
+    import torch
+
+    say("[protocol] gather missing push -> timeout -> lamport_arm -> exact")
+    cfg = wl.CONFIGS["c4"]
+    shards = wl.gather_shards(cfg)
+    gshape = (cfg.cap, cfg.tp * cfg.s)
+    gbox_d = armed_box(gshape)
+    assert lib.gather_push(dev32(shards[1:]), gbox_d, cfg.tp, 1) is True  # rank 0 missing
+    out_d = torch.empty((cfg.m, cfg.tp * cfg.s), dtype=torch.int32, device="cuda")
+    assert lib.gather_poll(gbox_d, cfg.tp, cfg.m, out=out_d, copy=True) is True
+    assert lib.status() == lib.TIMEOUT
+    assert lib.lamport_arm(gbox_d) is True
+    gbox_h = oracle.arm(np.empty(gshape, dtype=np.uint32))
+    assert lib.gather_push(dev32(shards), gbox_d, cfg.tp, 0) is True
+    oracle.gather_push(gbox_h, shards, 0)
+    assert lib.gather_poll(gbox_d, cfg.tp, cfg.m, out=out_d, copy=True) is True
+    assert lib.status() == lib.OK
+    assert_bits_equal(host32(out_d), oracle.gather_poll(gbox_h, cfg.m, True), "gathered words")
+    assert_bits_equal(host32(gbox_d), gbox_h, "gather mailbox")
+
+
+def test_graph_replay_alternating_parities(lib):
+    """push + reduce_norm for parity 0, then parity 1, captured once and replayed; every
+    replay (with eager work and synchronizations in between) matches the oracle."""
+    import torch
+
+    say("[protocol] HIP graph replay, c2 shape")
+    cfg = wl.CONFIGS["c2"]
+    src = wl.ArNormInputs(cfg)
+    shape = (2, 8, 64, W // 2)
+    box_d = armed_box(shape)
+    p0, _ = src.call()
+    p1, _ = src.call()
+    p0_d, p1_d, g_d = dev16(p0), dev16(p1), dev16(src.gamma)
+    outs = [(empty16((4, W)), empty16((4, W))) for _ in range(2)]
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for parity, p_d in ((0, p0_d), (1, p1_d)):
+            assert lib.arnorm_push(p_d, box_d, parity, 0) is True
+            assert lib.arnorm_reduce_norm(None, g_d, box_d, parity, EPS, outs[parity][0], outs[parity][1]) is True
+    box_h = oracle.arm(np.empty(shape, dtype=np.uint32))
+    wants = []
+    for parity, p in ((0, p0), (1, p1)):
+        oracle.arnorm_push(box_h, p, parity, 0)
+        wants.append(oracle.arnorm_reduce_norm(box_h, parity, 4, None, src.gamma, EPS))
+    for replay in range(5):
+        for o, r in outs:
+            o.fill_(0)
+            r.fill_(0)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for parity in (0, 1):
+            assert_bits_equal(host16(outs[parity][1]), wants[parity][1], f"replay {replay} residual_out")
+            assert_out_close(host16(outs[parity][0]), wants[parity][0], f"replay {replay} out")
+        assert_bits_equal(host32(box_d), box_h, f"replay {replay} mailbox")
+        _ = torch.ones(1024, device="cuda").sum().item()  # eager work between replays
+    assert lib.status() == lib.OK

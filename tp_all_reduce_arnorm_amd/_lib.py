@@ -1,0 +1,154 @@
+"""ctypes binding of libarnorm.so (include/arnorm.h), with the same entry-point names.
+
+Argument marshalling only: torch tensors become device pointers and sizes, the
+stream becomes torch's current HIP stream, return codes become None (NOT_SERVED,
+the pages' "shape not served" answer) or an exception.  Every step of the method
+runs in the HIP kernels of the library; importing this module fails loudly when the
+library is not built.
+"""
+
+import ctypes
+import os
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libarnorm.so")
+
+OK, NOT_SERVED, BAD_ARG, HIP_ERROR, TIMEOUT = 0, 1, 2, 3, 4
+SENTINEL = 0x80000000
+HIDDEN = 7168
+ROW_WORDS = 3584
+
+_c_int, _c_ptr, _c_size, _c_u32, _c_u64, _c_float = (
+    ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_uint32, ctypes.c_uint64, ctypes.c_float)
+
+_SIGNATURES = {
+    "lamport_arm": (_c_int, [_c_ptr, _c_size, _c_u32, _c_ptr]),
+    "arnorm_push": (_c_int, [_c_ptr, _c_ptr, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_ptr]),
+    "arnorm_reduce_norm": (_c_int, [_c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_int, _c_int, _c_int,
+                                    _c_int, _c_int, _c_int, _c_float, _c_ptr]),
+    "gather_push": (_c_int, [_c_ptr, _c_ptr, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_ptr]),
+    "gather_poll": (_c_int, [_c_ptr, _c_ptr, _c_int, _c_int, _c_int, _c_int, _c_int, _c_ptr]),
+    "arnorm_set_spin_limit": (_c_int, [_c_u64]),
+    "arnorm_get_spin_limit": (_c_u64, []),
+    "arnorm_set_reduce_threads": (_c_int, [_c_int]),
+    "arnorm_status": (_c_int, [ctypes.POINTER(_c_int), _c_ptr]),
+    "arnorm_strerror": (ctypes.c_char_p, [_c_int]),
+}
+
+
+def load_library(path=LIB_PATH):
+    """dlopen libarnorm.so and declare the C signatures (no GPU call is made)."""
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is not built: run `python -m tp_all_reduce_arnorm_amd.build`")
+    lib = ctypes.CDLL(path)
+    for name, (res, args) in _SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype, fn.argtypes = res, args
+    return lib
+
+
+LIB = load_library()
+
+
+class ArnormError(RuntimeError):
+    def __init__(self, fn, code):
+        super().__init__(f"{fn}: {LIB.arnorm_strerror(code).decode()} (code {code})")
+        self.code = code
+
+
+def _check(fn, code):
+    if code == OK:
+        return True
+    if code == NOT_SERVED:
+        return None
+    raise ArnormError(fn, code)
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _ptr(t, nbytes_per_elem=None, what="tensor"):
+    if t is None:
+        return None
+    if not t.is_cuda or not t.is_contiguous():
+        raise ValueError(f"{what} must be a contiguous device tensor")
+    if nbytes_per_elem is not None and t.element_size() != nbytes_per_elem:
+        raise ValueError(f"{what} must have {nbytes_per_elem}-byte elements, got {t.dtype}")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def lamport_arm(buf, sentinel=SENTINEL, stream=None):
+    """Fill a mailbox (any contiguous 32-bit tensor) with the sentinel."""
+    return _check("lamport_arm", LIB.lamport_arm(_ptr(buf, 4, "buf"), buf.numel(), sentinel, _stream(stream)))
+
+
+def arnorm_push(partial, mailbox, parity, rank, stream=None):
+    """partial: BF16 [nslots, M, 7168] (bfloat16/int16/uint16); mailbox: int32
+    [parities, tp, cap, 3584].  Pushes slots rank .. rank+nslots-1 of mailbox[parity]."""
+    nslots, m, width = partial.shape
+    if width != HIDDEN:
+        return None
+    p, tp, cap, words = mailbox.shape
+    assert words == ROW_WORDS
+    return _check("arnorm_push", LIB.arnorm_push(
+        _ptr(partial, 2, "partial"), _ptr(mailbox, 4, "mailbox"), p, tp, cap, parity, rank, nslots, m,
+        _stream(stream)))
+
+
+def arnorm_reduce_norm(residual, gamma, mailbox, parity, eps, out, residual_out, partial=None, rank=0,
+                       stream=None):
+    """Poll, re-arm and reduce rows < M (M = out.shape[0]) of mailbox[parity]; writes
+    out and residual_out (BF16 [M, 7168]).  residual None: residual = AR(x).
+    partial (BF16 [M, 7168]) is the fused own-rank push of rank `rank`."""
+    m, width = out.shape
+    if width != HIDDEN:
+        return None
+    p, tp, cap, words = mailbox.shape
+    assert words == ROW_WORDS
+    return _check("arnorm_reduce_norm", LIB.arnorm_reduce_norm(
+        _ptr(partial, 2, "partial"), _ptr(residual, 2, "residual"), _ptr(gamma, 2, "gamma"),
+        _ptr(out, 2, "out"), _ptr(residual_out, 2, "residual_out"), _ptr(mailbox, 4, "mailbox"),
+        p, tp, cap, parity, rank, m, float(eps), _stream(stream)))
+
+
+def gather_push(shard, mailbox, tp, rank, stream=None):
+    """shard: int32 [nslots, M, S]; mailbox: int32 [cap, tp*S]."""
+    nslots, m, s = shard.shape
+    cap, width = mailbox.shape
+    assert width == tp * s
+    return _check("gather_push", LIB.gather_push(
+        _ptr(shard, 4, "shard"), _ptr(mailbox, 4, "mailbox"), tp, cap, s, rank, nslots, m, _stream(stream)))
+
+
+def gather_poll(mailbox, tp, m, out=None, copy=True, stream=None):
+    """Poll rows < m of mailbox (int32 [cap, tp*S]); copy: into out (int32 [m, tp*S])
+    and re-arm; no copy: leave the published rows in place."""
+    cap, width = mailbox.shape
+    s = width // tp
+    return _check("gather_poll", LIB.gather_poll(
+        _ptr(mailbox, 4, "mailbox"), _ptr(out, 4, "out") if copy else None, tp, cap, s, m, 1 if copy else 0,
+        _stream(stream)))
+
+
+def set_spin_limit(polls):
+    return _check("arnorm_set_spin_limit", LIB.arnorm_set_spin_limit(polls))
+
+
+def get_spin_limit():
+    return int(LIB.arnorm_get_spin_limit())
+
+
+def set_reduce_threads(threads):
+    return _check("arnorm_set_reduce_threads", LIB.arnorm_set_reduce_threads(threads))
+
+
+def status(stream=None):
+    """Synchronize the stream; read and clear the device status (OK or TIMEOUT)."""
+    v = ctypes.c_int(-1)
+    _check("arnorm_status", LIB.arnorm_status(ctypes.byref(v), _stream(stream)))
+    return v.value

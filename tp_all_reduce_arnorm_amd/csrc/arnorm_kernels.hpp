@@ -1,0 +1,210 @@
+// arnorm_kernels.hpp -- the ArNorm producer and consumer kernels for gfx950.
+//
+// Method: vLLM DSpark drafter pages, "drafter.comm" (module prose, ArNorm entry and
+// kernel), in the one-GPU stand-in of the two-shot page (owners = 1: TP local slots
+// of one mailbox play the ranks).  The pages' design (one 8-CTA cluster per row,
+// 112 threads of 8 columns, sums of squares exchanged through distributed shared
+// memory, a multicast push) is NVIDIA prior art; here one workgroup owns a whole row,
+// so the row's sum of squares never leaves the CU: per-thread FMA chains, a wave64
+// butterfly, and the wave sums added through LDS in wave order.
+#pragma once
+
+#include "device.hpp"
+
+namespace arn {
+
+// ---------------------------------------------------------------------------------
+// lamport_arm: fill `nfrag` fragments and `ntail` trailing words with the sentinel.
+__global__ void __launch_bounds__(256)
+arm_kernel(u32x4 *__restrict__ buf, size_t nfrag, uint32_t *__restrict__ tail, int ntail,
+           uint32_t sentinel) {
+  const u32x4 v = u32x4{sentinel, sentinel, sentinel, sentinel};
+  const size_t stride = (size_t)gridDim.x * blockDim.x;
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < nfrag; i += stride) buf[i] = v;
+  if (blockIdx.x == 0 && (int)threadIdx.x < ntail) tail[threadIdx.x] = sentinel;
+}
+
+// ---------------------------------------------------------------------------------
+// arnorm_push: slot s = blockIdx.y of the nslots pushed; each slot's M rows are one
+// contiguous block of `frags` fragments in both the partial rows and the mailbox.
+// U fragments per thread per step, loads first, so a wave has U x 1 KB in flight.
+template <int U, int POL>
+__global__ void __launch_bounds__(256)
+push_kernel(const u32x4 *__restrict__ partial, uint8_t *__restrict__ first_slot,
+            size_t slot_stride_bytes, uint32_t frags) {
+  const uint32_t s = blockIdx.y;
+  const u32x4 *src = partial + (size_t)s * frags;
+  const __amdgpu_buffer_rsrc_t dst = make_rsrc(first_slot + s * slot_stride_bytes, frags * 16u);
+  const uint32_t step = gridDim.x * 256u * U;
+  for (uint32_t base = blockIdx.x * 256u * U + threadIdx.x; base < frags; base += step) {
+    u32x4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const uint32_t i = base + u * 256u;
+      if (i < frags) v[u] = nt_load(src + i);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const uint32_t i = base + u * 256u;
+      if (i < frags) buf_store<POL>(clean4(v[u]), dst, i * 16u);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------------
+// arnorm_reduce_norm: one workgroup of NT threads per row (blockIdx.x); thread t owns
+// fragments t, t + NT, ... (< 896), NF of them, so every wave instruction touches
+// 1 KB of contiguous row.  Every access is a buffer instruction on a per-row resource
+// of 14336 bytes, so the hot path has no branch: a fragment past the row end, the own
+// slot of the fused form (a resource of 0 bytes) and the re-arm of a fragment whose
+// poll timed out (offset kOffNone) are out of range, read as 0 and store nothing.
+// All TP slot loads of a thread, its residual and gamma loads are in flight together.
+struct ReduceArgs {
+  const uint8_t *partial;   // [M, 14336 B] (FUSED only)
+  const uint8_t *residual;  // [M, 14336 B] (RES only)
+  const uint8_t *gamma;     // [14336 B]
+  uint8_t *out;             // [M, 14336 B]
+  uint8_t *res_out;         // [M, 14336 B]
+  uint8_t *box;             // mailbox[parity]: [TP, cap, 14336 B]
+  size_t slot_stride;       // cap * 14336 bytes
+  int rank;                 // own slot (FUSED only)
+  float eps;
+  uint64_t spin_limit;
+};
+
+constexpr uint32_t kOffNone = 0x80000000u;  // an offset past every resource
+
+template <int TP, bool RES, bool FUSED, int NT, int POL_LD, int POL_ST>
+__global__ void __launch_bounds__(NT) reduce_norm_kernel(ReduceArgs a) {
+  constexpr int NF = (kRowFrags + NT - 1) / NT;
+  constexpr int NW = NT / 64;
+  static_assert(NT % 64 == 0 && NW <= 16, "wave64 workgroups of at most 16 waves");
+  __shared__ float wave_sums[NW];
+
+  const int t = threadIdx.x;
+  const size_t row_off = (size_t)blockIdx.x * kRowBytes;
+  uint32_t off[NF];
+#pragma unroll
+  for (int f = 0; f < NF; ++f) off[f] = (uint32_t)(t + f * NT) * 16u;
+
+  const __amdgpu_buffer_rsrc_t gam = make_rsrc(a.gamma, kRowBytes);
+  const __amdgpu_buffer_rsrc_t resr = make_rsrc(RES ? a.residual + row_off : nullptr, RES ? kRowBytes : 0);
+  const __amdgpu_buffer_rsrc_t part = make_rsrc(FUSED ? a.partial + row_off : nullptr, FUSED ? kRowBytes : 0);
+  const __amdgpu_buffer_rsrc_t rout = make_rsrc(a.res_out + row_off, kRowBytes);
+  const __amdgpu_buffer_rsrc_t nout = make_rsrc(a.out + row_off, kRowBytes);
+  __amdgpu_buffer_rsrc_t slot[TP];
+#pragma unroll
+  for (int s = 0; s < TP; ++s) {
+    const bool own = FUSED && s == a.rank;
+    slot[s] = make_rsrc(a.box + s * a.slot_stride + row_off, own ? 0u : (uint32_t)kRowBytes);
+  }
+
+  // issue every load: gamma (L2-resident), residual, own partial, the TP slots
+  u32x4 g[NF], res[NF], mine[NF], raw[TP][NF];
+#pragma unroll
+  for (int f = 0; f < NF; ++f) g[f] = buf_load<kPolPlain>(gam, off[f]);
+  if constexpr (RES) {
+#pragma unroll
+    for (int f = 0; f < NF; ++f) res[f] = buf_load<kPolNT>(resr, off[f]);
+  }
+  if constexpr (FUSED) {
+#pragma unroll
+    for (int f = 0; f < NF; ++f) mine[f] = buf_load<kPolNT>(part, off[f]);
+  }
+#pragma unroll
+  for (int s = 0; s < TP; ++s)
+#pragma unroll
+    for (int f = 0; f < NF; ++f) raw[s][f] = buf_load<POL_LD>(slot[s], off[f]);
+  if constexpr (FUSED) {
+#pragma unroll
+    for (int s = 0; s < TP; ++s)
+#pragma unroll
+      for (int f = 0; f < NF; ++f) raw[s][f] = (s == a.rank) ? clean4(mine[f]) : raw[s][f];
+  }
+
+  // first poll pass done; later passes only while a producer is still writing
+  bool all = true;
+#pragma unroll
+  for (int s = 0; s < TP; ++s)
+#pragma unroll
+    for (int f = 0; f < NF; ++f) all = all && published(raw[s][f]);
+  bool timed_out[NF];
+#pragma unroll
+  for (int f = 0; f < NF; ++f) timed_out[f] = false;
+  if (!all) {
+#pragma unroll
+    for (int f = 0; f < NF; ++f) {
+      bool done = true;
+#pragma unroll
+      for (int s = 0; s < TP; ++s) done = done && published(raw[s][f]);
+      for (uint64_t polls = 0; !done; ++polls) {
+        if (polls >= a.spin_limit) {
+          atomicOr(&g_status, 1u);
+          timed_out[f] = true;
+          break;
+        }
+        __builtin_amdgcn_s_sleep(2);
+        done = true;
+#pragma unroll
+        for (int s = 0; s < TP; ++s) {
+          if (!published(raw[s][f])) {
+            raw[s][f] = load_fragment_coherent(
+                reinterpret_cast<const uint32_t *>(a.box + s * a.slot_stride + row_off + off[f]));
+            done = done && published(raw[s][f]);
+          }
+        }
+      }
+    }
+  }
+
+  // re-arm every slot read; a fragment that timed out is left for lamport_arm
+#pragma unroll
+  for (int s = 0; s < TP; ++s)
+#pragma unroll
+    for (int f = 0; f < NF; ++f) buf_store<POL_ST>(sentinel4(), slot[s], timed_out[f] ? kOffNone : off[f]);
+
+  // rank-order sum, one BF16 rounding; residual add, one rounding; sum of squares
+  float sq = 0.0f;
+  u32x4 nres[NF];
+#pragma unroll
+  for (int f = 0; f < NF; ++f) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      float lo = lo_f32(raw[0][f][j]);
+      float hi = hi_f32(raw[0][f][j]);
+#pragma unroll
+      for (int s = 1; s < TP; ++s) {
+        lo = lo + lo_f32(raw[s][f][j]);
+        hi = hi + hi_f32(raw[s][f][j]);
+      }
+      uint32_t w = pack_bf16x2(lo, hi);
+      if constexpr (RES) w = pack_bf16x2(lo_f32(w) + lo_f32(res[f][j]), hi_f32(w) + hi_f32(res[f][j]));
+      nres[f][j] = w;
+      sq = __builtin_fmaf(lo_f32(w), lo_f32(w), sq);
+      sq = __builtin_fmaf(hi_f32(w), hi_f32(w), sq);
+    }
+    buf_store<kPolNT>(nres[f], rout, off[f]);
+  }
+
+  // the row's sum of squares: wave butterfly, then wave sums in wave order
+  sq = wave_sum(sq);
+  if ((t & 63) == 0) wave_sums[t >> 6] = sq;
+  __syncthreads();
+  float total = wave_sums[0];
+#pragma unroll
+  for (int w = 1; w < NW; ++w) total = total + wave_sums[w];
+  const float rstd = 1.0f / sqrtf(total / (float)kHidden + a.eps);  // IEEE div and sqrt
+
+#pragma unroll
+  for (int f = 0; f < NF; ++f) {
+    u32x4 o;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t w = nres[f][j];
+      o[j] = pack_bf16x2((lo_f32(w) * rstd) * lo_f32(g[f][j]), (hi_f32(w) * rstd) * hi_f32(g[f][j]));
+    }
+    buf_store<kPolNT>(o, nout, off[f]);
+  }
+}
+
+}  // namespace arn

@@ -1,0 +1,239 @@
+// libarnorm.hip -- the C ABI declared in include/arnorm.h: argument validation, launch
+// geometry and dispatch to the gfx950 kernels.  One translation unit, so the device
+// status word has a single definition per device.
+#include <algorithm>
+#include <atomic>
+#include <cstdint>
+#include <tuple>
+#include <utility>
+
+#include "arnorm.h"
+#include "arnorm_kernels.hpp"
+#include "gather_kernels.hpp"
+
+namespace {
+
+using arn::u32x4;
+
+std::atomic<uint64_t> g_spin_limit{uint64_t(1) << 22};
+std::atomic<int> g_reduce_threads{0};
+
+// Mailbox cache policies: slot reads and re-arm writes are device-scope coherent
+// (sc1) and non-temporal; a push writes device-coherent.
+constexpr int kPolPoll = arn::kPolDeviceNT;
+constexpr int kPolRearm = arn::kPolDeviceNT;
+constexpr int kPolPush = arn::kPolDeviceNT;
+
+bool aligned16(const void *p) { return p != nullptr && (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// hipLaunchKernel with the kernel's own parameter types, so every argument is passed
+// exactly as the kernel declares it; returns the launch status.
+template <typename... KArgs, typename... Args>
+int launch(void (*kernel)(KArgs...), dim3 grid, dim3 block, hipStream_t stream, Args &&...args) {
+  std::tuple<KArgs...> values(std::forward<Args>(args)...);
+  void *argv[sizeof...(KArgs) > 0 ? sizeof...(KArgs) : 1];
+  std::apply([&](auto &...v) {
+    int i = 0;
+    ((argv[i++] = static_cast<void *>(&v)), ...);
+  }, values);
+  const hipError_t e = hipLaunchKernel(reinterpret_cast<const void *>(kernel), grid, block, argv, 0, stream);
+  return e == hipSuccess ? ARNORM_OK : ARNORM_HIP_ERROR;
+}
+
+// Shape and argument checks shared by arnorm_push / arnorm_reduce_norm.
+int check_box(int parities, int tp, int cap, int parity, int M) {
+  if (tp < 2 || tp > 8) return ARNORM_NOT_SERVED;
+  if (cap < 1 || parities < 1) return ARNORM_BAD_ARG;
+  if (parity < 0 || parity >= parities) return ARNORM_BAD_ARG;
+  if (M < 1 || M > cap) return ARNORM_NOT_SERVED;
+  // one slot's M rows form one buffer range; keep it inside 2 GiB
+  if ((uint64_t)M * arn::kRowBytes >= (uint64_t(1) << 31)) return ARNORM_NOT_SERVED;
+  return ARNORM_OK;
+}
+
+int check_gather(int tp, int cap, int S, int M) {
+  if (tp < 2 || tp > 8) return ARNORM_NOT_SERVED;
+  if (cap < 1) return ARNORM_BAD_ARG;
+  if (S < 4 || S % 4 != 0) return ARNORM_NOT_SERVED;
+  if (M < 1 || M > cap) return ARNORM_NOT_SERVED;
+  if ((uint64_t)tp * S * 4 >= (uint64_t(1) << 31)) return ARNORM_NOT_SERVED;
+  return ARNORM_OK;
+}
+
+uint8_t *parity_base(int32_t *mailbox, int parity, int tp, int cap) {
+  return reinterpret_cast<uint8_t *>(mailbox) + (size_t)parity * tp * cap * arn::kRowBytes;
+}
+
+template <int TP, bool RES, bool FUSED, int NT>
+int launch_reduce(const arn::ReduceArgs &a, int M, hipStream_t stream) {
+  return launch(arn::reduce_norm_kernel<TP, RES, FUSED, NT, kPolPoll, kPolRearm>, dim3(M), dim3(NT), stream, a);
+}
+
+template <int TP, bool RES, bool FUSED>
+int launch_reduce_nt(const arn::ReduceArgs &a, int M, int threads, hipStream_t stream) {
+  switch (threads) {
+    case 896: return launch_reduce<TP, RES, FUSED, 896>(a, M, stream);
+    case 448: return launch_reduce<TP, RES, FUSED, 448>(a, M, stream);
+    case 256: return launch_reduce<TP, RES, FUSED, 256>(a, M, stream);
+    default: return ARNORM_BAD_ARG;
+  }
+}
+
+template <int TP>
+int launch_reduce_tp(const arn::ReduceArgs &a, bool res, bool fused, int M, int threads, hipStream_t stream) {
+  if (fused)
+    return res ? launch_reduce_nt<TP, true, true>(a, M, threads, stream)
+               : launch_reduce_nt<TP, false, true>(a, M, threads, stream);
+  return res ? launch_reduce_nt<TP, true, false>(a, M, threads, stream)
+             : launch_reduce_nt<TP, false, false>(a, M, threads, stream);
+}
+
+// Workgroup size of the consumer: one workgroup per row either way.
+int reduce_threads(int M) {
+  const int forced = g_reduce_threads.load(std::memory_order_relaxed);
+  if (forced) return forced;
+  (void)M;
+  return 896;
+}
+
+}  // namespace
+
+extern "C" {
+
+int lamport_arm(int32_t *buf, size_t words, uint32_t sentinel, hipStream_t stream) {
+  if (!aligned16(buf)) return ARNORM_BAD_ARG;
+  if (words == 0) return ARNORM_OK;
+  const size_t nfrag = words / 4;
+  const int ntail = (int)(words % 4);
+  const size_t want = (nfrag + 255) / 256;
+  const unsigned blocks = (unsigned)std::max<size_t>(1, std::min<size_t>(want, 8192));
+  return launch(arn::arm_kernel, dim3(blocks), dim3(256), stream, reinterpret_cast<u32x4 *>(buf), nfrag,
+                reinterpret_cast<uint32_t *>(buf) + nfrag * 4, ntail, sentinel);
+}
+
+int arnorm_push(const uint16_t *partial, int32_t *mailbox, int parities, int tp, int cap, int parity,
+                int rank, int nslots, int M, hipStream_t stream) {
+  int rc = check_box(parities, tp, cap, parity, M);
+  if (rc != ARNORM_OK) return rc;
+  if (rank < 0 || nslots < 1 || rank + nslots > tp) return ARNORM_BAD_ARG;
+  if (!aligned16(partial) || !aligned16(mailbox)) return ARNORM_BAD_ARG;
+  constexpr int U = 4;
+  const uint32_t frags = (uint32_t)M * arn::kRowFrags;
+  const uint32_t want = (frags + 256 * U - 1) / (256 * U);
+  const dim3 grid(std::max(1u, std::min(want, 1024u)), (unsigned)nslots);
+  uint8_t *first = parity_base(mailbox, parity, tp, cap) + (size_t)rank * cap * arn::kRowBytes;
+  return launch(arn::push_kernel<U, kPolPush>, grid, dim3(256), stream, reinterpret_cast<const u32x4 *>(partial),
+                first, (size_t)cap * arn::kRowBytes, frags);
+}
+
+int arnorm_reduce_norm(const uint16_t *partial, const uint16_t *residual, const uint16_t *gamma, uint16_t *out,
+                       uint16_t *residual_out, int32_t *mailbox, int parities, int tp, int cap, int parity,
+                       int rank, int M, float eps, hipStream_t stream) {
+  int rc = check_box(parities, tp, cap, parity, M);
+  if (rc != ARNORM_OK) return rc;
+  if (partial && (rank < 0 || rank >= tp)) return ARNORM_BAD_ARG;
+  if ((partial && !aligned16(partial)) || (residual && !aligned16(residual))) return ARNORM_BAD_ARG;
+  if (!aligned16(gamma) || !aligned16(out) || !aligned16(residual_out) || !aligned16(mailbox))
+    return ARNORM_BAD_ARG;
+  const void *outs[2] = {out, residual_out};
+  const void *ins[4] = {partial, residual, gamma, mailbox};
+  for (const void *o : outs)
+    for (const void *i : ins)
+      if (o == i && !(o == residual_out && i == residual)) return ARNORM_BAD_ARG;
+  if (out == residual_out) return ARNORM_BAD_ARG;
+
+  arn::ReduceArgs a;
+  a.partial = reinterpret_cast<const uint8_t *>(partial);
+  a.residual = reinterpret_cast<const uint8_t *>(residual);
+  a.gamma = reinterpret_cast<const uint8_t *>(gamma);
+  a.out = reinterpret_cast<uint8_t *>(out);
+  a.res_out = reinterpret_cast<uint8_t *>(residual_out);
+  a.box = parity_base(mailbox, parity, tp, cap);
+  a.slot_stride = (size_t)cap * arn::kRowBytes;
+  a.rank = partial ? rank : -1;
+  a.eps = eps;
+  a.spin_limit = g_spin_limit.load(std::memory_order_relaxed);
+  const bool res = residual != nullptr;
+  const bool fused = partial != nullptr;
+  const int threads = reduce_threads(M);
+  switch (tp) {
+    case 2: return launch_reduce_tp<2>(a, res, fused, M, threads, stream);
+    case 3: return launch_reduce_tp<3>(a, res, fused, M, threads, stream);
+    case 4: return launch_reduce_tp<4>(a, res, fused, M, threads, stream);
+    case 5: return launch_reduce_tp<5>(a, res, fused, M, threads, stream);
+    case 6: return launch_reduce_tp<6>(a, res, fused, M, threads, stream);
+    case 7: return launch_reduce_tp<7>(a, res, fused, M, threads, stream);
+    case 8: return launch_reduce_tp<8>(a, res, fused, M, threads, stream);
+  }
+  return ARNORM_NOT_SERVED;
+}
+
+int gather_push(const int32_t *shard, int32_t *mailbox, int tp, int cap, int S, int rank, int nslots, int M,
+                hipStream_t stream) {
+  int rc = check_gather(tp, cap, S, M);
+  if (rc != ARNORM_OK) return rc;
+  if (rank < 0 || nslots < 1 || rank + nslots > tp) return ARNORM_BAD_ARG;
+  if (!aligned16(shard) || !aligned16(mailbox)) return ARNORM_BAD_ARG;
+  const uint32_t frags = (uint32_t)S / 4;
+  const dim3 grid((frags + 255) / 256, (unsigned)M, (unsigned)nslots);
+  return launch(arn::gather_push_kernel<kPolPush>, grid, dim3(256), stream, reinterpret_cast<const u32x4 *>(shard),
+                reinterpret_cast<uint8_t *>(mailbox), frags, (uint32_t)M, (uint32_t)tp * S * 4u,
+                (uint32_t)rank * S * 4u);
+}
+
+int gather_poll(int32_t *mailbox, int32_t *out, int tp, int cap, int S, int M, int copy, hipStream_t stream) {
+  int rc = check_gather(tp, cap, S, M);
+  if (rc != ARNORM_OK) return rc;
+  if (!aligned16(mailbox) || (copy && !aligned16(out))) return ARNORM_BAD_ARG;
+  if (copy && static_cast<void *>(out) == static_cast<void *>(mailbox)) return ARNORM_BAD_ARG;
+  const uint32_t row_frags = (uint32_t)tp * S / 4;
+  // about one fragment per thread, the whole grid resident at once (at most 2048
+  // workgroups of 256 threads over 256 CUs), at least one workgroup per row
+  const uint32_t want = (row_frags + 255) / 256;
+  const uint32_t ctas = std::max(1u, std::min(want, 2048u / (uint32_t)M));
+  return launch(arn::gather_poll_kernel<kPolPoll, kPolRearm>, dim3(ctas, (unsigned)M), dim3(256), stream,
+                reinterpret_cast<uint8_t *>(mailbox), reinterpret_cast<u32x4 *>(out), row_frags, copy ? 1 : 0,
+                (uint64_t)g_spin_limit.load(std::memory_order_relaxed));
+}
+
+int arnorm_set_spin_limit(uint64_t polls) {
+  if (polls == 0) return ARNORM_BAD_ARG;
+  g_spin_limit.store(polls, std::memory_order_relaxed);
+  return ARNORM_OK;
+}
+
+uint64_t arnorm_get_spin_limit(void) { return g_spin_limit.load(std::memory_order_relaxed); }
+
+int arnorm_set_reduce_threads(int threads) {
+  if (threads != 0 && threads != 896 && threads != 448 && threads != 256) return ARNORM_BAD_ARG;
+  g_reduce_threads.store(threads, std::memory_order_relaxed);
+  return ARNORM_OK;
+}
+
+int arnorm_status(int *status, hipStream_t stream) {
+  if (status == nullptr) return ARNORM_BAD_ARG;
+  if (hipStreamSynchronize(stream) != hipSuccess) return ARNORM_HIP_ERROR;
+  unsigned int v = 0;
+  if (hipMemcpyFromSymbol(&v, HIP_SYMBOL(arn::g_status), sizeof(v), 0, hipMemcpyDeviceToHost) != hipSuccess)
+    return ARNORM_HIP_ERROR;
+  if (v != 0) {
+    const unsigned int zero = 0;
+    if (hipMemcpyToSymbol(HIP_SYMBOL(arn::g_status), &zero, sizeof(zero), 0, hipMemcpyHostToDevice) != hipSuccess)
+      return ARNORM_HIP_ERROR;
+  }
+  *status = v ? ARNORM_TIMEOUT : ARNORM_OK;
+  return ARNORM_OK;
+}
+
+const char *arnorm_strerror(int code) {
+  switch (code) {
+    case ARNORM_OK: return "ok";
+    case ARNORM_NOT_SERVED: return "shape not served (use the stock collective)";
+    case ARNORM_BAD_ARG: return "bad argument";
+    case ARNORM_HIP_ERROR: return "HIP runtime error";
+    case ARNORM_TIMEOUT: return "poll timed out (re-arm the mailbox)";
+  }
+  return "unknown code";
+}
+
+}  // extern "C"
