@@ -64,13 +64,19 @@ def assert_bits_equal(got, want, what):
                              f"want {int(want[i]):#x}")
 
 
-def assert_out_close(got, want, what="out"):
-    """|gpu - oracle| <= 2^-7 |oracle| elementwise (<= 1 BF16 ulp); zero exactly zero;
-    infinities equal; NaN where the oracle has NaN (any NaN pattern)."""
+def assert_out_close(got, want, what="out", exact_zero=None):
+    """Within one BF16 ulp of the oracle's value: |gpu - oracle| <= 2^-7 |oracle| for
+    normal values, <= 2^-133 (the BF16 subnormal step) below the normal range.
+    Elements whose exact value is zero (``exact_zero``; default: where the oracle is
+    zero) must be exactly zero (+0 and -0 compare equal); infinities must be equal;
+    NaN where the oracle has NaN (any NaN pattern)."""
     g = oracle.widen(got).astype(np.float64)
     w = oracle.widen(want).astype(np.float64)
+    if exact_zero is None:
+        exact_zero = w == 0
+    ulp = np.where(exact_zero, 0.0, np.maximum(2.0**-7 * np.abs(w), 2.0**-133))
     with np.errstate(invalid="ignore"):
-        ok = (np.abs(g - w) <= 2.0**-7 * np.abs(w)) | (g == w) | (np.isnan(g) & np.isnan(w))
+        ok = (np.abs(g - w) <= ulp) | (g == w) | (np.isnan(g) & np.isnan(w))
     if not ok.all():
         i = tuple(np.argwhere(~ok)[0])
         raise AssertionError(f"{what}: {(~ok).sum()} outside 1 ulp, first at {i}: got {g[i]!r} "

@@ -42,7 +42,8 @@ def run_call(lib, box_d, box_h, partials, residual, gamma_d, gamma, parity, eps=
         partial=partials[fused_rank] if fused_rank is not None else None, rank=fused_rank or 0)
     got_res = host16(rout_d)
     assert_bits_equal(got_res, want_res, "residual_out")
-    assert_out_close(host16(out_d), want_out)
+    exact_zero = (oracle.widen(want_res) == 0) | (oracle.widen(gamma) == 0)[None, :]
+    assert_out_close(host16(out_d), want_out, exact_zero=exact_zero)
     assert_bits_equal(host32(box_d), box_h, "mailbox")
     assert lib.status() == lib.OK
     return got_res
