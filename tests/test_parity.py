@@ -182,12 +182,15 @@ def torture_partials(rng, tp, m):
         elif kind == 3:  # exact cancellation: slot 1 = -slot 0, the rest -0
             x = rng.integers(0, 1 << 15, W).astype(np.uint16) & np.uint16(0x7F7F)
             p[0, r] = x
-            p[1, r] = x ^ np.uint16(0x8000)
+            if tp > 1:
+                p[1, r] = x ^ np.uint16(0x8000)
             p[2:, r] = 0x8000
         elif kind == 4:  # ties: 1.0 + k * 2^-8 style values per column
             p[0, r] = 0x3F80
-            p[1, r] = rng.choice([0x3B80, 0x3C40, 0x3BC0, 0x3C00], W)
-            p[2:, r] = rng.choice([0x0000, 0x8000, 0x3300], (tp - 2, W))
+            if tp > 1:
+                p[1, r] = rng.choice([0x3B80, 0x3C40, 0x3BC0, 0x3C00], W)
+            if tp > 2:
+                p[2:, r] = rng.choice([0x0000, 0x8000, 0x3300], (tp - 2, W))
         else:  # the sentinel pair everywhere in some slots, -0 words in others
             p[:, r] = rng.integers(0, 1 << 16, (tp, W)).astype(np.uint16) & np.uint16(0xBF7F)
             p[: tp // 2, r, 0::2] = 0x0000
