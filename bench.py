@@ -118,19 +118,7 @@ def time_latency(lib, torch, steps, warmup, chunk=50):
     elapsed = time.perf_counter() - t0
     assert lib.status() == lib.OK
 
-    # the consumer kernel alone at this size: events around eager launches
-    evs = []
-    for i in range(200):
-        parity = i % 2
-        assert lib.arnorm_push(parts[parity], box, parity, 0) is True
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        assert lib.arnorm_reduce_norm(None, gamma, box, parity, EPS, outs[parity][0], outs[parity][1]) is True
-        e1.record()
-        evs.append((e0, e1))
-    torch.cuda.synchronize()
-    kern_us = float(np.median([a.elapsed_time(b) for a, b in evs[20:]])) * 1e3
-    return elapsed, kern_us
+    return elapsed
 
 
 def time_roofline(lib, torch, launches=20):
@@ -168,6 +156,20 @@ def time_roofline(lib, torch, launches=20):
     return cfg, red_us, push_us
 
 
+def pmc_workload(lib, torch, launches=3):
+    """What the rocprofv3 counter runs profile: the consumer and producer kernels at
+    TP=8, M=4096 with residual, and a plain 1 GiB device copy (torch's copy kernel)
+    whose FETCH_SIZE / WRITE_SIZE calibrate the counters against known bytes."""
+    cfg, red_us, push_us = time_roofline(lib, torch, launches=launches)
+    n = 1 << 28  # int32 elements: 1 GiB
+    a = torch.ones(n, dtype=torch.int32, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(launches):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    return {"reduce_us": red_us, "push_us": push_us, "copy_bytes": n * 4}
+
+
 def cpu_baseline(budget_s=10.0):
     """The oracle (numpy, one thread) on the TP=8, M=4 stand-in call: push of 8 slots +
     poll / re-arm / reduce / norm, fresh partials each call."""
@@ -192,6 +194,97 @@ def cpu_baseline(budget_s=10.0):
     return float(np.median(times)) * 1e6, len(times)
 
 
+# -- rocprofv3 summaries (run on the CSVs a profiled run wrote) ----------------------
+
+PROFILE_COMMANDS = {
+    "lat": "rocprofv3 --kernel-trace --stats -f csv -d gpurun_out/prof_lat -o lat -- "
+           "python bench.py --mode latency --steps 2000",
+    "roof": "rocprofv3 --kernel-trace --stats -f csv -d gpurun_out/prof_roof -o roof -- "
+            "python bench.py --mode roofline",
+    "fetch": "rocprofv3 --pmc FETCH_SIZE -f csv -d gpurun_out/pmc_fetch -o fetch -- python bench.py --mode pmc",
+    "write": "rocprofv3 --pmc WRITE_SIZE -f csv -d gpurun_out/pmc_write -o write -- python bench.py --mode pmc",
+}
+
+
+def _short(name):
+    return name.split("(")[0].replace("void ", "")
+
+
+def _stats_table(path):
+    import csv
+
+    rows = list(csv.DictReader(open(path)))
+    out = ["| kernel | calls | average µs | min µs | max µs | share of GPU time |", "|---|---|---|---|---|---|"]
+    for r in rows:
+        out.append(f"| `{_short(r['Name'])}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                   f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | {float(r['Percentage']):.1f} % |")
+    return rows, "\n".join(out)
+
+
+def summarize_profiles(outdir):
+    """Write profiles/*.md and profiles/hbm_traffic.json from the CSVs of the four
+    profiled runs in PROFILE_COMMANDS (a directory laid out as those commands write)."""
+    import csv
+
+    prof = os.path.join(ROOT, "profiles")
+    os.makedirs(prof, exist_ok=True)
+    sha = kernel_sources_hash()
+    for key, title, fname in (
+            ("lat", "Stand-in ArNorm call at TP=8, M=4, no residual (arnorm_push of 8 slots + "
+                    "arnorm_reduce_norm, HIP-graph replay, 2000 calls)", "arnorm_tp8_m4_kernel_stats.md"),
+            ("roof", "ArNorm kernels at TP=8, M=4096, residual (one push of 8 slots + one consumer "
+                     "launch, 23 times)", "arnorm_tp8_m4096_kernel_stats.md")):
+        rows, table = _stats_table(os.path.join(outdir, f"prof_{key}", f"{key}_kernel_stats.csv"))
+        with open(os.path.join(prof, fname), "w") as f:
+            f.write(f"# rocprofv3 kernel statistics: {title}\n\n"
+                    f"Command, from the repository root on one MI355X:\n\n    {PROFILE_COMMANDS[key]}\n\n"
+                    f"Kernel sources sha256[:16] = `{sha}`.\n\n{table}\n")
+
+    def counters(key):
+        path = os.path.join(outdir, f"pmc_{key}", f"{key}_counter_collection.csv")
+        return list(csv.DictReader(open(path)))
+
+    fetch, write = counters("fetch"), counters("write")
+
+    def calib(rows):
+        copies = [r for r in rows if "copyBuffer" in r["Kernel_Name"]]
+        big = max(int(r["Grid_Size"]) for r in copies)
+        vals = [float(r["Counter_Value"]) for r in copies if int(r["Grid_Size"]) == big]
+        return (1 << 30) / 1024 / float(np.mean(vals)), float(np.mean(vals))
+
+    f_scale, f_raw = calib(fetch)
+    w_scale, w_raw = calib(write)
+
+    def per_launch(rows, pattern):
+        vals = [float(r["Counter_Value"]) for r in rows if pattern in r["Kernel_Name"]]
+        return float(np.mean(vals)), len(vals)
+
+    kernels = (("reduce_norm_tp8_m4096_res", "reduce_norm_kernel<8, true, false, 896", reduce_bytes(8, 4096, True)),
+               ("push_tp8_m4096", "push_kernel", push_bytes(8, 4096)))
+    rec, lines = {}, []
+    for key, pat, alg in kernels:
+        fr, n = per_launch(fetch, pat)
+        wr, _ = per_launch(write, pat)
+        rd, wt = fr * 1024 * f_scale, wr * 1024 * w_scale
+        rec[key] = {"bytes_per_launch": round(rd + wt), "read_bytes": round(rd), "write_bytes": round(wt),
+                    "algorithmic_bytes": alg, "sources_sha": sha, "launches": n}
+        lines.append(f"| `{pat.split('<')[0]}` ({key}) | {fr:,.1f} | {rd / 1e6:,.1f} | {wr:,.1f} | {wt / 1e6:,.1f} | "
+                     f"{(rd + wt) / 1e6:,.1f} | {alg / 1e6:,.1f} | {(rd + wt) / alg:.4f} |")
+    with open(os.path.join(prof, "hbm_traffic.json"), "w") as f:
+        json.dump(rec, f, indent=1)
+    with open(os.path.join(prof, "arnorm_tp8_m4096_hbm_traffic.md"), "w") as f:
+        f.write("# HBM traffic per launch from rocprofv3 counters: TP=8, M=4096, residual\n\n"
+                "Commands, from the repository root on one MI355X (two runs, one counter each):\n\n"
+                f"    {PROFILE_COMMANDS['fetch']}\n    {PROFILE_COMMANDS['write']}\n\n"
+                f"Kernel sources sha256[:16] = `{sha}`.\n\n"
+                "Calibration: the same runs copy 1 GiB device to device (`__amd_rocclr_copyBuffer`, the largest "
+                f"grid). It reads FETCH_SIZE = {f_raw:,.1f} KiB and WRITE_SIZE = {w_raw:,.1f} KiB for 1,048,576 KiB "
+                f"moved each way, so bytes = FETCH_SIZE x 1024 x {f_scale:.4f} and WRITE_SIZE x 1024 x {w_scale:.4f}.\n\n"
+                "| kernel | FETCH_SIZE KiB | read MB | WRITE_SIZE KiB | written MB | total MB | algorithmic MB | "
+                "total / algorithmic |\n|---|---|---|---|---|---|---|---|\n" + "\n".join(lines) + "\n")
+    print(json.dumps(rec))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -199,7 +292,14 @@ def main():
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--mode", choices=["full", "latency", "roofline", "pmc"], default="full",
+                    help="latency / roofline / pmc run one part only (for profiler runs)")
+    ap.add_argument("--summarize-profiles", metavar="DIR",
+                    help="write profiles/ summaries from the CSVs of the profiled runs under DIR")
     args = ap.parse_args()
+    if args.summarize_profiles:
+        summarize_profiles(args.summarize_profiles)
+        return
     if args.gpus != 1:
         print(f"bench.py: this benchmark runs on one GPU; the TP ranks are mailbox slots of "
               f"one MI355X (--gpus {args.gpus} is not supported)", file=sys.stderr)
@@ -209,7 +309,18 @@ def main():
     from tp_all_reduce_arnorm_amd import _lib as lib
 
     torch.cuda.set_device(0)
-    elapsed, kern_us = time_latency(lib, torch, args.steps, args.warmup)
+    if args.mode == "latency":
+        elapsed = time_latency(lib, torch, args.steps, args.warmup)
+        print(json.dumps({"mode": "latency", "us_per_call": elapsed / args.steps * 1e6}), flush=True)
+        return
+    if args.mode == "roofline":
+        _, red_us, push_us = time_roofline(lib, torch)
+        print(json.dumps({"mode": "roofline", "reduce_us": red_us, "push_us": push_us}), flush=True)
+        return
+    if args.mode == "pmc":
+        print(json.dumps(dict(mode="pmc", **pmc_workload(lib, torch))), flush=True)
+        return
+    elapsed = time_latency(lib, torch, args.steps, args.warmup)
     cfg5, red_us, push_us = time_roofline(lib, torch)
     rb = reduce_bytes(cfg5.tp, cfg5.m, True)
     pb = push_bytes(cfg5.tp, cfg5.m)
@@ -239,7 +350,6 @@ def main():
             "workload": "ArNorm TP=8 M=4 width 7168, residual=False, 2 parities alternating "
                         "(arnorm_push of 8 slots + arnorm_reduce_norm per call, HIP-graph replay)",
             "tp": 8, "m": 4, "hidden": HIDDEN, "parities": 2, "residual": False,
-            "reduce_norm_kernel_us": round(kern_us, 3),
         },
         "roofline": {
             "bound": "hbm",

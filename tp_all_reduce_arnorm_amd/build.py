@@ -40,18 +40,18 @@ FLAGS = [
 ]
 
 
-def build(verbose=True):
+def build(verbose=True, out=LIB, defines=()):
     """Compile every HIP source into libarnorm.so (always recompiles)."""
-    tmp = LIB + ".tmp"
-    cmd = [HIPCC] + FLAGS + SOURCES + ["-o", tmp]
+    tmp = out + ".tmp"
+    cmd = [HIPCC] + FLAGS + [f"-D{d}" for d in defines] + SOURCES + ["-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         sys.stderr.write(res.stdout + res.stderr)
         raise RuntimeError(f"hipcc failed with exit code {res.returncode}")
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
 
 
 def assembly(out_path, kernel_filter=None):

@@ -74,15 +74,60 @@ struct ReduceArgs {
 
 constexpr uint32_t kOffNone = 0x80000000u;  // an offset past every resource
 
-template <int TP, bool RES, bool FUSED, int NT, int POL_LD, int POL_ST>
-__global__ void __launch_bounds__(NT) reduce_norm_kernel(ReduceArgs a) {
+// The later poll passes of one thread: re-read each of its fragments' slots (all but
+// `own`) with device-coherent loads until every slot is published, at most
+// `spin_limit` passes per fragment.  Returns bit f set for a fragment that gave up
+// (and records ARNORM_TIMEOUT in the status word).  Out of line: the hot path does
+// not carry its registers.
+template <int TP, int NF, int NT>
+__device__ __noinline__ uint32_t wait_published(const uint8_t *row_base, size_t slot_stride, int t, int own,
+                                                uint64_t spin_limit) {
+  uint32_t timed_out = 0;
+  for (int f = 0; f < NF; ++f) {
+    const uint32_t off = (uint32_t)(t + f * NT) * 16u;
+    if (off >= (uint32_t)kRowBytes) continue;  // past the row end: nothing to wait for
+    for (int s = 0; s < TP; ++s) {
+      if (s == own) continue;
+      const uint32_t *p = reinterpret_cast<const uint32_t *>(row_base + s * slot_stride + off);
+      uint64_t polls = 0;
+      while (!published(load_fragment_coherent(p))) {
+        if (polls++ >= spin_limit) {
+          atomicOr(&g_status, 1u);
+          timed_out |= 1u << f;
+          break;
+        }
+        __builtin_amdgcn_s_sleep(2);
+      }
+      if ((timed_out >> f) & 1u) break;
+    }
+  }
+  return timed_out;
+}
+
+// Occupancy target (waves per SIMD) for each workgroup size: enough for two or more
+// workgroups per CU, so one workgroup's loads overlap another's stores and reduction.
+template <int NT> struct ReduceOccupancy;
+template <> struct ReduceOccupancy<896> { static constexpr int kWaves = ARNORM_WPE_896; };
+template <> struct ReduceOccupancy<448> { static constexpr int kWaves = ARNORM_WPE_448; };
+template <> struct ReduceOccupancy<256> { static constexpr int kWaves = ARNORM_WPE_256; };
+
+template <int TP, bool RES, bool FUSED, int NT, int POL_LD, int POL_ST, int POL_IO>
+__global__ void __launch_bounds__(NT, ReduceOccupancy<NT>::kWaves) reduce_norm_kernel(ReduceArgs a) {
   constexpr int NF = (kRowFrags + NT - 1) / NT;
   constexpr int NW = NT / 64;
   static_assert(NT % 64 == 0 && NW <= 16, "wave64 workgroups of at most 16 waves");
   __shared__ float wave_sums[NW];
 
   const int t = threadIdx.x;
+#if ARNORM_ROW_ORDER == 1
+  // workgroup i runs on XCD i % 8: give each XCD a contiguous block of rows
+  const uint32_t nblk = gridDim.x, xcd = blockIdx.x % 8u, k = blockIdx.x / 8u;
+  const uint32_t per = nblk / 8u, extra = nblk % 8u;
+  const uint32_t row = xcd < extra ? xcd * (per + 1) + k : extra * (per + 1) + (xcd - extra) * per + k;
+  const size_t row_off = (size_t)row * kRowBytes;
+#else
   const size_t row_off = (size_t)blockIdx.x * kRowBytes;
+#endif
   uint32_t off[NF];
 #pragma unroll
   for (int f = 0; f < NF; ++f) off[f] = (uint32_t)(t + f * NT) * 16u;
@@ -105,11 +150,11 @@ __global__ void __launch_bounds__(NT) reduce_norm_kernel(ReduceArgs a) {
   for (int f = 0; f < NF; ++f) g[f] = buf_load<kPolPlain>(gam, off[f]);
   if constexpr (RES) {
 #pragma unroll
-    for (int f = 0; f < NF; ++f) res[f] = buf_load<kPolNT>(resr, off[f]);
+    for (int f = 0; f < NF; ++f) res[f] = buf_load<POL_IO>(resr, off[f]);
   }
   if constexpr (FUSED) {
 #pragma unroll
-    for (int f = 0; f < NF; ++f) mine[f] = buf_load<kPolNT>(part, off[f]);
+    for (int f = 0; f < NF; ++f) mine[f] = buf_load<POL_IO>(part, off[f]);
   }
 #pragma unroll
   for (int s = 0; s < TP; ++s)
@@ -122,38 +167,26 @@ __global__ void __launch_bounds__(NT) reduce_norm_kernel(ReduceArgs a) {
       for (int f = 0; f < NF; ++f) raw[s][f] = (s == a.rank) ? clean4(mine[f]) : raw[s][f];
   }
 
-  // first poll pass done; later passes only while a producer is still writing
+  // first poll pass done; later passes only while a producer is still writing.  The
+  // waiting happens out of line; afterwards every fragment is published (a published
+  // fragment cannot change before this thread re-arms it), so it is simply re-read.
   bool all = true;
 #pragma unroll
   for (int s = 0; s < TP; ++s)
 #pragma unroll
     for (int f = 0; f < NF; ++f) all = all && published(raw[s][f]);
-  bool timed_out[NF];
-#pragma unroll
-  for (int f = 0; f < NF; ++f) timed_out[f] = false;
+  uint32_t timed_out = 0;  // bit f: fragment f gave up
   if (!all) {
+    timed_out = wait_published<TP, NF, NT>(a.box + row_off, a.slot_stride, t, FUSED ? a.rank : -1, a.spin_limit);
 #pragma unroll
-    for (int f = 0; f < NF; ++f) {
-      bool done = true;
+    for (int s = 0; s < TP; ++s)
 #pragma unroll
-      for (int s = 0; s < TP; ++s) done = done && published(raw[s][f]);
-      for (uint64_t polls = 0; !done; ++polls) {
-        if (polls >= a.spin_limit) {
-          atomicOr(&g_status, 1u);
-          timed_out[f] = true;
-          break;
-        }
-        __builtin_amdgcn_s_sleep(2);
-        done = true;
+      for (int f = 0; f < NF; ++f) raw[s][f] = buf_load<POL_LD>(slot[s], off[f]);
+    if constexpr (FUSED) {
 #pragma unroll
-        for (int s = 0; s < TP; ++s) {
-          if (!published(raw[s][f])) {
-            raw[s][f] = load_fragment_coherent(
-                reinterpret_cast<const uint32_t *>(a.box + s * a.slot_stride + row_off + off[f]));
-            done = done && published(raw[s][f]);
-          }
-        }
-      }
+      for (int s = 0; s < TP; ++s)
+#pragma unroll
+        for (int f = 0; f < NF; ++f) raw[s][f] = (s == a.rank) ? clean4(mine[f]) : raw[s][f];
     }
   }
 
@@ -161,7 +194,7 @@ __global__ void __launch_bounds__(NT) reduce_norm_kernel(ReduceArgs a) {
 #pragma unroll
   for (int s = 0; s < TP; ++s)
 #pragma unroll
-    for (int f = 0; f < NF; ++f) buf_store<POL_ST>(sentinel4(), slot[s], timed_out[f] ? kOffNone : off[f]);
+    for (int f = 0; f < NF; ++f) buf_store<POL_ST>(sentinel4(), slot[s], (timed_out >> f) & 1u ? kOffNone : off[f]);
 
   // rank-order sum, one BF16 rounding; residual add, one rounding; sum of squares
   float sq = 0.0f;
@@ -183,7 +216,7 @@ __global__ void __launch_bounds__(NT) reduce_norm_kernel(ReduceArgs a) {
       sq = __builtin_fmaf(lo_f32(w), lo_f32(w), sq);
       sq = __builtin_fmaf(hi_f32(w), hi_f32(w), sq);
     }
-    buf_store<kPolNT>(nres[f], rout, off[f]);
+    buf_store<POL_IO>(nres[f], rout, off[f]);
   }
 
   // the row's sum of squares: wave butterfly, then wave sums in wave order
@@ -203,7 +236,7 @@ __global__ void __launch_bounds__(NT) reduce_norm_kernel(ReduceArgs a) {
       const uint32_t w = nres[f][j];
       o[j] = pack_bf16x2((lo_f32(w) * rstd) * lo_f32(g[f][j]), (hi_f32(w) * rstd) * hi_f32(g[f][j]));
     }
-    buf_store<kPolNT>(o, nout, off[f]);
+    buf_store<POL_IO>(o, nout, off[f]);
   }
 }
 

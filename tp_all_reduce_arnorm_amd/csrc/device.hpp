@@ -26,6 +26,23 @@ constexpr int kRowBytes = 14336;  // bytes per row
 // XCDs' L2s, which is what a poll needs when its producer runs concurrently.
 enum : int { kPolPlain = 0, kPolNT = 2, kPolDevice = 16, kPolDeviceNT = 18 };
 
+// Minimum waves per SIMD asked of the compiler for each consumer workgroup size
+// (0 = no request).
+#ifndef ARNORM_WPE_896
+#define ARNORM_WPE_896 0
+#endif
+#ifndef ARNORM_WPE_448
+#define ARNORM_WPE_448 0
+#endif
+#ifndef ARNORM_WPE_256
+#define ARNORM_WPE_256 0
+#endif
+// Row order of the consumer grid: 0 = workgroup i takes row i; 1 = each XCD (the
+// dispatcher sends workgroup i to XCD i % 8) takes a contiguous block of rows.
+#ifndef ARNORM_ROW_ORDER
+#define ARNORM_ROW_ORDER 0
+#endif
+
 // Device status word: bit 0 set when a poll gave up (ARNORM_TIMEOUT).  Written with a
 // vector atomic, read and cleared by the host through its symbol.  The library is one
 // translation unit, so this is its only definition.
