@@ -121,6 +121,47 @@ def time_latency(lib, torch, steps, warmup, chunk=50):
     return elapsed
 
 
+def gather_bytes(tp, m, s, copy=True):
+    """Algorithmic bytes: gather_push of all TP slots reads and writes M*S words per
+    slot; gather_poll reads the M*TP*S gathered words and, with copy, writes them out
+    and writes the sentinel back."""
+    words = tp * m * s
+    return 2 * words * 4, (3 if copy else 1) * words * 4
+
+
+def time_gather(lib, torch, calls=1000, chunk=50):
+    """µs per Gather call at TP=8, M=32, S=896 (gather_push of the 8 ranks' shards,
+    then gather_poll with copy), graph-replayed."""
+    from tp_all_reduce_arnorm_amd import workloads as wl
+
+    cfg = wl.CONFIGS["c4"]
+    shards = torch.from_numpy(wl.gather_shards(cfg).view(np.int32)).cuda()
+    box = torch.empty((cfg.cap, cfg.tp * cfg.s), dtype=torch.int32, device="cuda")
+    assert lib.lamport_arm(box) is True
+    out = torch.empty((cfg.m, cfg.tp * cfg.s), dtype=torch.int32, device="cuda")
+
+    def call():
+        assert lib.gather_push(shards, box, cfg.tp, 0) is True
+        assert lib.gather_poll(box, cfg.tp, cfg.m, out=out, copy=True) is True
+
+    for _ in range(4):
+        call()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(chunk):
+            call()
+    g.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(calls // chunk):
+        g.replay()
+    torch.cuda.synchronize()
+    us = (time.perf_counter() - t0) / (calls // chunk * chunk) * 1e6
+    assert lib.status() == lib.OK
+    return cfg, us
+
+
 def time_roofline(lib, torch, launches=20):
     """Consumer and producer kernels at TP=8, M=4096 with residual."""
     from tp_all_reduce_arnorm_amd import workloads as wl
@@ -201,6 +242,8 @@ PROFILE_COMMANDS = {
            "python bench.py --mode latency --steps 2000",
     "roof": "rocprofv3 --kernel-trace --stats -f csv -d gpurun_out/prof_roof -o roof -- "
             "python bench.py --mode roofline",
+    "gather": "rocprofv3 --kernel-trace --stats -f csv -d gpurun_out/prof_gather -o gather -- "
+              "python bench.py --mode gather",
     "fetch": "rocprofv3 --pmc FETCH_SIZE -f csv -d gpurun_out/pmc_fetch -o fetch -- python bench.py --mode pmc",
     "write": "rocprofv3 --pmc WRITE_SIZE -f csv -d gpurun_out/pmc_write -o write -- python bench.py --mode pmc",
 }
@@ -233,7 +276,11 @@ def summarize_profiles(outdir):
             ("lat", "Stand-in ArNorm call at TP=8, M=4, no residual (arnorm_push of 8 slots + "
                     "arnorm_reduce_norm, HIP-graph replay, 2000 calls)", "arnorm_tp8_m4_kernel_stats.md"),
             ("roof", "ArNorm kernels at TP=8, M=4096, residual (one push of 8 slots + one consumer "
-                     "launch, 23 times)", "arnorm_tp8_m4096_kernel_stats.md")):
+                     "launch, 23 times)", "arnorm_tp8_m4096_kernel_stats.md"),
+            ("gather", "Gather at TP=8, M=32, S=896 words, cap=64 (gather_push of 8 slots + gather_poll "
+                       "with copy, HIP-graph replay, 1000 calls)", "gather_tp8_m32_s896_kernel_stats.md")):
+        if not os.path.exists(os.path.join(outdir, f"prof_{key}", f"{key}_kernel_stats.csv")):
+            continue
         rows, table = _stats_table(os.path.join(outdir, f"prof_{key}", f"{key}_kernel_stats.csv"))
         with open(os.path.join(prof, fname), "w") as f:
             f.write(f"# rocprofv3 kernel statistics: {title}\n\n"
@@ -292,7 +339,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--mode", choices=["full", "latency", "roofline", "pmc"], default="full",
+    ap.add_argument("--mode", choices=["full", "latency", "roofline", "pmc", "gather"], default="full",
                     help="latency / roofline / pmc run one part only (for profiler runs)")
     ap.add_argument("--summarize-profiles", metavar="DIR",
                     help="write profiles/ summaries from the CSVs of the profiled runs under DIR")
@@ -317,11 +364,17 @@ def main():
         _, red_us, push_us = time_roofline(lib, torch)
         print(json.dumps({"mode": "roofline", "reduce_us": red_us, "push_us": push_us}), flush=True)
         return
+    if args.mode == "gather":
+        _, us = time_gather(lib, torch)
+        print(json.dumps({"mode": "gather", "us_per_call": us}), flush=True)
+        return
     if args.mode == "pmc":
         print(json.dumps(dict(mode="pmc", **pmc_workload(lib, torch))), flush=True)
         return
     elapsed = time_latency(lib, torch, args.steps, args.warmup)
     cfg5, red_us, push_us = time_roofline(lib, torch)
+    cfg4, gather_us = time_gather(lib, torch)
+    gpb, gqb = gather_bytes(cfg4.tp, cfg4.m, cfg4.s)
     rb = reduce_bytes(cfg5.tp, cfg5.m, True)
     pb = push_bytes(cfg5.tp, cfg5.m)
     achieved = rb / (red_us * 1e-6) / 1e9
@@ -367,6 +420,11 @@ def main():
             "kernel": "arnorm_push", "workload": "8 slots, M=4096", "algorithmic_bytes": pb,
             "kernel_us": round(push_us, 2), "achieved_gbps": round(pb / (push_us * 1e-6) / 1e9, 1),
             "frac": round(pb / (push_us * 1e-6) / 1e9 / PEAK_HBM_GBPS, 4),
+        },
+        "gather": {
+            "workload": "Gather TP=8 M=32 S=896 words cap=64, gather_push of 8 slots + gather_poll "
+                        "with copy, HIP-graph replay",
+            "us_per_call": round(gather_us, 3), "push_algorithmic_bytes": gpb, "poll_algorithmic_bytes": gqb,
         },
         "cpu_baseline": cpu,
     }
