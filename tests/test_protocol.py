@@ -112,3 +112,90 @@ def test_graph_replay_alternating_parities(lib):
         assert_bits_equal(host32(box_d), box_h, f"replay {replay} mailbox")
         _ = torch.ones(1024, device="cuda").sum().item()  # eager work between replays
     assert lib.status() == lib.OK
+
+
+@pytest.mark.parametrize("m,residual", [(4, False), (64, True), (1, True)])
+def test_concurrent_consumer_polls_while_producer_pushes(lib, m, residual):
+    """The Lamport mode proper: the consumer is launched first on its own stream and
+    spins on the mailbox while the producer, delayed on another stream, pushes; no
+    kernel boundary orders them.  Every call must match the oracle.  (A spin limit of
+    2^16 passes ends the wait early should the two streams ever be serialized.)"""
+    import torch
+
+    say(f"[protocol] concurrent consumer-first M={m} residual={residual}")
+    old = lib.get_spin_limit()
+    lib.set_spin_limit(1 << 16)
+    try:
+        rng = np.random.default_rng(40 + m)
+        tp, cap = 8, 64
+        shape = (2, tp, cap, W // 2)
+        box_d = armed_box(shape)
+        box_h = oracle.arm(np.empty(shape, dtype=np.uint32))
+        gamma = (np.float32(1) + np.float32(0.1) * rng.standard_normal(W, dtype=np.float32)).view(np.uint32)
+        gamma = (gamma >> 16).astype(np.uint16)
+        g_d = dev16(gamma)
+        cur = torch.cuda.current_stream()
+        s_prod, s_cons = torch.cuda.Stream(), torch.cuda.Stream()
+        for call in range(6):
+            parity = call % 2
+            p = (rng.standard_normal((tp, m, W), dtype=np.float32).view(np.uint32) >> 16).astype(np.uint16)
+            res = (rng.standard_normal((m, W), dtype=np.float32).view(np.uint32) >> 16).astype(np.uint16) \
+                if residual else None
+            p_d = dev16(p)
+            res_d = dev16(res) if residual else None
+            out_d, rout_d = empty16((m, W)), empty16((m, W))
+            torch.cuda.synchronize()
+            s_prod.wait_stream(cur)
+            s_cons.wait_stream(cur)
+            with torch.cuda.stream(s_cons):
+                assert lib.arnorm_reduce_norm(res_d, g_d, box_d, parity, EPS, out_d, rout_d) is True
+            with torch.cuda.stream(s_prod):
+                torch.cuda._sleep(200000)  # hold the producer back so that the consumer spins
+                assert lib.arnorm_push(p_d, box_d, parity, 0) is True
+            cur.wait_stream(s_prod)
+            cur.wait_stream(s_cons)
+            torch.cuda.synchronize()
+            assert lib.status() == lib.OK, "a poll timed out: producer and consumer did not overlap"
+            oracle.arnorm_push(box_h, p, parity, 0)
+            want_out, want_res = oracle.arnorm_reduce_norm(box_h, parity, m, res, gamma, EPS)
+            assert_bits_equal(host16(rout_d), want_res, f"call {call} residual_out")
+            assert_out_close(host16(out_d), want_out, f"call {call} out")
+            assert_bits_equal(host32(box_d), box_h, f"call {call} mailbox")
+    finally:
+        lib.set_spin_limit(old)
+
+
+def test_concurrent_gather_consumer_first(lib):
+    import torch
+
+    say("[protocol] concurrent gather consumer-first")
+    old = lib.get_spin_limit()
+    lib.set_spin_limit(1 << 16)
+    try:
+        cfg = wl.CONFIGS["c4"]
+        shards = wl.gather_shards(cfg)
+        gshape = (cfg.cap, cfg.tp * cfg.s)
+        gbox_d = armed_box(gshape)
+        gbox_h = oracle.arm(np.empty(gshape, dtype=np.uint32))
+        sh_d = dev32(shards)
+        cur = torch.cuda.current_stream()
+        s_prod, s_cons = torch.cuda.Stream(), torch.cuda.Stream()
+        for _ in range(3):
+            out_d = torch.empty((cfg.m, cfg.tp * cfg.s), dtype=torch.int32, device="cuda")
+            torch.cuda.synchronize()
+            s_prod.wait_stream(cur)
+            s_cons.wait_stream(cur)
+            with torch.cuda.stream(s_cons):
+                assert lib.gather_poll(gbox_d, cfg.tp, cfg.m, out=out_d, copy=True) is True
+            with torch.cuda.stream(s_prod):
+                torch.cuda._sleep(200000)
+                assert lib.gather_push(sh_d, gbox_d, cfg.tp, 0) is True
+            cur.wait_stream(s_prod)
+            cur.wait_stream(s_cons)
+            torch.cuda.synchronize()
+            assert lib.status() == lib.OK
+            oracle.gather_push(gbox_h, shards, 0)
+            assert_bits_equal(host32(out_d), oracle.gather_poll(gbox_h, cfg.m, True), "gathered words")
+            assert_bits_equal(host32(gbox_d), gbox_h, "gather mailbox")
+    finally:
+        lib.set_spin_limit(old)

@@ -74,36 +74,6 @@ struct ReduceArgs {
 
 constexpr uint32_t kOffNone = 0x80000000u;  // an offset past every resource
 
-// The later poll passes of one thread: re-read each of its fragments' slots (all but
-// `own`) with device-coherent loads until every slot is published, at most
-// `spin_limit` passes per fragment.  Returns bit f set for a fragment that gave up
-// (and records ARNORM_TIMEOUT in the status word).  Out of line: the hot path does
-// not carry its registers.
-template <int TP, int NF, int NT>
-__device__ __noinline__ uint32_t wait_published(const uint8_t *row_base, size_t slot_stride, int t, int own,
-                                                uint64_t spin_limit) {
-  uint32_t timed_out = 0;
-  for (int f = 0; f < NF; ++f) {
-    const uint32_t off = (uint32_t)(t + f * NT) * 16u;
-    if (off >= (uint32_t)kRowBytes) continue;  // past the row end: nothing to wait for
-    for (int s = 0; s < TP; ++s) {
-      if (s == own) continue;
-      const uint32_t *p = reinterpret_cast<const uint32_t *>(row_base + s * slot_stride + off);
-      uint64_t polls = 0;
-      while (!published(load_fragment_coherent(p))) {
-        if (polls++ >= spin_limit) {
-          atomicOr(&g_status, 1u);
-          timed_out |= 1u << f;
-          break;
-        }
-        __builtin_amdgcn_s_sleep(2);
-      }
-      if ((timed_out >> f) & 1u) break;
-    }
-  }
-  return timed_out;
-}
-
 // Occupancy target (waves per SIMD) for each workgroup size: enough for two or more
 // workgroups per CU, so one workgroup's loads overlap another's stores and reduction.
 template <int NT> struct ReduceOccupancy;
@@ -167,26 +137,60 @@ __global__ void __launch_bounds__(NT, ReduceOccupancy<NT>::kWaves) reduce_norm_k
       for (int f = 0; f < NF; ++f) raw[s][f] = (s == a.rank) ? clean4(mine[f]) : raw[s][f];
   }
 
-  // first poll pass done; later passes only while a producer is still writing.  The
-  // waiting happens out of line; afterwards every fragment is published (a published
-  // fragment cannot change before this thread re-arms it), so it is simply re-read.
-  bool all = true;
+  // later poll passes, only while a producer is still writing.  Waiting must not steal
+  // the producer's bandwidth: each wave watches one witness fragment (the first pending
+  // one of its lowest waiting lane; every lane loads the same 16 B, one request) and only
+  // when that is published do its lanes re-read all their slots together.  Re-reading a
+  // published fragment is exact: it cannot change before this thread re-arms it.
+  uint32_t pending = 0;  // bit s * NF + f: slot s of fragment f not yet published
 #pragma unroll
   for (int s = 0; s < TP; ++s)
 #pragma unroll
-    for (int f = 0; f < NF; ++f) all = all && published(raw[s][f]);
+    for (int f = 0; f < NF; ++f)
+      if (!published(raw[s][f])) pending |= 1u << (s * NF + f);
   uint32_t timed_out = 0;  // bit f: fragment f gave up
-  if (!all) {
-    timed_out = wait_published<TP, NF, NT>(a.box + row_off, a.slot_stride, t, FUSED ? a.rank : -1, a.spin_limit);
+  if (__any(pending != 0)) {
+    const int lane = t & 63;
+    for (uint64_t polls = 0;; ++polls) {
+      const uint64_t waiting = __ballot(pending != 0);
+      if (waiting == 0) break;
+      if (polls >= a.spin_limit) {
 #pragma unroll
-    for (int s = 0; s < TP; ++s)
+        for (int f = 0; f < NF; ++f) {
+          uint32_t frag_bits = 0;
 #pragma unroll
-      for (int f = 0; f < NF; ++f) raw[s][f] = buf_load<POL_LD>(slot[s], off[f]);
-    if constexpr (FUSED) {
+          for (int s = 0; s < TP; ++s) frag_bits |= 1u << (s * NF + f);
+          if (pending & frag_bits) timed_out |= 1u << f;
+        }
+        if (pending) atomicOr(&g_status, 1u);
+        break;
+      }
+      const int wl = __ffsll((unsigned long long)waiting) - 1;
+      const int wbit = __shfl(__ffs(pending) - 1, wl, 64);  // s * NF + f of the witness
+      const int ws = wbit / NF, wf = wbit % NF;
+      const uint32_t *wp = reinterpret_cast<const uint32_t *>(
+          a.box + ws * a.slot_stride + row_off + (size_t)((t - lane + wl) + wf * NT) * 16u);
+      if (!published(load_fragment_coherent(wp))) {
+        __builtin_amdgcn_s_sleep(8);
+        continue;
+      }
+      asm volatile("" ::: "memory");
 #pragma unroll
       for (int s = 0; s < TP; ++s)
 #pragma unroll
-        for (int f = 0; f < NF; ++f) raw[s][f] = (s == a.rank) ? clean4(mine[f]) : raw[s][f];
+        for (int f = 0; f < NF; ++f) raw[s][f] = buf_load<POL_LD>(slot[s], off[f]);
+      if constexpr (FUSED) {
+#pragma unroll
+        for (int s = 0; s < TP; ++s)
+#pragma unroll
+          for (int f = 0; f < NF; ++f) raw[s][f] = (s == a.rank) ? clean4(mine[f]) : raw[s][f];
+      }
+      pending = 0;
+#pragma unroll
+      for (int s = 0; s < TP; ++s)
+#pragma unroll
+        for (int f = 0; f < NF; ++f)
+          if (!published(raw[s][f])) pending |= 1u << (s * NF + f);
     }
   }
 

@@ -35,25 +35,39 @@ gather_poll_kernel(uint8_t *__restrict__ box, u32x4 *__restrict__ out, uint32_t 
   const uint32_t m = blockIdx.y;
   uint8_t *row = box + (size_t)m * row_frags * 16u;
   const __amdgpu_buffer_rsrc_t r = make_rsrc(row, row_frags * 16u);
-  for (uint32_t i = blockIdx.x * 256u + threadIdx.x; i < row_frags; i += gridDim.x * 256u) {
-    u32x4 w = buf_load<POL_LD>(r, i * 16u);
-    bool ok = published(w);
-    if (!ok) {
-      const uint32_t *p = reinterpret_cast<const uint32_t *>(row + (size_t)i * 16u);
-      for (uint64_t polls = 0;; ++polls) {
-        if (polls >= spin_limit) {
-          atomicOr(&g_status, 1u);
-          break;
-        }
-        __builtin_amdgcn_s_sleep(2);
-        w = load_fragment_coherent(p);
-        if (published(w)) {
-          ok = true;
-          break;
-        }
+  // Waiting must not steal the producers' bandwidth: a wave with unpublished fragments
+  // watches one witness (the fragment of its lowest waiting lane; every lane loads the
+  // same 16 B) and its lanes re-read their own fragments only once that is published.
+  // The loop trip count is uniform per wave (the step is a multiple of 64).
+  const int lane = threadIdx.x & 63;
+  for (uint32_t base = blockIdx.x * 256u + (threadIdx.x & ~63u); base < row_frags; base += gridDim.x * 256u) {
+    const uint32_t i = base + lane;
+    const bool mine = i < row_frags;
+    u32x4 w = buf_load<POL_LD>(r, mine ? i * 16u : 0x80000000u);
+    bool ok = !mine || published(w);
+    bool gave_up = false;
+    for (uint64_t polls = 0;; ++polls) {
+      const uint64_t waiting = __ballot(!ok);
+      if (waiting == 0) break;
+      if (polls >= spin_limit) {
+        if (!ok) atomicOr(&g_status, 1u);
+        gave_up = true;
+        break;
+      }
+      const int wl = __ffsll((unsigned long long)waiting) - 1;
+      const uint32_t *wp = reinterpret_cast<const uint32_t *>(row + (size_t)(base + wl) * 16u);
+      if (!published(load_fragment_coherent(wp))) {
+        __builtin_amdgcn_s_sleep(8);
+        continue;
+      }
+      asm volatile("" ::: "memory");
+      if (!ok) {
+        w = buf_load<POL_LD>(r, i * 16u);
+        ok = published(w);
       }
     }
-    if (copy && ok) {
+    (void)gave_up;
+    if (copy && mine && ok) {
       nt_store(w, out + (size_t)m * row_frags + i);
       buf_store<POL_ST>(sentinel4(), r, i * 16u);
     }
