@@ -3,7 +3,8 @@
 This package is the plain, slow, obviously correct statement of what the hot path
 computes, written from the vLLM API-doc pages for the DSpark drafter's TP collectives
 (page "drafter.comm": the module prose, the ArNorm / Gather / clean / LamportRows
-entries) and the two-shot all-reduce page ("cutedsl.common.twoshot": its module prose).
+entries) and the two-shot all-reduce page ("cutedsl.common.twoshot": its module
+prose and the push / reduce entries).
 
 Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
 ``bench.py`` may import it.  The product path (the HIP library and its Python
@@ -25,6 +26,8 @@ Pins (what the oracle is checked against, in ``tests/test_oracle.py``):
                         row) and a 50-digit decimal reference on random rows
   * mailbox protocol -- arm / push / poll / re-arm invariants, parity reuse
   * gather           -- hand case, byte movement, state after copy / no-copy
+  * two-shot         -- the no-negative-zero hand cases (tests/golden/twoshot_words.txt),
+                        the TP=2 theorem with -0 mapped to +0, and its protocol
 Parity unpinned: the reference kernel's exact sum-of-squares bit pattern (its tree
 order is not something the oracle reproduces); ``out`` is pinned to 1 BF16 ulp.
 """
@@ -53,3 +56,4 @@ from .arnorm import (  # noqa: F401
     arnorm_rows,
 )
 from .gather import gather_push, gather_poll  # noqa: F401
+from .twoshot import twoshot_push, twoshot_reduce, twoshot_read, reduce_no_negative_zero  # noqa: F401

@@ -18,6 +18,7 @@ from oracle import bf16 as obf
 from oracle import arnorm as oar
 from oracle import gather as oga
 from oracle import lamport as olp
+from oracle import twoshot as ots
 from tests.conftest import read_golden
 
 S0 = 0x80000000
@@ -323,6 +324,65 @@ def check_gather(push_fn, poll_fn):
         poll_fn(gbox, m, True)  # nothing published
 
 
+def run_twoshot_words(push_fn, reduce_fn, words):
+    tp = len(words)
+    recv = np.full((1, tp, 1, 4), S0, dtype=np.uint32)
+    gath = np.full((1, 1, 1, 4), S0, dtype=np.uint32)
+    part = np.zeros((tp, 1, 8), dtype=np.uint16)
+    for k, w in enumerate(words):
+        part[k, 0, 0] = w & 0xFFFF
+        part[k, 0, 1] = w >> 16
+    push_fn(recv, part, 0, 0)
+    red = reduce_fn(recv, gath, 0, 1)
+    return int(red[0, 0]) | (int(red[0, 1]) << 16), recv, gath
+
+
+def check_twoshot_golden(push_fn, reduce_fn):
+    for ln in read_golden("twoshot_words.txt"):
+        name, slots, want = [p.strip() for p in ln.split("|")]
+        got, recv, gath = run_twoshot_words(push_fn, reduce_fn, [int(x, 16) for x in slots.split(",")])
+        assert got == int(want, 16), f"{name}: got {got:08X}, want {want}"
+        assert np.all(recv == S0), f"{name}: recv not re-armed"
+        assert gath[0, 0, 0, 0] == got, f"{name}: gather row does not hold the result"
+
+
+def check_twoshot_theorem(reduce_rows_fn):
+    """TP=2: correctly rounded exact sum, with -0 turned into +0."""
+    rng = np.random.default_rng(19)
+    n = 3000
+    a = random_finite_bf16(rng, n)
+    b = random_finite_bf16(rng, n)
+    b[: n // 3] = (a[: n // 3] ^ rng.integers(0, 1 << 7, n // 3).astype(np.uint16)) ^ np.uint16(0x8000)
+    a[-20:] = 0x8000  # -0 + -0: the one sum whose exact result is a negative zero
+    b[-20:] = 0x8000
+    got = np.asarray(reduce_rows_fn(np.stack([obf.pack_pairs(a), obf.pack_pairs(b)])[:, None, :]))[0]
+    for i in range(n):
+        want = exact_rne_bf16(bf16_bits_to_fraction(a[i]) + bf16_bits_to_fraction(b[i]))
+        want = 0 if want == 0x8000 else want
+        assert int(got[i]) == want, (hex(a[i]), hex(b[i]), hex(int(got[i])), hex(want))
+
+
+def check_twoshot_protocol(push_fn, reduce_fn, read_fn):
+    rng = np.random.default_rng(20)
+    tp, m, cap, width = 4, 3, 5, 64
+    recv = np.full((2, tp, cap, width // 2), S0, dtype=np.uint32)
+    gath = np.full((2, 1, cap, width // 2), S0, dtype=np.uint32)
+    for call in range(4):
+        parity = call % 2
+        other_r, other_g = recv[1 - parity].copy(), gath[1 - parity].copy()
+        part = random_finite_bf16(rng, tp * m * width, -3, 3).reshape(tp, m, width)
+        push_fn(recv, part, parity, 0)
+        red = reduce_fn(recv, gath, parity, m)
+        assert np.all(recv[parity] == S0), "the owner re-arms its slots"
+        assert not np.any(gath[parity, 0, :m] == S0), "the reduced row is published"
+        with pytest.raises(olp.ProtocolError):
+            reduce_fn(recv, gath, parity, m)  # nothing pushed any more
+        got = read_fn(gath, parity, m)
+        assert np.array_equal(got, red)
+        assert np.all(gath[parity] == S0), "the reader re-arms the gather row"
+        assert np.array_equal(recv[1 - parity], other_r) and np.array_equal(gath[1 - parity], other_g)
+
+
 # -- the pins, run on the oracle ---------------------------------------------------
 
 
@@ -385,6 +445,27 @@ def test_protocol():
 
 def test_gather():
     check_gather(oga.gather_push, oga.gather_poll)
+
+
+def test_twoshot_golden():
+    check_twoshot_golden(ots.twoshot_push, ots.twoshot_reduce)
+
+
+def test_twoshot_theorem():
+    check_twoshot_theorem(ots.reduce_no_negative_zero)
+
+
+def test_twoshot_protocol():
+    check_twoshot_protocol(ots.twoshot_push, ots.twoshot_reduce, ots.twoshot_read)
+
+
+def test_twoshot_matches_arnorm_sum_off_negative_zero():
+    """Away from -0 the two-shot sum is ArNorm's all-reduced row, bit for bit."""
+    rng = np.random.default_rng(21)
+    words = obf.pack_pairs(random_finite_bf16(rng, 8 * 2 * 512, -5, 5).reshape(8, 2, 512))
+    a = oar.allreduce_rows(words)
+    b = ots.reduce_no_negative_zero(words)
+    assert np.array_equal(np.where(a == 0x8000, 0, a), b)
 
 
 def test_fused_push_matches_separate_push():
@@ -540,7 +621,34 @@ def _gather_push_no_clean(gbox, shard, rank):
         gbox[:m, (rank + k) * s:(rank + k + 1) * s] = shard[k]
 
 
+def _ts_keep_negative_zero(recv, gath, parity, m):
+    slots = recv[parity, :, :m]
+    olp.check_published(slots, "mutant")
+    raw = slots.copy()
+    recv[parity, :, :m] = S0
+    red = oar.allreduce_rows(raw)
+    gath[parity, 0, :m] = obf.pack_pairs(red)
+    return red
+
+
+def _ts_reader_keeps_row(gath, parity, m):
+    return obf.unpack_pairs(gath[parity, 0, :m].copy())
+
+
+def _ts_owner_keeps_slots(recv, gath, parity, m):
+    raw = recv[parity, :, :m].copy()
+    red = ots.reduce_no_negative_zero(raw)
+    gath[parity, 0, :m] = obf.pack_pairs(red)
+    return red
+
+
 MUTANTS = {
+    "two-shot keeps -0": lambda: check_twoshot_golden(ots.twoshot_push, _ts_keep_negative_zero),
+    "two-shot -0 kept (theorem)": lambda: check_twoshot_theorem(oar.allreduce_rows),
+    "two-shot reader keeps row": lambda: check_twoshot_protocol(ots.twoshot_push, ots.twoshot_reduce,
+                                                                _ts_reader_keeps_row),
+    "two-shot owner keeps slots": lambda: check_twoshot_protocol(ots.twoshot_push, _ts_owner_keeps_slots,
+                                                                 ots.twoshot_read),
     "tree order": lambda: check_allreduce_golden(oar.arnorm_push, _with_allreduce(_mut_tree)),
     "reverse order": lambda: check_allreduce_golden(oar.arnorm_push, _with_allreduce(_mut_reverse)),
     "sum from +0": lambda: check_allreduce_golden(oar.arnorm_push, _with_allreduce(_mut_from_zero)),
