@@ -162,6 +162,75 @@ def time_gather(lib, torch, calls=1000, chunk=50):
     return cfg, us
 
 
+def twoshot_bytes(tp, m, width=HIDDEN):
+    """Algorithmic bytes of the two-shot owner's reduce (TP slot reads, TP re-arm writes,
+    the gather row) and of one read of the gather row (read, copy out, re-arm)."""
+    row = width * 2
+    return 2 * tp * m * row + m * row, 3 * m * row
+
+
+def time_twoshot(lib, torch, calls=1000, chunk=50, launches=20):
+    """Two-shot stand-in: µs per graph-replayed call at TP=8, M=4 (push of 8 slots,
+    owner's reduce, read of the gather row), and the reduce / read kernels at M=4096."""
+    from tp_all_reduce_arnorm_amd import workloads as wl
+
+    res = {}
+    cfg = wl.CONFIGS["c2"]
+    src = wl.ArNormInputs(cfg)
+    recv = torch.empty((2, 8, cfg.cap, HIDDEN // 2), dtype=torch.int32, device="cuda")
+    gath = torch.empty((2, 1, cfg.cap, HIDDEN // 2), dtype=torch.int32, device="cuda")
+    assert lib.lamport_arm(recv) is True and lib.lamport_arm(gath) is True
+    parts = [torch.from_numpy(src.partials().view(np.int16)).cuda() for _ in range(2)]
+    outs = [torch.empty((cfg.m, HIDDEN), dtype=torch.int16, device="cuda") for _ in range(2)]
+
+    def call(i):
+        p = i % 2
+        assert lib.twoshot_push(parts[p], recv, p, 0) is True
+        assert lib.twoshot_reduce(recv, gath, p, cfg.m) is True
+        assert lib.twoshot_read(gath, p, outs[p]) is True
+
+    for i in range(4):
+        call(i)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(chunk):
+            call(i)
+    g.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(calls // chunk):
+        g.replay()
+    torch.cuda.synchronize()
+    res["us_per_call_m4"] = (time.perf_counter() - t0) / (calls // chunk * chunk) * 1e6
+    del g
+
+    cfg = wl.CONFIGS["c5"]
+    p5 = torch.from_numpy(wl.ArNormInputs(cfg).partials().view(np.int16)).cuda()
+    recv = torch.empty((1, 8, cfg.cap, HIDDEN // 2), dtype=torch.int32, device="cuda")
+    gath = torch.empty((1, 1, cfg.cap, HIDDEN // 2), dtype=torch.int32, device="cuda")
+    assert lib.lamport_arm(recv) is True and lib.lamport_arm(gath) is True
+    out = torch.empty((cfg.m, HIDDEN), dtype=torch.int16, device="cuda")
+    red, rd = [], []
+    for i in range(launches + 3):
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+        assert lib.twoshot_push(p5, recv, 0, 0) is True
+        e[0].record()
+        assert lib.twoshot_reduce(recv, gath, 0, cfg.m) is True
+        e[1].record()
+        e[2].record()
+        assert lib.twoshot_read(gath, 0, out) is True
+        e[3].record()
+        if i >= 3:
+            red.append((e[0], e[1]))
+            rd.append((e[2], e[3]))
+    torch.cuda.synchronize()
+    assert lib.status() == lib.OK
+    res["reduce_us_m4096"] = float(np.mean([a.elapsed_time(b) for a, b in red])) * 1e3
+    res["read_us_m4096"] = float(np.mean([a.elapsed_time(b) for a, b in rd])) * 1e3
+    return res
+
+
 def time_roofline(lib, torch, launches=20):
     """Consumer and producer kernels at TP=8, M=4096 with residual."""
     from tp_all_reduce_arnorm_amd import workloads as wl
@@ -244,6 +313,8 @@ PROFILE_COMMANDS = {
             "python bench.py --mode roofline",
     "gather": "rocprofv3 --kernel-trace --stats -f csv -d gpurun_out/prof_gather -o gather -- "
               "python bench.py --mode gather",
+    "twoshot": "rocprofv3 --kernel-trace --stats -f csv -d gpurun_out/prof_twoshot -o twoshot -- "
+               "python bench.py --mode twoshot",
     "fetch": "rocprofv3 --pmc FETCH_SIZE -f csv -d gpurun_out/pmc_fetch -o fetch -- python bench.py --mode pmc",
     "write": "rocprofv3 --pmc WRITE_SIZE -f csv -d gpurun_out/pmc_write -o write -- python bench.py --mode pmc",
 }
@@ -278,7 +349,9 @@ def summarize_profiles(outdir):
             ("roof", "ArNorm kernels at TP=8, M=4096, residual (one push of 8 slots + one consumer "
                      "launch, 23 times)", "arnorm_tp8_m4096_kernel_stats.md"),
             ("gather", "Gather at TP=8, M=32, S=896 words, cap=64 (gather_push of 8 slots + gather_poll "
-                       "with copy, HIP-graph replay, 1000 calls)", "gather_tp8_m32_s896_kernel_stats.md")):
+                       "with copy, HIP-graph replay, 1000 calls)", "gather_tp8_m32_s896_kernel_stats.md"),
+            ("twoshot", "Two-shot all-reduce stand-in (owners = 1): TP=8, M=4 graph-replayed calls (push, "
+                        "owner's reduce, read), then 23 launches at TP=8, M=4096", "twoshot_tp8_kernel_stats.md")):
         if not os.path.exists(os.path.join(outdir, f"prof_{key}", f"{key}_kernel_stats.csv")):
             continue
         rows, table = _stats_table(os.path.join(outdir, f"prof_{key}", f"{key}_kernel_stats.csv"))
@@ -339,7 +412,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--mode", choices=["full", "latency", "roofline", "pmc", "gather"], default="full",
+    ap.add_argument("--mode", choices=["full", "latency", "roofline", "pmc", "gather", "twoshot"], default="full",
                     help="latency / roofline / pmc run one part only (for profiler runs)")
     ap.add_argument("--summarize-profiles", metavar="DIR",
                     help="write profiles/ summaries from the CSVs of the profiled runs under DIR")
@@ -368,12 +441,17 @@ def main():
         _, us = time_gather(lib, torch)
         print(json.dumps({"mode": "gather", "us_per_call": us}), flush=True)
         return
+    if args.mode == "twoshot":
+        print(json.dumps(dict(mode="twoshot", **time_twoshot(lib, torch))), flush=True)
+        return
     if args.mode == "pmc":
         print(json.dumps(dict(mode="pmc", **pmc_workload(lib, torch))), flush=True)
         return
     elapsed = time_latency(lib, torch, args.steps, args.warmup)
     cfg5, red_us, push_us = time_roofline(lib, torch)
     cfg4, gather_us = time_gather(lib, torch)
+    ts = time_twoshot(lib, torch)
+    tsr, tsq = twoshot_bytes(8, 4096)
     gpb, gqb = gather_bytes(cfg4.tp, cfg4.m, cfg4.s)
     rb = reduce_bytes(cfg5.tp, cfg5.m, True)
     pb = push_bytes(cfg5.tp, cfg5.m)
@@ -425,6 +503,16 @@ def main():
             "workload": "Gather TP=8 M=32 S=896 words cap=64, gather_push of 8 slots + gather_poll "
                         "with copy, HIP-graph replay",
             "us_per_call": round(gather_us, 3), "push_algorithmic_bytes": gpb, "poll_algorithmic_bytes": gqb,
+        },
+        "twoshot": {
+            "workload": "two-shot all-reduce, owners = 1: push of 8 slots + owner's reduce + read of the "
+                        "gather row; TP=8 M=4 graph-replayed, and the kernels at TP=8 M=4096",
+            "us_per_call_m4": round(ts["us_per_call_m4"], 3),
+            "reduce_us_m4096": round(ts["reduce_us_m4096"], 2),
+            "reduce_frac": round(tsr / (ts["reduce_us_m4096"] * 1e-6) / 1e9 / PEAK_HBM_GBPS, 4),
+            "read_us_m4096": round(ts["read_us_m4096"], 2),
+            "read_frac": round(tsq / (ts["read_us_m4096"] * 1e-6) / 1e9 / PEAK_HBM_GBPS, 4),
+            "reduce_algorithmic_bytes": tsr, "read_algorithmic_bytes": tsq,
         },
         "cpu_baseline": cpu,
     }

@@ -121,6 +121,21 @@ def test_gather_checks(L):
     assert L.gather_poll(FAKE, None, 8, 64, 896, 0, 0, None) == 1
 
 
+def test_twoshot_checks(L):
+    assert L.twoshot_push(FAKE, FAKE, 2, 1, 64, 7168, 0, 0, 1, 4, None) == 1   # tp 1
+    assert L.twoshot_push(FAKE, FAKE, 2, 8, 64, 7164, 0, 0, 8, 4, None) == 1   # width % 8
+    assert L.twoshot_push(FAKE, FAKE, 2, 8, 64, 7168, 0, 0, 8, 65, None) == 1  # M > cap
+    assert L.twoshot_push(FAKE, FAKE, 2, 8, 64, 7168, 2, 0, 8, 4, None) == 2   # parity
+    assert L.twoshot_push(FAKE, FAKE, 2, 8, 64, 7168, 0, 1, 8, 4, None) == 2   # rank + nslots
+    assert L.twoshot_push(MIS, FAKE, 2, 8, 64, 7168, 0, 0, 8, 4, None) == 2
+    assert L.twoshot_reduce(FAKE, FAKE + 0x100000, 2, 9, 64, 7168, 0, 4, None) == 1
+    assert L.twoshot_reduce(FAKE, FAKE, 2, 8, 64, 7168, 0, 4, None) == 2      # recv == gather
+    assert L.twoshot_reduce(FAKE, FAKE + 0x100000, 2, 8, 64, 0, 0, 4, None) == 1
+    assert L.twoshot_read(FAKE, FAKE, 2, 64, 7168, 0, 4, None) == 2           # out == gather
+    assert L.twoshot_read(FAKE, MIS, 2, 64, 7168, 0, 4, None) == 2
+    assert L.twoshot_read(FAKE, FAKE + 0x100000, 2, 64, 7168, 0, 0, None) == 1
+
+
 def test_spin_limit_and_threads(L):
     old = L.arnorm_get_spin_limit()
     assert L.arnorm_set_spin_limit(0) == 2
@@ -136,5 +151,6 @@ def test_spin_limit_and_threads(L):
 def test_binding_mirrors_the_abi():
     from tp_all_reduce_arnorm_amd import _lib
 
-    for n in ("lamport_arm", "arnorm_push", "arnorm_reduce_norm", "gather_push", "gather_poll"):
+    for n in ("lamport_arm", "arnorm_push", "arnorm_reduce_norm", "gather_push", "gather_poll", "twoshot_push",
+              "twoshot_reduce", "twoshot_read"):
         assert callable(getattr(_lib, n))

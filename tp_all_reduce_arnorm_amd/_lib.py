@@ -30,6 +30,10 @@ _SIGNATURES = {
                                     _c_int, _c_int, _c_int, _c_float, _c_ptr]),
     "gather_push": (_c_int, [_c_ptr, _c_ptr, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_ptr]),
     "gather_poll": (_c_int, [_c_ptr, _c_ptr, _c_int, _c_int, _c_int, _c_int, _c_int, _c_ptr]),
+    "twoshot_push": (_c_int, [_c_ptr, _c_ptr, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
+                              _c_ptr]),
+    "twoshot_reduce": (_c_int, [_c_ptr, _c_ptr, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_ptr]),
+    "twoshot_read": (_c_int, [_c_ptr, _c_ptr, _c_int, _c_int, _c_int, _c_int, _c_int, _c_ptr]),
     "arnorm_set_spin_limit": (_c_int, [_c_u64]),
     "arnorm_get_spin_limit": (_c_u64, []),
     "arnorm_set_reduce_threads": (_c_int, [_c_int]),
@@ -133,6 +137,34 @@ def gather_poll(mailbox, tp, m, out=None, copy=True, stream=None):
     return _check("gather_poll", LIB.gather_poll(
         _ptr(mailbox, 4, "mailbox"), _ptr(out, 4, "out") if copy else None, tp, cap, s, m, 1 if copy else 0,
         _stream(stream)))
+
+
+def twoshot_push(partial, recv, parity, rank, stream=None):
+    """partial: BF16 [nslots, M, width]; recv: int32 [parities, tp, cap, width/2]."""
+    nslots, m, width = partial.shape
+    p, tp, cap, words = recv.shape
+    assert words * 2 == width
+    return _check("twoshot_push", LIB.twoshot_push(
+        _ptr(partial, 2, "partial"), _ptr(recv, 4, "recv"), p, tp, cap, width, parity, rank, nslots, m,
+        _stream(stream)))
+
+
+def twoshot_reduce(recv, gather, parity, m, stream=None):
+    """The owner's reduce of rows < m: recv int32 [parities, tp, cap, width/2] into the
+    gather row int32 [parities, 1, cap, width/2]."""
+    p, tp, cap, words = recv.shape
+    assert tuple(gather.shape) == (p, 1, cap, words)
+    return _check("twoshot_reduce", LIB.twoshot_reduce(
+        _ptr(recv, 4, "recv"), _ptr(gather, 4, "gather"), p, tp, cap, 2 * words, parity, m, _stream(stream)))
+
+
+def twoshot_read(gather, parity, out, stream=None):
+    """A reader of the gather row: rows < M (M = out.shape[0]) into out (BF16 [M, width])."""
+    p, _, cap, words = gather.shape
+    m, width = out.shape
+    assert width == 2 * words
+    return _check("twoshot_read", LIB.twoshot_read(
+        _ptr(gather, 4, "gather"), _ptr(out, 2, "out"), p, cap, width, parity, m, _stream(stream)))
 
 
 def set_spin_limit(polls):

@@ -17,7 +17,8 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libarnorm.so")
 SOURCES = [os.path.join(CSRC, "libarnorm.hip")]
-HEADERS = [os.path.join(CSRC, n) for n in ("device.hpp", "arnorm_kernels.hpp", "gather_kernels.hpp")] + [
+HEADERS = [os.path.join(CSRC, n) for n in ("device.hpp", "arnorm_kernels.hpp", "gather_kernels.hpp",
+                                           "twoshot_kernels.hpp")] + [
     os.path.join(INCLUDE, "arnorm.h")
 ]
 

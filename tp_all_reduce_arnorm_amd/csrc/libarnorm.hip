@@ -10,6 +10,7 @@
 #include "arnorm.h"
 #include "arnorm_kernels.hpp"
 #include "gather_kernels.hpp"
+#include "twoshot_kernels.hpp"
 
 namespace {
 
@@ -81,6 +82,19 @@ int check_gather(int tp, int cap, int S, int M) {
   return ARNORM_OK;
 }
 
+int check_twoshot(int parities, int cap, int width, int parity, int M) {
+  if (width < 8 || width % 8 != 0) return ARNORM_NOT_SERVED;
+  if (cap < 1 || parities < 1) return ARNORM_BAD_ARG;
+  if (parity < 0 || parity >= parities) return ARNORM_BAD_ARG;
+  if (M < 1 || M > cap) return ARNORM_NOT_SERVED;
+  if ((uint64_t)M * width * 2 >= (uint64_t(1) << 31)) return ARNORM_NOT_SERVED;
+  return ARNORM_OK;
+}
+
+// A row-block poll with copy (the Gather consumer): rows < M of `box`, row_frags
+// fragments each; about one fragment per thread, the grid resident at once.
+int launch_poll(uint8_t *box, u32x4 *out, uint32_t row_frags, int M, int copy, hipStream_t stream);
+
 uint8_t *parity_base(int32_t *mailbox, int parity, int tp, int cap) {
   return reinterpret_cast<uint8_t *>(mailbox) + (size_t)parity * tp * cap * arn::kRowBytes;
 }
@@ -115,6 +129,15 @@ int reduce_threads(int M) {
   if (forced) return forced;
   (void)M;
   return 896;
+}
+
+int launch_poll(uint8_t *box, u32x4 *out, uint32_t row_frags, int M, int copy, hipStream_t stream) {
+  // about one fragment per thread, the whole grid resident at once (at most 2048
+  // workgroups of 256 threads over 256 CUs), at least one workgroup per row
+  const uint32_t want = (row_frags + 255) / 256;
+  const uint32_t ctas = std::max(1u, std::min(want, 2048u / (uint32_t)M));
+  return launch(arn::gather_poll_kernel<kPolPoll, kPolRearm>, dim3(ctas, (unsigned)M), dim3(256), stream, box, out,
+                row_frags, copy ? 1 : 0, (uint64_t)g_spin_limit.load(std::memory_order_relaxed));
 }
 
 }  // namespace
@@ -207,14 +230,62 @@ int gather_poll(int32_t *mailbox, int32_t *out, int tp, int cap, int S, int M, i
   if (rc != ARNORM_OK) return rc;
   if (!aligned16(mailbox) || (copy && !aligned16(out))) return ARNORM_BAD_ARG;
   if (copy && static_cast<void *>(out) == static_cast<void *>(mailbox)) return ARNORM_BAD_ARG;
-  const uint32_t row_frags = (uint32_t)tp * S / 4;
-  // about one fragment per thread, the whole grid resident at once (at most 2048
-  // workgroups of 256 threads over 256 CUs), at least one workgroup per row
-  const uint32_t want = (row_frags + 255) / 256;
-  const uint32_t ctas = std::max(1u, std::min(want, 2048u / (uint32_t)M));
-  return launch(arn::gather_poll_kernel<kPolPoll, kPolRearm>, dim3(ctas, (unsigned)M), dim3(256), stream,
-                reinterpret_cast<uint8_t *>(mailbox), reinterpret_cast<u32x4 *>(out), row_frags, copy ? 1 : 0,
-                (uint64_t)g_spin_limit.load(std::memory_order_relaxed));
+  return launch_poll(reinterpret_cast<uint8_t *>(mailbox), reinterpret_cast<u32x4 *>(out), (uint32_t)tp * S / 4, M,
+                     copy, stream);
+}
+
+int twoshot_push(const uint16_t *partial, int32_t *recv, int parities, int tp, int cap, int width, int parity,
+                 int rank, int nslots, int M, hipStream_t stream) {
+  if (tp < 2 || tp > 8) return ARNORM_NOT_SERVED;
+  int rc = check_twoshot(parities, cap, width, parity, M);
+  if (rc != ARNORM_OK) return rc;
+  if (rank < 0 || nslots < 1 || rank + nslots > tp) return ARNORM_BAD_ARG;
+  if (!aligned16(partial) || !aligned16(recv)) return ARNORM_BAD_ARG;
+  constexpr int U = ARNORM_PUSH_U;
+  const size_t row_bytes = (size_t)width * 2;
+  const uint32_t frags = (uint32_t)((size_t)M * row_bytes / 16);
+  const uint32_t want = (frags + 256 * U - 1) / (256 * U);
+  const dim3 grid(std::max(1u, std::min(want, 1024u)), (unsigned)nslots);
+  uint8_t *first = reinterpret_cast<uint8_t *>(recv) + ((size_t)parity * tp + rank) * cap * row_bytes;
+  return launch(arn::push_kernel<U, kPolPush>, grid, dim3(256), stream, reinterpret_cast<const u32x4 *>(partial),
+                first, (size_t)cap * row_bytes, frags);
+}
+
+int twoshot_reduce(int32_t *recv, int32_t *gather, int parities, int tp, int cap, int width, int parity, int M,
+                   hipStream_t stream) {
+  if (tp < 2 || tp > 8) return ARNORM_NOT_SERVED;
+  int rc = check_twoshot(parities, cap, width, parity, M);
+  if (rc != ARNORM_OK) return rc;
+  if (!aligned16(recv) || !aligned16(gather) || recv == gather) return ARNORM_BAD_ARG;
+  const size_t row_bytes = (size_t)width * 2;
+  arn::TwoShotArgs a;
+  a.recv = reinterpret_cast<uint8_t *>(recv) + (size_t)parity * tp * cap * row_bytes;
+  a.gather = reinterpret_cast<uint8_t *>(gather) + (size_t)parity * cap * row_bytes;
+  a.slot_stride = (size_t)cap * row_bytes;
+  a.frags = (uint32_t)((size_t)M * row_bytes / 16);
+  a.spin_limit = g_spin_limit.load(std::memory_order_relaxed);
+  const dim3 grid(std::max(1u, std::min((a.frags + 255) / 256, 16384u)));
+  switch (tp) {
+    case 2: return launch(arn::twoshot_reduce_kernel<2, kPolPoll, kPolRearm, kPolPush>, grid, dim3(256), stream, a);
+    case 3: return launch(arn::twoshot_reduce_kernel<3, kPolPoll, kPolRearm, kPolPush>, grid, dim3(256), stream, a);
+    case 4: return launch(arn::twoshot_reduce_kernel<4, kPolPoll, kPolRearm, kPolPush>, grid, dim3(256), stream, a);
+    case 5: return launch(arn::twoshot_reduce_kernel<5, kPolPoll, kPolRearm, kPolPush>, grid, dim3(256), stream, a);
+    case 6: return launch(arn::twoshot_reduce_kernel<6, kPolPoll, kPolRearm, kPolPush>, grid, dim3(256), stream, a);
+    case 7: return launch(arn::twoshot_reduce_kernel<7, kPolPoll, kPolRearm, kPolPush>, grid, dim3(256), stream, a);
+    case 8: return launch(arn::twoshot_reduce_kernel<8, kPolPoll, kPolRearm, kPolPush>, grid, dim3(256), stream, a);
+  }
+  return ARNORM_NOT_SERVED;
+}
+
+int twoshot_read(int32_t *gather, uint16_t *out, int parities, int cap, int width, int parity, int M,
+                 hipStream_t stream) {
+  int rc = check_twoshot(parities, cap, width, parity, M);
+  if (rc != ARNORM_OK) return rc;
+  if (!aligned16(gather) || !aligned16(out)) return ARNORM_BAD_ARG;
+  if (static_cast<void *>(out) == static_cast<void *>(gather)) return ARNORM_BAD_ARG;
+  const size_t row_bytes = (size_t)width * 2;
+  return launch_poll(reinterpret_cast<uint8_t *>(gather) + (size_t)parity * cap * row_bytes,
+                     reinterpret_cast<u32x4 *>(out), (uint32_t)(row_bytes / 16), M, 1, stream);
 }
 
 int arnorm_set_spin_limit(uint64_t polls) {
