@@ -129,13 +129,15 @@ def gather_bytes(tp, m, s, copy=True):
     return 2 * words * 4, (3 if copy else 1) * words * 4
 
 
-def time_gather(lib, torch, calls=1000, chunk=50):
-    """µs per Gather call at TP=8, M=32, S=896 (gather_push of the 8 ranks' shards,
-    then gather_poll with copy), graph-replayed."""
+def time_gather(lib, torch, calls=1000, chunk=50, name="c4"):
+    """µs per Gather call (gather_push of the 8 ranks' shards, then gather_poll with
+    copy), graph-replayed: c4 is TP=8, M=32, S=896; ctx and logits are the drafter's
+    context-projection and lm_head shapes."""
     from tp_all_reduce_arnorm_amd import workloads as wl
 
-    cfg = wl.CONFIGS["c4"]
-    shards = torch.from_numpy(wl.gather_shards(cfg).view(np.int32)).cuda()
+    cfg = wl.CONFIGS[name]
+    words = wl.gather_shards(cfg) if name == "c4" else wl.bf16_shards(cfg)
+    shards = torch.from_numpy(words.view(np.int32)).cuda()
     box = torch.empty((cfg.cap, cfg.tp * cfg.s), dtype=torch.int32, device="cuda")
     assert lib.lamport_arm(box) is True
     out = torch.empty((cfg.m, cfg.tp * cfg.s), dtype=torch.int32, device="cuda")
@@ -451,6 +453,12 @@ def main():
     cfg5, red_us, push_us = time_roofline(lib, torch)
     cfg4, gather_us = time_gather(lib, torch)
     ts = time_twoshot(lib, torch)
+    shapes = {}
+    for name in ("ctx", "logits"):
+        c, us = time_gather(lib, torch, name=name)
+        shapes[name] = {"tp": c.tp, "m": c.m, "s_words": c.s, "us_per_call": round(us, 3),
+                        "push_algorithmic_bytes": gather_bytes(c.tp, c.m, c.s)[0],
+                        "poll_algorithmic_bytes": gather_bytes(c.tp, c.m, c.s)[1]}
     tsr, tsq = twoshot_bytes(8, 4096)
     gpb, gqb = gather_bytes(cfg4.tp, cfg4.m, cfg4.s)
     rb = reduce_bytes(cfg5.tp, cfg5.m, True)
@@ -503,6 +511,7 @@ def main():
             "workload": "Gather TP=8 M=32 S=896 words cap=64, gather_push of 8 slots + gather_poll "
                         "with copy, HIP-graph replay",
             "us_per_call": round(gather_us, 3), "push_algorithmic_bytes": gpb, "poll_algorithmic_bytes": gqb,
+            "drafter_shapes": shapes,
         },
         "twoshot": {
             "workload": "two-shot all-reduce, owners = 1: push of 8 slots + owner's reduce + read of the "

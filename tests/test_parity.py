@@ -131,6 +131,40 @@ def test_c4_gather(lib):
             assert np.array_equal(blk[src != S0], src[src != S0]) and np.all(blk[src == S0] == 0)
 
 
+@pytest.mark.parametrize("name,m,tp", [("ctx", 64, 8), ("ctx", 1, 8), ("ctx", 7, 4), ("ctx", 3, 2),
+                                        ("logits", 4, 8), ("logits", 1, 8)])
+def test_drafter_gather_shapes(lib, name, m, tp):
+    """The drafter's own gathers: the context projection's [M, 7168/TP] BF16 rows and
+    the lm_head's [M, V/TP] logits, moved as 32-bit words of BF16 pairs; bit-exact."""
+    import dataclasses
+
+    import torch
+
+    say(f"[parity] drafter gather {name} M={m} TP={tp}")
+    base = wl.CONFIGS[name]
+    s = base.s * base.tp // tp  # same row width at another TP
+    cfg = dataclasses.replace(base, m=m, tp=tp, s=s)
+    shards = wl.bf16_shards(cfg)
+    gshape = (cfg.cap, cfg.tp * cfg.s)
+    gbox_d, gbox_h = armed_box(gshape), oracle.arm(np.empty(gshape, dtype=np.uint32))
+    for rank in range(tp):
+        assert lib.gather_push(dev32(shards[rank:rank + 1]), gbox_d, tp, rank) is True
+        oracle.gather_push(gbox_h, shards[rank:rank + 1], rank)
+    out_d = torch.empty((m, tp * s), dtype=torch.int32, device="cuda")
+    assert lib.gather_poll(gbox_d, tp, m, out=out_d, copy=True) is True
+    want = oracle.gather_poll(gbox_h, m, True)
+    assert lib.status() == lib.OK
+    assert_bits_equal(host32(out_d), want, "gathered words")
+    assert_bits_equal(host32(gbox_d), gbox_h, "gather mailbox")
+    # as BF16: the gathered row is the shards side by side, only (+0, -0) pairs made (+0, +0)
+    row = oracle.unpack_pairs(want)
+    for r in range(tp):
+        src = oracle.unpack_pairs(shards[r])
+        blk = row[:, r * 2 * s:(r + 1) * 2 * s]
+        sent = (src[:, 0::2] == 0) & (src[:, 1::2] == 0x8000)
+        assert np.array_equal(blk[:, 1::2][~sent], src[:, 1::2][~sent]) and np.all(blk[:, 1::2][sent] == 0)
+
+
 def test_c5_full_size_sampled_rows(lib):
     """M = 4096, TP = 8, in the launch configuration the benchmark times; the oracle
     checks a sample of rows one by one (rows are independent), and the whole mailbox

@@ -21,6 +21,10 @@ rows M = tokens in flight, TP slots playing the ranks of the one-GPU stand-in):
       61 calls over 2 parities, seed 2
   c4  Gather TP=8, M=32, S=896 words, cap=64, uniform words with 3 % sentinel, seed 3
   c5  ArNorm TP=8, M=4096, residual, partials and residual N(0, 1), seed 4
+  ctx     Gather of the context projection: TP=8, [M=64, 896] BF16 shards (448 words),
+          N(0, 1) with 1 % of values -0, seed 5
+  logits  Gather of the lm_head logits: TP=8, [M=4, 20480] BF16 shards (10240 words) of
+          a synthetic V = 163840, N(0, 1) with 1 % of values -0, seed 6
 """
 
 from dataclasses import dataclass, field
@@ -79,6 +83,15 @@ CONFIGS = {
     "c4": GatherConfig(
         "c4", tp=8, m=32, s=896, cap=64, sentinel_frac=0.03, seed=3,
         description="Gather TP=8, [M=32, S=896] word shards into [cap=64, 8*896]"),
+    # the drafter's own gather shapes: the context projection's [M, 7168/TP] BF16 rows
+    # and the lm_head's [M, V/TP] BF16 logits (V = 163840, a synthetic vocabulary: the
+    # pages print none), as 32-bit words of BF16 pairs
+    "ctx": GatherConfig(
+        "ctx", tp=8, m=64, s=448, cap=64, sentinel_frac=0.0, seed=5,
+        description="context-projection gather: TP=8, [M=64, 896] BF16 shards -> [M, 7168]"),
+    "logits": GatherConfig(
+        "logits", tp=8, m=4, s=10240, cap=64, sentinel_frac=0.0, seed=6,
+        description="lm_head logits gather: TP=8, [M=4, 20480] BF16 shards -> [M, 163840]"),
     "c5": ArNormConfig(
         "c5", tp=8, m=4096, cap=4096, parities=1, residual=True, sigma_partial=1.0,
         sigma_residual=1.0, seed=4,
@@ -168,6 +181,19 @@ class ArNormInputs:
     def call(self):
         p = self.partials()
         return p, self.residual()
+
+
+def bf16_shards(cfg: GatherConfig, sigma=1.0, neg_zero_frac=0.01):
+    """Seeded BF16 shards as uint32 [TP, M, S] words: sigma * N(0, 1) values, with about
+    ``neg_zero_frac`` of the BF16 values set to -0 (so some words are the sentinel pair
+    and others other -0 patterns, as real BF16 activations and logits can hold)."""
+    rng = np.random.default_rng(cfg.seed)
+    h = bf16_normal(rng, (cfg.tp, cfg.m, 2 * cfg.s), sigma)
+    h[rng.random(size=h.shape) < neg_zero_frac] = 0x8000
+    h[..., 0::2][rng.random(size=h[..., 0::2].shape) < neg_zero_frac] = 0x0000
+    lo = h[..., 0::2].astype(np.uint32)
+    hi = h[..., 1::2].astype(np.uint32)
+    return lo | (hi << np.uint32(16))
 
 
 def gather_shards(cfg: GatherConfig):
