@@ -273,6 +273,21 @@ def pmc_workload(lib, torch, launches=3):
     TP=8, M=4096 with residual, and a plain 1 GiB device copy (torch's copy kernel)
     whose FETCH_SIZE / WRITE_SIZE calibrate the counters against known bytes."""
     cfg, red_us, push_us = time_roofline(lib, torch, launches=launches)
+    # the two-shot owner's reduce and the gather-row read at the same size
+    from tp_all_reduce_arnorm_amd import workloads as wl
+
+    p5 = torch.from_numpy(wl.ArNormInputs(cfg).partials().view(np.int16)).cuda()
+    recv = torch.empty((1, cfg.tp, cfg.cap, HIDDEN // 2), dtype=torch.int32, device="cuda")
+    gath = torch.empty((1, 1, cfg.cap, HIDDEN // 2), dtype=torch.int32, device="cuda")
+    out = torch.empty((cfg.m, HIDDEN), dtype=torch.int16, device="cuda")
+    assert lib.lamport_arm(recv) is True and lib.lamport_arm(gath) is True
+    for _ in range(launches):
+        assert lib.twoshot_push(p5, recv, 0, 0) is True
+        assert lib.twoshot_reduce(recv, gath, 0, cfg.m) is True
+        assert lib.twoshot_read(gath, 0, out) is True
+    torch.cuda.synchronize()
+    assert lib.status() == lib.OK
+    del p5, recv, gath, out
     n = 1 << 28  # int32 elements: 1 GiB
     a = torch.ones(n, dtype=torch.int32, device="cuda")
     b = torch.empty_like(a)
@@ -310,16 +325,29 @@ def cpu_baseline(budget_s=10.0):
 
 PROFILE_COMMANDS = {
     "lat": "rocprofv3 --kernel-trace --stats -f csv -d gpurun_out/prof_lat -o lat -- "
-           "python bench.py --mode latency --steps 2000",
+           "python bench.py --mode latency --steps 2000 > gpurun_out/prof_lat.log 2>&1",
     "roof": "rocprofv3 --kernel-trace --stats -f csv -d gpurun_out/prof_roof -o roof -- "
-            "python bench.py --mode roofline",
+            "python bench.py --mode roofline > gpurun_out/prof_roof.log 2>&1",
     "gather": "rocprofv3 --kernel-trace --stats -f csv -d gpurun_out/prof_gather -o gather -- "
-              "python bench.py --mode gather",
+              "python bench.py --mode gather > gpurun_out/prof_gather.log 2>&1",
     "twoshot": "rocprofv3 --kernel-trace --stats -f csv -d gpurun_out/prof_twoshot -o twoshot -- "
-               "python bench.py --mode twoshot",
-    "fetch": "rocprofv3 --pmc FETCH_SIZE -f csv -d gpurun_out/pmc_fetch -o fetch -- python bench.py --mode pmc",
-    "write": "rocprofv3 --pmc WRITE_SIZE -f csv -d gpurun_out/pmc_write -o write -- python bench.py --mode pmc",
+               "python bench.py --mode twoshot > gpurun_out/prof_twoshot.log 2>&1",
+    "fetch": "rocprofv3 --pmc FETCH_SIZE -f csv -d gpurun_out/pmc_fetch -o fetch -- "
+             "python bench.py --mode pmc > gpurun_out/pmc_fetch.log 2>&1",
+    "write": "rocprofv3 --pmc WRITE_SIZE -f csv -d gpurun_out/pmc_write -o write -- "
+             "python bench.py --mode pmc > gpurun_out/pmc_write.log 2>&1",
 }
+
+
+def _profiled_sha(log_path):
+    """The kernel-sources hash that a profiled bench run printed (None if absent)."""
+    try:
+        for ln in open(log_path, errors="replace"):
+            if ln.startswith('{"mode"'):
+                return json.loads(ln).get("sources_sha")
+    except OSError:
+        pass
+    return None
 
 
 def _short(name):
@@ -344,7 +372,6 @@ def summarize_profiles(outdir):
 
     prof = os.path.join(ROOT, "profiles")
     os.makedirs(prof, exist_ok=True)
-    sha = kernel_sources_hash()
     for key, title, fname in (
             ("lat", "Stand-in ArNorm call at TP=8, M=4, no residual (arnorm_push of 8 slots + "
                     "arnorm_reduce_norm, HIP-graph replay, 2000 calls)", "arnorm_tp8_m4_kernel_stats.md"),
@@ -357,6 +384,7 @@ def summarize_profiles(outdir):
         if not os.path.exists(os.path.join(outdir, f"prof_{key}", f"{key}_kernel_stats.csv")):
             continue
         rows, table = _stats_table(os.path.join(outdir, f"prof_{key}", f"{key}_kernel_stats.csv"))
+        sha = _profiled_sha(os.path.join(outdir, f"prof_{key}.log"))
         with open(os.path.join(prof, fname), "w") as f:
             f.write(f"# rocprofv3 kernel statistics: {title}\n\n"
                     f"Command, from the repository root on one MI355X:\n\n    {PROFILE_COMMANDS[key]}\n\n"
@@ -367,6 +395,9 @@ def summarize_profiles(outdir):
         return list(csv.DictReader(open(path)))
 
     fetch, write = counters("fetch"), counters("write")
+    sha = _profiled_sha(os.path.join(outdir, "pmc_fetch.log"))
+    if sha is None or sha != _profiled_sha(os.path.join(outdir, "pmc_write.log")):
+        raise SystemExit("the two counter runs do not name the same kernel sources")
 
     def calib(rows):
         copies = [r for r in rows if "copyBuffer" in r["Kernel_Name"]]
@@ -382,7 +413,9 @@ def summarize_profiles(outdir):
         return float(np.mean(vals)), len(vals)
 
     kernels = (("reduce_norm_tp8_m4096_res", "reduce_norm_kernel<8, true, false, 896", reduce_bytes(8, 4096, True)),
-               ("push_tp8_m4096", "push_kernel", push_bytes(8, 4096)))
+               ("push_tp8_m4096", "push_kernel", push_bytes(8, 4096)),
+               ("twoshot_reduce_tp8_m4096", "twoshot_reduce_kernel<8", twoshot_bytes(8, 4096)[0]),
+               ("twoshot_read_m4096", "gather_poll_kernel", twoshot_bytes(8, 4096)[1]))
     rec, lines = {}, []
     for key, pat, alg in kernels:
         fr, n = per_launch(fetch, pat)
@@ -395,7 +428,8 @@ def summarize_profiles(outdir):
     with open(os.path.join(prof, "hbm_traffic.json"), "w") as f:
         json.dump(rec, f, indent=1)
     with open(os.path.join(prof, "arnorm_tp8_m4096_hbm_traffic.md"), "w") as f:
-        f.write("# HBM traffic per launch from rocprofv3 counters: TP=8, M=4096, residual\n\n"
+        f.write("# HBM traffic per launch from rocprofv3 counters: TP=8, M=4096 (ArNorm with residual; "
+                "the two-shot stand-in)\n\n"
                 "Commands, from the repository root on one MI355X (two runs, one counter each):\n\n"
                 f"    {PROFILE_COMMANDS['fetch']}\n    {PROFILE_COMMANDS['write']}\n\n"
                 f"Kernel sources sha256[:16] = `{sha}`.\n\n"
@@ -431,23 +465,26 @@ def main():
     from tp_all_reduce_arnorm_amd import _lib as lib
 
     torch.cuda.set_device(0)
+    sha = kernel_sources_hash()
     if args.mode == "latency":
         elapsed = time_latency(lib, torch, args.steps, args.warmup)
-        print(json.dumps({"mode": "latency", "us_per_call": elapsed / args.steps * 1e6}), flush=True)
+        print(json.dumps({"mode": "latency", "us_per_call": elapsed / args.steps * 1e6, "sources_sha": sha}),
+              flush=True)
         return
     if args.mode == "roofline":
         _, red_us, push_us = time_roofline(lib, torch)
-        print(json.dumps({"mode": "roofline", "reduce_us": red_us, "push_us": push_us}), flush=True)
+        print(json.dumps({"mode": "roofline", "reduce_us": red_us, "push_us": push_us, "sources_sha": sha}),
+              flush=True)
         return
     if args.mode == "gather":
         _, us = time_gather(lib, torch)
-        print(json.dumps({"mode": "gather", "us_per_call": us}), flush=True)
+        print(json.dumps({"mode": "gather", "us_per_call": us, "sources_sha": sha}), flush=True)
         return
     if args.mode == "twoshot":
-        print(json.dumps(dict(mode="twoshot", **time_twoshot(lib, torch))), flush=True)
+        print(json.dumps(dict(mode="twoshot", sources_sha=sha, **time_twoshot(lib, torch))), flush=True)
         return
     if args.mode == "pmc":
-        print(json.dumps(dict(mode="pmc", **pmc_workload(lib, torch))), flush=True)
+        print(json.dumps(dict(mode="pmc", sources_sha=sha, **pmc_workload(lib, torch))), flush=True)
         return
     elapsed = time_latency(lib, torch, args.steps, args.warmup)
     cfg5, red_us, push_us = time_roofline(lib, torch)
