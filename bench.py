@@ -79,7 +79,8 @@ def time_latency(lib, torch, steps, warmup, chunk=50):
     cfg = wl.CONFIGS["c2"]
     src = wl.ArNormInputs(cfg)
     box = torch.empty((2, cfg.tp, cfg.cap, HIDDEN // 2), dtype=torch.int32, device="cuda")
-    assert lib.lamport_arm(box) is True
+    nbox = torch.empty((2, cfg.cap, 256), dtype=torch.int32, device="cuda")
+    assert lib.lamport_arm(box) is True and lib.lamport_arm(nbox) is True
     parts = [torch.from_numpy(src.partials().view(np.int16)).cuda() for _ in range(2)]
     gamma = torch.from_numpy(src.gamma.view(np.int16)).cuda()
     outs = [(torch.empty((cfg.m, HIDDEN), dtype=torch.int16, device="cuda"),
@@ -88,7 +89,8 @@ def time_latency(lib, torch, steps, warmup, chunk=50):
     def call(i):
         parity = i % 2
         assert lib.arnorm_push(parts[parity], box, parity, 0) is True
-        assert lib.arnorm_reduce_norm(None, gamma, box, parity, EPS, outs[parity][0], outs[parity][1]) is True
+        assert lib.arnorm_reduce_norm(None, gamma, box, parity, EPS, outs[parity][0], outs[parity][1],
+                                      norm_box=nbox) is True
 
     def capture(n):
         g = torch.cuda.CUDAGraph()
@@ -524,7 +526,8 @@ def main():
         "data": "synthetic",
         "config": {
             "workload": "ArNorm TP=8 M=4 width 7168, residual=False, 2 parities alternating "
-                        "(arnorm_push of 8 slots + arnorm_reduce_norm per call, HIP-graph replay)",
+                        "(arnorm_push of 8 slots + arnorm_reduce_norm with its norm box, rows split over "
+                        "7 workgroups, per call; HIP-graph replay)",
             "tp": 8, "m": 4, "hidden": HIDDEN, "parities": 2, "residual": False,
         },
         "roofline": {

@@ -84,12 +84,12 @@ def test_push_bad_args(L, args):
 
 def reduce_rc(L, **kw):
     a = dict(partial=None, residual=FAKE + 0x100000, gamma=FAKE + 0x200000, out=FAKE + 0x300000,
-             residual_out=FAKE + 0x400000, mailbox=FAKE + 0x500000, parities=2, tp=8, cap=64, parity=0,
-             rank=0, M=4, eps=1e-6)
+             residual_out=FAKE + 0x400000, mailbox=FAKE + 0x500000, norm_box=None, parities=2, tp=8, cap=64,
+             parity=0, rank=0, M=4, eps=1e-6)
     a.update(kw)
     return L.arnorm_reduce_norm(a["partial"], a["residual"], a["gamma"], a["out"], a["residual_out"],
-                                a["mailbox"], a["parities"], a["tp"], a["cap"], a["parity"], a["rank"], a["M"],
-                                a["eps"], None)
+                                a["mailbox"], a["norm_box"], a["parities"], a["tp"], a["cap"], a["parity"],
+                                a["rank"], a["M"], a["eps"], None)
 
 
 def test_reduce_checks(L):
@@ -107,6 +107,12 @@ def test_reduce_checks(L):
     assert reduce_rc(L, residual_out=FAKE + 0x300000) == 2
     assert reduce_rc(L, residual_out=FAKE + 0x500000) == 2
     assert reduce_rc(L, out=FAKE + 0x200000) == 2
+    # the norm box: aligned, and no alias of the mailbox or an output
+    assert reduce_rc(L, norm_box=MIS) == 2
+    assert reduce_rc(L, norm_box=FAKE + 0x500000) == 2
+    assert reduce_rc(L, norm_box=FAKE + 0x300000) == 2
+    assert reduce_rc(L, norm_box=FAKE + 0x400000) == 2
+    assert reduce_rc(L, norm_box=FAKE + 0x600000, tp=1) == 1
 
 
 def test_gather_checks(L):
@@ -142,6 +148,9 @@ def test_spin_limit_and_threads(L):
     assert L.arnorm_set_spin_limit(12345) == 0
     assert L.arnorm_get_spin_limit() == 12345
     assert L.arnorm_set_spin_limit(old) == 0
+    assert L.arnorm_set_reduce_split(3) == 2
+    for k in (7, 14, 1, 0):
+        assert L.arnorm_set_reduce_split(k) == 0
     assert L.arnorm_set_reduce_threads(300) == 2
     for t in (896, 448, 256, 0):
         assert L.arnorm_set_reduce_threads(t) == 0

@@ -18,12 +18,19 @@ EPS = 1e-6
 @pytest.fixture(autouse=True)
 def _defaults(lib):
     lib.set_reduce_threads(0)
+    lib.set_reduce_split(0)
     yield
     lib.set_reduce_threads(0)
+    lib.set_reduce_split(0)
+
+
+def norm_box_for(box_shape):
+    """A sentinel-armed norm box [parities, cap, 256] for a mailbox of this shape."""
+    return armed_box((box_shape[0], box_shape[2], 256))
 
 
 def run_call(lib, box_d, box_h, partials, residual, gamma_d, gamma, parity, eps=EPS, pushes=None,
-             fused_rank=None):
+             fused_rank=None, norm_box=None):
     """One ArNorm call on both sides: pushes (list of (rank, nslots)), then the
     consumer; returns after comparing outputs and the whole mailbox."""
     tp = partials.shape[0]
@@ -36,7 +43,7 @@ def run_call(lib, box_d, box_h, partials, residual, gamma_d, gamma, parity, eps=
     res_d = dev16(residual) if residual is not None else None
     part_d = dev16(partials[fused_rank]) if fused_rank is not None else None
     assert lib.arnorm_reduce_norm(res_d, gamma_d, box_d, parity, eps, out_d, rout_d, partial=part_d,
-                                  rank=fused_rank or 0) is True
+                                  rank=fused_rank or 0, norm_box=norm_box) is True
     want_out, want_res = oracle.arnorm_reduce_norm(
         box_h, parity, m, residual, gamma, eps,
         partial=partials[fused_rank] if fused_rank is not None else None, rank=fused_rank or 0)
@@ -45,22 +52,30 @@ def run_call(lib, box_d, box_h, partials, residual, gamma_d, gamma, parity, eps=
     exact_zero = (oracle.widen(want_res) == 0) | (oracle.widen(gamma) == 0)[None, :]
     assert_out_close(host16(out_d), want_out, exact_zero=exact_zero)
     assert_bits_equal(host32(box_d), box_h, "mailbox")
+    if norm_box is not None:
+        assert np.all(host32(norm_box) == S0), "the norm box is left re-armed"
     assert lib.status() == lib.OK
     return got_res
 
 
-def run_config(lib, name, calls=None, threads=0):
+def run_config(lib, name, calls=None, threads=0, split=None):
+    """split None: no norm box (one workgroup per row); else a norm box with
+    arnorm_set_reduce_split(split)."""
     cfg = wl.CONFIGS[name]
-    say(f"[parity] {name} threads={threads}")
+    say(f"[parity] {name} threads={threads} split={split}")
     lib.set_reduce_threads(threads)
     src = wl.ArNormInputs(cfg)
     shape = (cfg.parities, cfg.tp, cfg.cap, W // 2)
     box_d = armed_box(shape)
     box_h = oracle.arm(np.empty(shape, dtype=np.uint32))
+    nbox = None
+    if split is not None:
+        lib.set_reduce_split(split)
+        nbox = norm_box_for(shape)
     gamma_d = dev16(src.gamma)
     for call in range(calls or cfg.calls):
         p, r = src.call()
-        run_call(lib, box_d, box_h, p, r, gamma_d, src.gamma, call % cfg.parities)
+        run_call(lib, box_d, box_h, p, r, gamma_d, src.gamma, call % cfg.parities, norm_box=nbox)
 
 
 def test_c1(lib):
@@ -78,6 +93,14 @@ def test_c3(lib):
 @pytest.mark.parametrize("threads", [448, 256])
 def test_c3_other_workgroup_sizes(lib, threads):
     run_config(lib, "c3", calls=4, threads=threads)
+
+
+@pytest.mark.parametrize("split", [0, 7, 14])
+@pytest.mark.parametrize("name", ["c1", "c2", "c3"])
+def test_split_rows(lib, name, split):
+    """Rows split over 7 or 14 workgroups (and the automatic choice), the row's sum of
+    squares exchanged through the norm box, which every call leaves re-armed."""
+    run_config(lib, name, calls=min(wl.CONFIGS[name].calls, 12), split=split)
 
 
 def test_c3_per_rank_pushes_and_chained_residual(lib):
@@ -253,6 +276,22 @@ def test_all_tp_torture_rows(lib, tp, residual):
         run_call(lib, box_d, box_h, p, res, g_d, gamma, 0)
 
 
+@pytest.mark.parametrize("tp", [2, 5, 8])
+def test_torture_rows_split(lib, tp):
+    say(f"[parity] torture tp={tp} split=14")
+    lib.set_reduce_split(14)
+    rng = np.random.default_rng(150 + tp)
+    m, cap = 13, 17
+    shape = (2, tp, cap, W // 2)
+    box_d, box_h, nbox = armed_box(shape), oracle.arm(np.empty(shape, dtype=np.uint32)), norm_box_for(shape)
+    gamma = (rng.integers(0, 2, W) << 15 | (rng.integers(120, 132, W) << 7) | rng.integers(0, 128, W)).astype(np.uint16)
+    g_d = dev16(gamma)
+    for call in range(3):
+        p = torture_partials(rng, tp, m)
+        res = torture_partials(rng, 1, m)[0] if call % 2 else None
+        run_call(lib, box_d, box_h, p, res, g_d, gamma, call % 2, norm_box=nbox)
+
+
 @pytest.mark.parametrize("threads", [896, 448, 256])
 def test_norm_closed_form_rows(lib, threads):
     """All-zero row, one-hot row, constant row, an eps-dominated row and a row whose
@@ -275,19 +314,24 @@ def test_norm_closed_form_rows(lib, threads):
     assert np.all(got_res[4] == 0)
 
 
-@pytest.mark.parametrize("rank", [0, 3, 7])
-def test_fused_own_push(lib, rank):
+@pytest.mark.parametrize("rank,split", [(0, None), (3, None), (7, None), (3, 7), (5, 14)])
+def test_fused_own_push(lib, rank, split):
     """The one-kernel form: the consumer brings rank `rank`'s row itself."""
-    say(f"[parity] fused own push rank={rank}")
+    say(f"[parity] fused own push rank={rank} split={split}")
     cfg = wl.CONFIGS["c3"]
     src = wl.ArNormInputs(cfg)
     shape = (2, 8, 64, W // 2)
     box_d, box_h = armed_box(shape), oracle.arm(np.empty(shape, dtype=np.uint32))
+    nbox = None
+    if split is not None:
+        lib.set_reduce_split(split)
+        nbox = norm_box_for(shape)
     g_d = dev16(src.gamma)
     for call in range(3):
         p, r = src.call()
         pushes = [(k, 1) for k in range(8) if k != rank]
-        run_call(lib, box_d, box_h, p, r, g_d, src.gamma, call % 2, pushes=pushes, fused_rank=rank)
+        run_call(lib, box_d, box_h, p, r, g_d, src.gamma, call % 2, pushes=pushes, fused_rank=rank,
+                 norm_box=nbox)
 
 
 def test_max_rows_and_single_row(lib):

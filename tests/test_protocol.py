@@ -114,23 +114,26 @@ def test_graph_replay_alternating_parities(lib):
     assert lib.status() == lib.OK
 
 
-@pytest.mark.parametrize("m,residual", [(4, False), (64, True), (1, True)])
-def test_concurrent_consumer_polls_while_producer_pushes(lib, m, residual):
+@pytest.mark.parametrize("m,residual,split", [(4, False, None), (64, True, None), (1, True, None),
+                                              (4, False, 14), (64, True, 7)])
+def test_concurrent_consumer_polls_while_producer_pushes(lib, m, residual, split):
     """The Lamport mode proper: the consumer is launched first on its own stream and
     spins on the mailbox while the producer, delayed on another stream, pushes; no
     kernel boundary orders them.  Every call must match the oracle.  (A spin limit of
     2^16 passes ends the wait early should the two streams ever be serialized.)"""
     import torch
 
-    say(f"[protocol] concurrent consumer-first M={m} residual={residual}")
+    say(f"[protocol] concurrent consumer-first M={m} residual={residual} split={split}")
     old = lib.get_spin_limit()
     lib.set_spin_limit(1 << 16)
+    lib.set_reduce_split(split or 0)
     try:
         rng = np.random.default_rng(40 + m)
         tp, cap = 8, 64
         shape = (2, tp, cap, W // 2)
         box_d = armed_box(shape)
         box_h = oracle.arm(np.empty(shape, dtype=np.uint32))
+        nbox = armed_box((2, cap, 256)) if split else None
         gamma = (np.float32(1) + np.float32(0.1) * rng.standard_normal(W, dtype=np.float32)).view(np.uint32)
         gamma = (gamma >> 16).astype(np.uint16)
         g_d = dev16(gamma)
@@ -148,7 +151,7 @@ def test_concurrent_consumer_polls_while_producer_pushes(lib, m, residual):
             s_prod.wait_stream(cur)
             s_cons.wait_stream(cur)
             with torch.cuda.stream(s_cons):
-                assert lib.arnorm_reduce_norm(res_d, g_d, box_d, parity, EPS, out_d, rout_d) is True
+                assert lib.arnorm_reduce_norm(res_d, g_d, box_d, parity, EPS, out_d, rout_d, norm_box=nbox) is True
             with torch.cuda.stream(s_prod):
                 torch.cuda._sleep(200000)  # hold the producer back so that the consumer spins
                 assert lib.arnorm_push(p_d, box_d, parity, 0) is True
@@ -161,8 +164,11 @@ def test_concurrent_consumer_polls_while_producer_pushes(lib, m, residual):
             assert_bits_equal(host16(rout_d), want_res, f"call {call} residual_out")
             assert_out_close(host16(out_d), want_out, f"call {call} out")
             assert_bits_equal(host32(box_d), box_h, f"call {call} mailbox")
+            if nbox is not None:
+                assert np.all(host32(nbox) == 0x80000000), "the norm box is left re-armed"
     finally:
         lib.set_spin_limit(old)
+        lib.set_reduce_split(0)
 
 
 def test_concurrent_gather_consumer_first(lib):

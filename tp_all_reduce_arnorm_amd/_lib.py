@@ -19,6 +19,7 @@ OK, NOT_SERVED, BAD_ARG, HIP_ERROR, TIMEOUT = 0, 1, 2, 3, 4
 SENTINEL = 0x80000000
 HIDDEN = 7168
 ROW_WORDS = 3584
+NORM_BOX_ROW_WORDS = 256
 
 _c_int, _c_ptr, _c_size, _c_u32, _c_u64, _c_float = (
     ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_uint32, ctypes.c_uint64, ctypes.c_float)
@@ -26,8 +27,8 @@ _c_int, _c_ptr, _c_size, _c_u32, _c_u64, _c_float = (
 _SIGNATURES = {
     "lamport_arm": (_c_int, [_c_ptr, _c_size, _c_u32, _c_ptr]),
     "arnorm_push": (_c_int, [_c_ptr, _c_ptr, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_ptr]),
-    "arnorm_reduce_norm": (_c_int, [_c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_int, _c_int, _c_int,
-                                    _c_int, _c_int, _c_int, _c_float, _c_ptr]),
+    "arnorm_reduce_norm": (_c_int, [_c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_int, _c_int,
+                                    _c_int, _c_int, _c_int, _c_int, _c_float, _c_ptr]),
     "gather_push": (_c_int, [_c_ptr, _c_ptr, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_ptr]),
     "gather_poll": (_c_int, [_c_ptr, _c_ptr, _c_int, _c_int, _c_int, _c_int, _c_int, _c_ptr]),
     "twoshot_push": (_c_int, [_c_ptr, _c_ptr, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
@@ -37,6 +38,7 @@ _SIGNATURES = {
     "arnorm_set_spin_limit": (_c_int, [_c_u64]),
     "arnorm_get_spin_limit": (_c_u64, []),
     "arnorm_set_reduce_threads": (_c_int, [_c_int]),
+    "arnorm_set_reduce_split": (_c_int, [_c_int]),
     "arnorm_status": (_c_int, [ctypes.POINTER(_c_int), _c_ptr]),
     "arnorm_strerror": (ctypes.c_char_p, [_c_int]),
 }
@@ -105,19 +107,22 @@ def arnorm_push(partial, mailbox, parity, rank, stream=None):
 
 
 def arnorm_reduce_norm(residual, gamma, mailbox, parity, eps, out, residual_out, partial=None, rank=0,
-                       stream=None):
+                       norm_box=None, stream=None):
     """Poll, re-arm and reduce rows < M (M = out.shape[0]) of mailbox[parity]; writes
     out and residual_out (BF16 [M, 7168]).  residual None: residual = AR(x).
-    partial (BF16 [M, 7168]) is the fused own-rank push of rank `rank`."""
+    partial (BF16 [M, 7168]) is the fused own-rank push of rank `rank`.  norm_box
+    (int32 [parities, cap, 256], sentinel-armed) lets small-M calls split rows."""
     m, width = out.shape
     if width != HIDDEN:
         return None
     p, tp, cap, words = mailbox.shape
     assert words == ROW_WORDS
+    if norm_box is not None:
+        assert tuple(norm_box.shape) == (p, cap, NORM_BOX_ROW_WORDS)
     return _check("arnorm_reduce_norm", LIB.arnorm_reduce_norm(
         _ptr(partial, 2, "partial"), _ptr(residual, 2, "residual"), _ptr(gamma, 2, "gamma"),
         _ptr(out, 2, "out"), _ptr(residual_out, 2, "residual_out"), _ptr(mailbox, 4, "mailbox"),
-        p, tp, cap, parity, rank, m, float(eps), _stream(stream)))
+        _ptr(norm_box, 4, "norm_box"), p, tp, cap, parity, rank, m, float(eps), _stream(stream)))
 
 
 def gather_push(shard, mailbox, tp, rank, stream=None):
@@ -173,6 +178,10 @@ def set_spin_limit(polls):
 
 def get_spin_limit():
     return int(LIB.arnorm_get_spin_limit())
+
+
+def set_reduce_split(workgroups_per_row):
+    return _check("arnorm_set_reduce_split", LIB.arnorm_set_reduce_split(workgroups_per_row))
 
 
 def set_reduce_threads(threads):

@@ -67,40 +67,46 @@ struct ReduceArgs {
   uint8_t *res_out;         // [M, 14336 B]
   uint8_t *box;             // mailbox[parity]: [TP, cap, 14336 B]
   size_t slot_stride;       // cap * 14336 bytes
+  uint32_t *nbox;           // norm_box[parity]: [cap, 256 words] (split rows only)
   int rank;                 // own slot (FUSED only)
   float eps;
   uint64_t spin_limit;
 };
 
+constexpr int kNormBoxRowWords = 256;  // a row's inbox block: [K readers][K writers], K <= 14
+
 constexpr uint32_t kOffNone = 0x80000000u;  // an offset past every resource
 
-// Occupancy target (waves per SIMD) for each workgroup size: enough for two or more
-// workgroups per CU, so one workgroup's loads overlap another's stores and reduction.
-template <int NT> struct ReduceOccupancy;
-template <> struct ReduceOccupancy<896> { static constexpr int kWaves = ARNORM_WPE_896; };
-template <> struct ReduceOccupancy<448> { static constexpr int kWaves = ARNORM_WPE_448; };
-template <> struct ReduceOccupancy<256> { static constexpr int kWaves = ARNORM_WPE_256; };
+// Occupancy target (waves per SIMD) asked of the compiler for a workgroup size.
+constexpr int reduce_occupancy(int nt) {
+  return nt == 896 ? ARNORM_WPE_896 : nt == 448 ? ARNORM_WPE_448 : nt == 256 ? ARNORM_WPE_256 : 0;
+}
 
-template <int TP, bool RES, bool FUSED, int NT, int POL_LD, int POL_ST, int POL_IO>
-__global__ void __launch_bounds__(NT, ReduceOccupancy<NT>::kWaves) reduce_norm_kernel(ReduceArgs a) {
-  constexpr int NF = (kRowFrags + NT - 1) / NT;
+// K = workgroups per row.  K = 1: one workgroup of NT threads owns the whole row
+// (fragments t, t + NT, ...).  K > 1 (small M, a grid small enough to be resident at
+// once): workgroup k of the row owns fragments k*NT .. k*NT + NT - 1, one per thread
+// (NT * K = 896), so each CU moves 1/K of the row; the row's sum of squares is then
+// exchanged through the sentinel-armed norm box, itself a small Lamport mailbox: each
+// workgroup writes its part into slot k of every peer's inbox, polls its own inbox,
+// adds the K parts in workgroup order and re-arms its inbox.  A part is a sum of FMA
+// products started from +0, so it is never -0, the sentinel word.
+template <int TP, bool RES, bool FUSED, int NT, int K, int POL_LD, int POL_ST, int POL_IO>
+__global__ void __launch_bounds__(NT, reduce_occupancy(NT)) reduce_norm_kernel(ReduceArgs a) {
+  constexpr int NF = K > 1 ? 1 : (kRowFrags + NT - 1) / NT;  // fragments per thread
   constexpr int NW = NT / 64;
   static_assert(NT % 64 == 0 && NW <= 16, "wave64 workgroups of at most 16 waves");
+  static_assert(K == 1 || (NT * K == kRowFrags && K * K <= kNormBoxRowWords), "a split row is K * NT fragments");
   __shared__ float wave_sums[NW];
+  __shared__ float row_total;
 
   const int t = threadIdx.x;
-#if ARNORM_ROW_ORDER == 1
-  // workgroup i runs on XCD i % 8: give each XCD a contiguous block of rows
-  const uint32_t nblk = gridDim.x, xcd = blockIdx.x % 8u, k = blockIdx.x / 8u;
-  const uint32_t per = nblk / 8u, extra = nblk % 8u;
-  const uint32_t row = xcd < extra ? xcd * (per + 1) + k : extra * (per + 1) + (xcd - extra) * per + k;
+  const uint32_t row = blockIdx.x;
+  const uint32_t k = K > 1 ? blockIdx.y : 0;
   const size_t row_off = (size_t)row * kRowBytes;
-#else
-  const size_t row_off = (size_t)blockIdx.x * kRowBytes;
-#endif
+  const uint32_t base = k * NT;  // first fragment of this workgroup's part of the row
   uint32_t off[NF];
 #pragma unroll
-  for (int f = 0; f < NF; ++f) off[f] = (uint32_t)(t + f * NT) * 16u;
+  for (int f = 0; f < NF; ++f) off[f] = (uint32_t)(base + t + f * NT) * 16u;
 
   const __amdgpu_buffer_rsrc_t gam = make_rsrc(a.gamma, kRowBytes);
   const __amdgpu_buffer_rsrc_t resr = make_rsrc(RES ? a.residual + row_off : nullptr, RES ? kRowBytes : 0);
@@ -169,7 +175,7 @@ __global__ void __launch_bounds__(NT, ReduceOccupancy<NT>::kWaves) reduce_norm_k
       const int wbit = __shfl(__ffs(pending) - 1, wl, 64);  // s * NF + f of the witness
       const int ws = wbit / NF, wf = wbit % NF;
       const uint32_t *wp = reinterpret_cast<const uint32_t *>(
-          a.box + ws * a.slot_stride + row_off + (size_t)((t - lane + wl) + wf * NT) * 16u);
+          a.box + ws * a.slot_stride + row_off + (size_t)(base + (t - lane + wl) + wf * NT) * 16u);
       if (!published(load_fragment_coherent(wp))) {
         __builtin_amdgcn_s_sleep(8);
         continue;
@@ -230,6 +236,34 @@ __global__ void __launch_bounds__(NT, ReduceOccupancy<NT>::kWaves) reduce_norm_k
   float total = wave_sums[0];
 #pragma unroll
   for (int w = 1; w < NW; ++w) total = total + wave_sums[w];
+  if constexpr (K > 1) {
+    // `total` is this workgroup's part; wave 0 exchanges it with the row's K workgroups
+    if (t < 64) {
+      uint32_t *inbox = a.nbox + (size_t)row * kNormBoxRowWords;  // [reader][writer]
+      if (t < K) __hip_atomic_store(inbox + t * K + k, __float_as_uint(total), __ATOMIC_RELAXED,
+                                    __HIP_MEMORY_SCOPE_AGENT);
+      uint32_t v = kSentinel;
+      if (t < K) v = __hip_atomic_load(inbox + k * K + t, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      for (uint64_t polls = 0;; ++polls) {
+        if (__ballot(t < K && v == kSentinel) == 0) break;
+        if (polls >= a.spin_limit) {
+          if (t == 0) atomicOr(&g_status, 1u);
+          break;
+        }
+        __builtin_amdgcn_s_sleep(2);
+        if (t < K && v == kSentinel)
+          v = __hip_atomic_load(inbox + k * K + t, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+      float sum = __uint_as_float(__shfl(v, 0, 64));
+#pragma unroll
+      for (int j = 1; j < K; ++j) sum = sum + __uint_as_float(__shfl(v, j, 64));
+      if (t < K && v != kSentinel)
+        __hip_atomic_store(inbox + k * K + t, kSentinel, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (t == 0) row_total = sum;
+    }
+    __syncthreads();
+    total = row_total;
+  }
   const float rstd = 1.0f / sqrtf(total / (float)kHidden + a.eps);  // IEEE div and sqrt
 
 #pragma unroll

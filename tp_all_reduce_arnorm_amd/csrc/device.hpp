@@ -37,11 +37,6 @@ enum : int { kPolPlain = 0, kPolNT = 2, kPolDevice = 16, kPolDeviceNT = 18 };
 #ifndef ARNORM_WPE_256
 #define ARNORM_WPE_256 0
 #endif
-// Row order of the consumer grid: 0 = workgroup i takes row i; 1 = each XCD (the
-// dispatcher sends workgroup i to XCD i % 8) takes a contiguous block of rows.
-#ifndef ARNORM_ROW_ORDER
-#define ARNORM_ROW_ORDER 0
-#endif
 
 // Device status word: bit 0 set when a poll gave up (ARNORM_TIMEOUT).  Written with a
 // vector atomic, read and cleared by the host through its symbol.  The library is one

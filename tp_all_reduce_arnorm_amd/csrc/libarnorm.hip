@@ -18,6 +18,7 @@ using arn::u32x4;
 
 std::atomic<uint64_t> g_spin_limit{uint64_t(1) << 22};
 std::atomic<int> g_reduce_threads{0};
+std::atomic<int> g_reduce_split{0};
 
 // Cache policies (gfx950 cache bits, see device.hpp).  Slot reads, re-arm writes and
 // pushes are device-scope coherent (sc1); the re-arm writes are also non-temporal
@@ -40,6 +41,16 @@ std::atomic<int> g_reduce_threads{0};
 #endif
 #ifndef ARNORM_PUSH_U
 #define ARNORM_PUSH_U 4
+#endif
+// Largest M for which a row is split over 14 (or 7) workgroups when a norm box is given.
+// Measured on MI355X, TP=8, stand-in call (push + consumer): 7 workgroups per row beat
+// one at every M <= 64 (M=4: 5.3 against 6.1 us; M=16: 5.5 against 7.1 us), and 14
+// were slower than 7 everywhere (more exchange, no less per-CU traffic that matters).
+#ifndef ARNORM_SPLIT14_MAX_M
+#define ARNORM_SPLIT14_MAX_M 0
+#endif
+#ifndef ARNORM_SPLIT7_MAX_M
+#define ARNORM_SPLIT7_MAX_M 64
 #endif
 constexpr int kPolPoll = ARNORM_POL_POLL;
 constexpr int kPolRearm = ARNORM_POL_REARM;
@@ -101,11 +112,21 @@ uint8_t *parity_base(int32_t *mailbox, int parity, int tp, int cap) {
 
 template <int TP, bool RES, bool FUSED, int NT>
 int launch_reduce(const arn::ReduceArgs &a, int M, hipStream_t stream) {
-  return launch(arn::reduce_norm_kernel<TP, RES, FUSED, NT, kPolPoll, kPolRearm, kPolIO>, dim3(M), dim3(NT), stream, a);
+  return launch(arn::reduce_norm_kernel<TP, RES, FUSED, NT, 1, kPolPoll, kPolRearm, kPolIO>, dim3(M), dim3(NT), stream,
+                a);
+}
+
+template <int TP, bool RES, bool FUSED, int K>
+int launch_reduce_split(const arn::ReduceArgs &a, int M, hipStream_t stream) {
+  constexpr int NT = arn::kRowFrags / K;
+  return launch(arn::reduce_norm_kernel<TP, RES, FUSED, NT, K, kPolPoll, kPolRearm, kPolIO>, dim3(M, K), dim3(NT),
+                stream, a);
 }
 
 template <int TP, bool RES, bool FUSED>
-int launch_reduce_nt(const arn::ReduceArgs &a, int M, int threads, hipStream_t stream) {
+int launch_reduce_nt(const arn::ReduceArgs &a, int M, int threads, int split, hipStream_t stream) {
+  if (split == 7) return launch_reduce_split<TP, RES, FUSED, 7>(a, M, stream);
+  if (split == 14) return launch_reduce_split<TP, RES, FUSED, 14>(a, M, stream);
   switch (threads) {
     case 896: return launch_reduce<TP, RES, FUSED, 896>(a, M, stream);
     case 448: return launch_reduce<TP, RES, FUSED, 448>(a, M, stream);
@@ -115,20 +136,32 @@ int launch_reduce_nt(const arn::ReduceArgs &a, int M, int threads, hipStream_t s
 }
 
 template <int TP>
-int launch_reduce_tp(const arn::ReduceArgs &a, bool res, bool fused, int M, int threads, hipStream_t stream) {
+int launch_reduce_tp(const arn::ReduceArgs &a, bool res, bool fused, int M, int threads, int split,
+                     hipStream_t stream) {
   if (fused)
-    return res ? launch_reduce_nt<TP, true, true>(a, M, threads, stream)
-               : launch_reduce_nt<TP, false, true>(a, M, threads, stream);
-  return res ? launch_reduce_nt<TP, true, false>(a, M, threads, stream)
-             : launch_reduce_nt<TP, false, false>(a, M, threads, stream);
+    return res ? launch_reduce_nt<TP, true, true>(a, M, threads, split, stream)
+               : launch_reduce_nt<TP, false, true>(a, M, threads, split, stream);
+  return res ? launch_reduce_nt<TP, true, false>(a, M, threads, split, stream)
+             : launch_reduce_nt<TP, false, false>(a, M, threads, split, stream);
 }
 
-// Workgroup size of the consumer: one workgroup per row either way.
+// Workgroup size of the consumer when a row is one workgroup.
 int reduce_threads(int M) {
   const int forced = g_reduce_threads.load(std::memory_order_relaxed);
   if (forced) return forced;
   (void)M;
   return 896;
+}
+
+// Workgroups per row: more than one only with a norm box and a grid small enough to be
+// resident at once (every workgroup of a row waits on its peers' parts).
+constexpr int kSplitMaxGrid = 1024;
+int reduce_split(int M, bool have_box) {
+  if (!have_box) return 1;
+  int k = g_reduce_split.load(std::memory_order_relaxed);
+  if (k == 0) k = M <= ARNORM_SPLIT14_MAX_M ? 14 : M <= ARNORM_SPLIT7_MAX_M ? 7 : 1;
+  if (k > 1 && M * k > kSplitMaxGrid) k = 1;
+  return k;
 }
 
 int launch_poll(uint8_t *box, u32x4 *out, uint32_t row_frags, int M, int copy, hipStream_t stream) {
@@ -171,19 +204,22 @@ int arnorm_push(const uint16_t *partial, int32_t *mailbox, int parities, int tp,
 }
 
 int arnorm_reduce_norm(const uint16_t *partial, const uint16_t *residual, const uint16_t *gamma, uint16_t *out,
-                       uint16_t *residual_out, int32_t *mailbox, int parities, int tp, int cap, int parity,
-                       int rank, int M, float eps, hipStream_t stream) {
+                       uint16_t *residual_out, int32_t *mailbox, int32_t *norm_box, int parities, int tp, int cap,
+                       int parity, int rank, int M, float eps, hipStream_t stream) {
   int rc = check_box(parities, tp, cap, parity, M);
   if (rc != ARNORM_OK) return rc;
   if (partial && (rank < 0 || rank >= tp)) return ARNORM_BAD_ARG;
   if ((partial && !aligned16(partial)) || (residual && !aligned16(residual))) return ARNORM_BAD_ARG;
   if (!aligned16(gamma) || !aligned16(out) || !aligned16(residual_out) || !aligned16(mailbox))
     return ARNORM_BAD_ARG;
-  const void *outs[2] = {out, residual_out};
+  if (norm_box && (!aligned16(norm_box) || norm_box == mailbox)) return ARNORM_BAD_ARG;
+  const void *outs[3] = {out, residual_out, norm_box};
   const void *ins[4] = {partial, residual, gamma, mailbox};
   for (const void *o : outs)
     for (const void *i : ins)
-      if (o == i && !(o == residual_out && i == residual)) return ARNORM_BAD_ARG;
+      if (o && o == i && !(o == residual_out && i == residual)) return ARNORM_BAD_ARG;
+  if (norm_box && (static_cast<void *>(norm_box) == out || static_cast<void *>(norm_box) == residual_out))
+    return ARNORM_BAD_ARG;
   if (out == residual_out) return ARNORM_BAD_ARG;
 
   arn::ReduceArgs a;
@@ -200,14 +236,16 @@ int arnorm_reduce_norm(const uint16_t *partial, const uint16_t *residual, const 
   const bool res = residual != nullptr;
   const bool fused = partial != nullptr;
   const int threads = reduce_threads(M);
+  const int split = reduce_split(M, norm_box != nullptr);
+  a.nbox = norm_box ? reinterpret_cast<uint32_t *>(norm_box) + (size_t)parity * cap * arn::kNormBoxRowWords : nullptr;
   switch (tp) {
-    case 2: return launch_reduce_tp<2>(a, res, fused, M, threads, stream);
-    case 3: return launch_reduce_tp<3>(a, res, fused, M, threads, stream);
-    case 4: return launch_reduce_tp<4>(a, res, fused, M, threads, stream);
-    case 5: return launch_reduce_tp<5>(a, res, fused, M, threads, stream);
-    case 6: return launch_reduce_tp<6>(a, res, fused, M, threads, stream);
-    case 7: return launch_reduce_tp<7>(a, res, fused, M, threads, stream);
-    case 8: return launch_reduce_tp<8>(a, res, fused, M, threads, stream);
+    case 2: return launch_reduce_tp<2>(a, res, fused, M, threads, split, stream);
+    case 3: return launch_reduce_tp<3>(a, res, fused, M, threads, split, stream);
+    case 4: return launch_reduce_tp<4>(a, res, fused, M, threads, split, stream);
+    case 5: return launch_reduce_tp<5>(a, res, fused, M, threads, split, stream);
+    case 6: return launch_reduce_tp<6>(a, res, fused, M, threads, split, stream);
+    case 7: return launch_reduce_tp<7>(a, res, fused, M, threads, split, stream);
+    case 8: return launch_reduce_tp<8>(a, res, fused, M, threads, split, stream);
   }
   return ARNORM_NOT_SERVED;
 }
@@ -295,6 +333,13 @@ int arnorm_set_spin_limit(uint64_t polls) {
 }
 
 uint64_t arnorm_get_spin_limit(void) { return g_spin_limit.load(std::memory_order_relaxed); }
+
+int arnorm_set_reduce_split(int workgroups_per_row) {
+  const int k = workgroups_per_row;
+  if (k != 0 && k != 1 && k != 7 && k != 14) return ARNORM_BAD_ARG;
+  g_reduce_split.store(k, std::memory_order_relaxed);
+  return ARNORM_OK;
+}
 
 int arnorm_set_reduce_threads(int threads) {
   if (threads != 0 && threads != 896 && threads != 448 && threads != 256) return ARNORM_BAD_ARG;
