@@ -72,8 +72,10 @@ def committed_traffic(kernel_key):
     return entry.get("bytes_per_launch")
 
 
-def time_latency(lib, torch, steps, warmup, chunk=50):
-    """µs per stand-in call at TP=8, M=4 (no residual), graph-replayed."""
+def time_latency(lib, torch, steps, warmup, chunk=50, one_launch=True):
+    """µs per stand-in call at TP=8, M=4 (no residual), graph-replayed.  one_launch:
+    arnorm_push_reduce_norm (every rank's push and the consumer in one launch); else the
+    pair arnorm_push + arnorm_reduce_norm."""
     from tp_all_reduce_arnorm_amd import workloads as wl
 
     cfg = wl.CONFIGS["c2"]
@@ -88,6 +90,10 @@ def time_latency(lib, torch, steps, warmup, chunk=50):
 
     def call(i):
         parity = i % 2
+        if one_launch:
+            assert lib.arnorm_push_reduce_norm(parts[parity], None, gamma, box, parity, EPS, outs[parity][0],
+                                               outs[parity][1], norm_box=nbox) is True
+            return
         assert lib.arnorm_push(parts[parity], box, parity, 0) is True
         assert lib.arnorm_reduce_norm(None, gamma, box, parity, EPS, outs[parity][0], outs[parity][1],
                                       norm_box=nbox) is True
@@ -489,6 +495,7 @@ def main():
         print(json.dumps(dict(mode="pmc", sources_sha=sha, **pmc_workload(lib, torch))), flush=True)
         return
     elapsed = time_latency(lib, torch, args.steps, args.warmup)
+    pair_us = time_latency(lib, torch, args.steps, args.warmup, one_launch=False) / args.steps * 1e6
     cfg5, red_us, push_us = time_roofline(lib, torch)
     cfg4, gather_us = time_gather(lib, torch)
     ts = time_twoshot(lib, torch)
@@ -525,10 +532,11 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {
-            "workload": "ArNorm TP=8 M=4 width 7168, residual=False, 2 parities alternating "
-                        "(arnorm_push of 8 slots + arnorm_reduce_norm with its norm box, rows split over "
-                        "7 workgroups, per call; HIP-graph replay)",
+            "workload": "ArNorm TP=8 M=4 width 7168, residual=False, 2 parities alternating: one "
+                        "arnorm_push_reduce_norm per call (the 8 ranks' pushes and the consumer in one "
+                        "launch, rows split over 7 workgroups through the norm box); HIP-graph replay",
             "tp": 8, "m": 4, "hidden": HIDDEN, "parities": 2, "residual": False,
+            "two_launch_us_per_call": round(pair_us, 3),
         },
         "roofline": {
             "bound": "hbm",

@@ -115,6 +115,18 @@ def test_reduce_checks(L):
     assert reduce_rc(L, norm_box=FAKE + 0x600000, tp=1) == 1
 
 
+def test_push_reduce_norm_checks(L):
+    a = (FAKE, FAKE + 0x100000, FAKE + 0x200000, FAKE + 0x300000, FAKE + 0x400000, FAKE + 0x500000,
+         FAKE + 0x600000)
+    assert L.arnorm_push_reduce_norm(*a, 2, 1, 64, 0, 4, 1e-6, None) == 1      # tp 1
+    assert L.arnorm_push_reduce_norm(*a, 2, 8, 64, 0, 65, 1e-6, None) == 1     # M > cap
+    assert L.arnorm_push_reduce_norm(*a, 2, 8, 64, 2, 4, 1e-6, None) == 2      # parity
+    assert L.arnorm_push_reduce_norm(MIS, *a[1:], 2, 8, 64, 0, 4, 1e-6, None) == 2
+    b = list(a)
+    b[6] = FAKE + 0x300000  # norm box aliases out
+    assert L.arnorm_push_reduce_norm(*b, 2, 8, 64, 0, 4, 1e-6, None) == 2
+
+
 def test_gather_checks(L):
     assert L.gather_push(FAKE, FAKE, 1, 64, 896, 0, 1, 32, None) == 1
     assert L.gather_push(FAKE, FAKE, 8, 64, 894, 0, 1, 32, None) == 1  # S % 4
@@ -160,6 +172,6 @@ def test_spin_limit_and_threads(L):
 def test_binding_mirrors_the_abi():
     from tp_all_reduce_arnorm_amd import _lib
 
-    for n in ("lamport_arm", "arnorm_push", "arnorm_reduce_norm", "gather_push", "gather_poll", "twoshot_push",
-              "twoshot_reduce", "twoshot_read"):
+    for n in ("lamport_arm", "arnorm_push", "arnorm_reduce_norm", "arnorm_push_reduce_norm", "gather_push",
+              "gather_poll", "twoshot_push", "twoshot_reduce", "twoshot_read"):
         assert callable(getattr(_lib, n))

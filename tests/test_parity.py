@@ -103,6 +103,58 @@ def test_split_rows(lib, name, split):
     run_config(lib, name, calls=min(wl.CONFIGS[name].calls, 12), split=split)
 
 
+@pytest.mark.parametrize("name,with_box", [("c1", True), ("c2", True), ("c3", True), ("c2", False)])
+def test_push_reduce_norm_one_call(lib, name, with_box):
+    """arnorm_push_reduce_norm (one launch with a norm box at M <= 64, else the pair of
+    launches) against the oracle's push of every slot followed by its consumer."""
+    cfg = wl.CONFIGS[name]
+    say(f"[parity] push_reduce_norm {name} norm_box={with_box}")
+    src = wl.ArNormInputs(cfg)
+    shape = (cfg.parities, cfg.tp, cfg.cap, W // 2)
+    box_d, box_h = armed_box(shape), oracle.arm(np.empty(shape, dtype=np.uint32))
+    nbox = norm_box_for(shape) if with_box else None
+    g_d = dev16(src.gamma)
+    for call in range(min(cfg.calls, 12)):
+        parity = call % cfg.parities
+        p, r = src.call()
+        out_d, rout_d = empty16((cfg.m, W)), empty16((cfg.m, W))
+        assert lib.arnorm_push_reduce_norm(dev16(p), dev16(r) if r is not None else None, g_d, box_d, parity, EPS,
+                                           out_d, rout_d, norm_box=nbox) is True
+        oracle.arnorm_push(box_h, p, parity, 0)
+        want_out, want_res = oracle.arnorm_reduce_norm(box_h, parity, cfg.m, r, src.gamma, EPS)
+        assert_bits_equal(host16(rout_d), want_res, f"call {call} residual_out")
+        exact_zero = (oracle.widen(want_res) == 0) | (oracle.widen(src.gamma) == 0)[None, :]
+        assert_out_close(host16(out_d), want_out, f"call {call} out", exact_zero=exact_zero)
+        assert_bits_equal(host32(box_d), box_h, f"call {call} mailbox")
+        if nbox is not None:
+            assert np.all(host32(nbox) == S0)
+        assert lib.status() == lib.OK
+
+
+@pytest.mark.parametrize("tp", [2, 3, 8])
+def test_push_reduce_norm_torture(lib, tp):
+    say(f"[parity] push_reduce_norm torture tp={tp}")
+    rng = np.random.default_rng(170 + tp)
+    m, cap = 13, 17
+    shape = (2, tp, cap, W // 2)
+    box_d, box_h, nbox = armed_box(shape), oracle.arm(np.empty(shape, dtype=np.uint32)), norm_box_for(shape)
+    gamma = (rng.integers(0, 2, W) << 15 | (rng.integers(120, 132, W) << 7) | rng.integers(0, 128, W)).astype(np.uint16)
+    for call in range(3):
+        parity = call % 2
+        p = torture_partials(rng, tp, m)
+        res = torture_partials(rng, 1, m)[0] if call % 2 else None
+        out_d, rout_d = empty16((m, W)), empty16((m, W))
+        assert lib.arnorm_push_reduce_norm(dev16(p), dev16(res) if res is not None else None, dev16(gamma), box_d,
+                                           parity, EPS, out_d, rout_d, norm_box=nbox) is True
+        oracle.arnorm_push(box_h, p, parity, 0)
+        want_out, want_res = oracle.arnorm_reduce_norm(box_h, parity, m, res, gamma, EPS)
+        assert_bits_equal(host16(rout_d), want_res, "residual_out")
+        exact_zero = (oracle.widen(want_res) == 0) | (oracle.widen(gamma) == 0)[None, :]
+        assert_out_close(host16(out_d), want_out, exact_zero=exact_zero)
+        assert_bits_equal(host32(box_d), box_h, "mailbox")
+        assert lib.status() == lib.OK
+
+
 def test_c3_per_rank_pushes_and_chained_residual(lib):
     """Ranks push one by one (and in groups), and each call's residual is the previous
     call's residual_out, as consecutive layers use it."""

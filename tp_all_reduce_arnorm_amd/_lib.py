@@ -29,6 +29,8 @@ _SIGNATURES = {
     "arnorm_push": (_c_int, [_c_ptr, _c_ptr, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_ptr]),
     "arnorm_reduce_norm": (_c_int, [_c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_int, _c_int,
                                     _c_int, _c_int, _c_int, _c_int, _c_float, _c_ptr]),
+    "arnorm_push_reduce_norm": (_c_int, [_c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_int, _c_int,
+                                         _c_int, _c_int, _c_int, _c_float, _c_ptr]),
     "gather_push": (_c_int, [_c_ptr, _c_ptr, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_ptr]),
     "gather_poll": (_c_int, [_c_ptr, _c_ptr, _c_int, _c_int, _c_int, _c_int, _c_int, _c_ptr]),
     "twoshot_push": (_c_int, [_c_ptr, _c_ptr, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
@@ -123,6 +125,23 @@ def arnorm_reduce_norm(residual, gamma, mailbox, parity, eps, out, residual_out,
         _ptr(partial, 2, "partial"), _ptr(residual, 2, "residual"), _ptr(gamma, 2, "gamma"),
         _ptr(out, 2, "out"), _ptr(residual_out, 2, "residual_out"), _ptr(mailbox, 4, "mailbox"),
         _ptr(norm_box, 4, "norm_box"), p, tp, cap, parity, rank, m, float(eps), _stream(stream)))
+
+
+def arnorm_push_reduce_norm(partials, residual, gamma, mailbox, parity, eps, out, residual_out, norm_box=None,
+                            stream=None):
+    """One stand-in call: every rank's push (partials BF16 [tp, M, 7168]) and the
+    consumer, in one launch when norm_box is given and M <= 64."""
+    tp_, m, width = partials.shape
+    if width != HIDDEN:
+        return None
+    p, tp, cap, words = mailbox.shape
+    assert words == ROW_WORDS and tp_ == tp and tuple(out.shape) == (m, HIDDEN)
+    if norm_box is not None:
+        assert tuple(norm_box.shape) == (p, cap, NORM_BOX_ROW_WORDS)
+    return _check("arnorm_push_reduce_norm", LIB.arnorm_push_reduce_norm(
+        _ptr(partials, 2, "partials"), _ptr(residual, 2, "residual"), _ptr(gamma, 2, "gamma"),
+        _ptr(out, 2, "out"), _ptr(residual_out, 2, "residual_out"), _ptr(mailbox, 4, "mailbox"),
+        _ptr(norm_box, 4, "norm_box"), p, tp, cap, parity, m, float(eps), _stream(stream)))
 
 
 def gather_push(shard, mailbox, tp, rank, stream=None):

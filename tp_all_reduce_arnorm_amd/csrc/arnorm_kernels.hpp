@@ -69,6 +69,7 @@ struct ReduceArgs {
   size_t slot_stride;       // cap * 14336 bytes
   uint32_t *nbox;           // norm_box[parity]: [cap, 256 words] (split rows only)
   int rank;                 // own slot (FUSED only)
+  int poll_all;             // later poll passes re-read every slot (small grids) instead of a witness
   float eps;
   uint64_t spin_limit;
 };
@@ -91,7 +92,7 @@ constexpr int reduce_occupancy(int nt) {
 // adds the K parts in workgroup order and re-arms its inbox.  A part is a sum of FMA
 // products started from +0, so it is never -0, the sentinel word.
 template <int TP, bool RES, bool FUSED, int NT, int K, int POL_LD, int POL_ST, int POL_IO>
-__global__ void __launch_bounds__(NT, reduce_occupancy(NT)) reduce_norm_kernel(ReduceArgs a) {
+__device__ __forceinline__ void reduce_row(const ReduceArgs &a, const uint32_t row, const uint32_t k) {
   constexpr int NF = K > 1 ? 1 : (kRowFrags + NT - 1) / NT;  // fragments per thread
   constexpr int NW = NT / 64;
   static_assert(NT % 64 == 0 && NW <= 16, "wave64 workgroups of at most 16 waves");
@@ -100,8 +101,6 @@ __global__ void __launch_bounds__(NT, reduce_occupancy(NT)) reduce_norm_kernel(R
   __shared__ float row_total;
 
   const int t = threadIdx.x;
-  const uint32_t row = blockIdx.x;
-  const uint32_t k = K > 1 ? blockIdx.y : 0;
   const size_t row_off = (size_t)row * kRowBytes;
   const uint32_t base = k * NT;  // first fragment of this workgroup's part of the row
   uint32_t off[NF];
@@ -171,14 +170,19 @@ __global__ void __launch_bounds__(NT, reduce_occupancy(NT)) reduce_norm_kernel(R
         if (pending) atomicOr(&g_status, 1u);
         break;
       }
-      const int wl = __ffsll((unsigned long long)waiting) - 1;
-      const int wbit = __shfl(__ffs(pending) - 1, wl, 64);  // s * NF + f of the witness
-      const int ws = wbit / NF, wf = wbit % NF;
-      const uint32_t *wp = reinterpret_cast<const uint32_t *>(
-          a.box + ws * a.slot_stride + row_off + (size_t)(base + (t - lane + wl) + wf * NT) * 16u);
-      if (!published(load_fragment_coherent(wp))) {
-        __builtin_amdgcn_s_sleep(8);
-        continue;
+      if (a.poll_all) {
+        // a small grid: every pass re-reads all slots, so the data arrives with the news
+        __builtin_amdgcn_s_sleep(1);
+      } else {
+        const int wl = __ffsll((unsigned long long)waiting) - 1;
+        const int wbit = __shfl(__ffs(pending) - 1, wl, 64);  // s * NF + f of the witness
+        const int ws = wbit / NF, wf = wbit % NF;
+        const uint32_t *wp = reinterpret_cast<const uint32_t *>(
+            a.box + ws * a.slot_stride + row_off + (size_t)(base + (t - lane + wl) + wf * NT) * 16u);
+        if (!published(load_fragment_coherent(wp))) {
+          __builtin_amdgcn_s_sleep(8);
+          continue;
+        }
       }
       asm volatile("" ::: "memory");
 #pragma unroll
@@ -276,6 +280,53 @@ __global__ void __launch_bounds__(NT, reduce_occupancy(NT)) reduce_norm_kernel(R
     }
     buf_store<POL_IO>(o, nout, off[f]);
   }
+}
+
+template <int TP, bool RES, bool FUSED, int NT, int K, int POL_LD, int POL_ST, int POL_IO>
+__global__ void __launch_bounds__(NT, reduce_occupancy(NT)) reduce_norm_kernel(ReduceArgs a) {
+  reduce_row<TP, RES, FUSED, NT, K, POL_LD, POL_ST, POL_IO>(a, blockIdx.x, K > 1 ? blockIdx.y : 0);
+}
+
+// ---------------------------------------------------------------------------------
+// arnorm_push_reduce_norm in one launch: the pages' ArNorm kernel pushes a rank's row
+// and then polls every slot, with no kernel boundary between a producer and its
+// reader.  The one-GPU stand-in of such a call puts every rank's push in the same grid:
+// workgroups [0, TP * per_slot) are the producers (per_slot of them per slot, the
+// lowest workgroup ids, which the dispatcher places first), the others are the row
+// consumers, split 7 ways (128 threads each), which poll until the producers' stores
+// land, re-arm and reduce.
+struct StepArgs {
+  ReduceArgs r;
+  const u32x4 *partials;  // [TP, M, 896]
+  uint32_t frags;         // M * 896: one slot's fragments, one block in the mailbox
+  uint32_t per_slot;      // producer workgroups per slot
+};
+
+template <int TP, bool RES, int U, int POL_PUSH, int POL_LD, int POL_ST, int POL_IO>
+__global__ void __launch_bounds__(128) push_reduce_kernel(StepArgs a) {
+  constexpr int K = 7, NT = kRowFrags / K;
+  const uint32_t producers = TP * a.per_slot;
+  if (blockIdx.x < producers) {
+    const uint32_t s = blockIdx.x / a.per_slot, p = blockIdx.x - s * a.per_slot;
+    const u32x4 *src = a.partials + (size_t)s * a.frags;
+    const __amdgpu_buffer_rsrc_t dst = make_rsrc(a.r.box + s * a.r.slot_stride, a.frags * 16u);
+    for (uint32_t i0 = p * NT * U + threadIdx.x; i0 < a.frags; i0 += a.per_slot * NT * U) {
+      u32x4 v[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const uint32_t i = i0 + u * NT;
+        if (i < a.frags) v[u] = nt_load(src + i);
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const uint32_t i = i0 + u * NT;
+        if (i < a.frags) buf_store<POL_PUSH>(clean4(v[u]), dst, i * 16u);
+      }
+    }
+    return;
+  }
+  const uint32_t c = blockIdx.x - producers;
+  reduce_row<TP, RES, false, NT, K, POL_LD, POL_ST, POL_IO>(a.r, c / K, c % K);
 }
 
 }  // namespace arn

@@ -52,6 +52,16 @@ std::atomic<int> g_reduce_split{0};
 #ifndef ARNORM_SPLIT7_MAX_M
 #define ARNORM_SPLIT7_MAX_M 64
 #endif
+// arnorm_push_reduce_norm, one-launch form: fragments per producer thread per step.
+#ifndef ARNORM_STEP_PUSH_U
+#define ARNORM_STEP_PUSH_U 2
+#endif
+// A consumer grid whose TP slots of rows < M total at most this many bytes re-reads all
+// of them on every later poll pass (the data arrives with the news); a larger one
+// watches one witness fragment per wave, so that waiting does not starve the producer.
+#ifndef ARNORM_POLL_ALL_MAX_BYTES
+#define ARNORM_POLL_ALL_MAX_BYTES (1u << 20)
+#endif
 constexpr int kPolPoll = ARNORM_POL_POLL;
 constexpr int kPolRearm = ARNORM_POL_REARM;
 constexpr int kPolPush = ARNORM_POL_PUSH;
@@ -233,6 +243,7 @@ int arnorm_reduce_norm(const uint16_t *partial, const uint16_t *residual, const 
   a.rank = partial ? rank : -1;
   a.eps = eps;
   a.spin_limit = g_spin_limit.load(std::memory_order_relaxed);
+  a.poll_all = (uint64_t)tp * M * arn::kRowBytes <= ARNORM_POLL_ALL_MAX_BYTES;
   const bool res = residual != nullptr;
   const bool fused = partial != nullptr;
   const int threads = reduce_threads(M);
@@ -247,6 +258,73 @@ int arnorm_reduce_norm(const uint16_t *partial, const uint16_t *residual, const 
     case 7: return launch_reduce_tp<7>(a, res, fused, M, threads, split, stream);
     case 8: return launch_reduce_tp<8>(a, res, fused, M, threads, split, stream);
   }
+  return ARNORM_NOT_SERVED;
+}
+
+int arnorm_push_reduce_norm(const uint16_t *partials, const uint16_t *residual, const uint16_t *gamma,
+                            uint16_t *out, uint16_t *residual_out, int32_t *mailbox, int32_t *norm_box, int parities,
+                            int tp, int cap, int parity, int M, float eps, hipStream_t stream) {
+  int rc = check_box(parities, tp, cap, parity, M);
+  if (rc != ARNORM_OK) return rc;
+  if (!aligned16(partials) || (residual && !aligned16(residual))) return ARNORM_BAD_ARG;
+  // One launch only where its consumer may re-read every slot on each poll pass (a small
+  // grid): measured at TP=8 it is then faster than the pair (M=4: 4.8 against 5.3 us),
+  // while with witness polling (larger M) the pair of launches is faster.
+  const bool one_launch = norm_box != nullptr && reduce_split(M, true) == 7 &&
+                          (uint64_t)tp * M * arn::kRowBytes <= ARNORM_POLL_ALL_MAX_BYTES;
+  if (!one_launch) {
+    // the same call as two launches: every rank's push, then the consumer
+    rc = arnorm_push(partials, mailbox, parities, tp, cap, parity, 0, tp, M, stream);
+    if (rc != ARNORM_OK) return rc;
+    return arnorm_reduce_norm(nullptr, residual, gamma, out, residual_out, mailbox, norm_box, parities, tp, cap,
+                              parity, 0, M, eps, stream);
+  }
+  if (!aligned16(gamma) || !aligned16(out) || !aligned16(residual_out) || !aligned16(mailbox) ||
+      !aligned16(norm_box))
+    return ARNORM_BAD_ARG;
+  const void *outs[3] = {out, residual_out, norm_box};
+  const void *ins[4] = {partials, residual, gamma, mailbox};
+  for (const void *o : outs)
+    for (const void *i : ins)
+      if (o == i && !(o == residual_out && i == residual)) return ARNORM_BAD_ARG;
+  if (out == residual_out || static_cast<void *>(norm_box) == out || static_cast<void *>(norm_box) == residual_out)
+    return ARNORM_BAD_ARG;
+
+  arn::StepArgs a;
+  a.r.partial = nullptr;
+  a.r.residual = reinterpret_cast<const uint8_t *>(residual);
+  a.r.gamma = reinterpret_cast<const uint8_t *>(gamma);
+  a.r.out = reinterpret_cast<uint8_t *>(out);
+  a.r.res_out = reinterpret_cast<uint8_t *>(residual_out);
+  a.r.box = parity_base(mailbox, parity, tp, cap);
+  a.r.slot_stride = (size_t)cap * arn::kRowBytes;
+  a.r.nbox = reinterpret_cast<uint32_t *>(norm_box) + (size_t)parity * cap * arn::kNormBoxRowWords;
+  a.r.rank = -1;
+  a.r.eps = eps;
+  a.r.spin_limit = g_spin_limit.load(std::memory_order_relaxed);
+  a.r.poll_all = (uint64_t)tp * M * arn::kRowBytes <= ARNORM_POLL_ALL_MAX_BYTES;
+  a.partials = reinterpret_cast<const u32x4 *>(partials);
+  a.frags = (uint32_t)M * arn::kRowFrags;
+  constexpr int U = ARNORM_STEP_PUSH_U;
+  a.per_slot = (a.frags + 128 * U - 1) / (128 * U);
+  const dim3 grid(tp * a.per_slot + M * 7);
+  const bool res = residual != nullptr;
+#define ARNORM_STEP_LAUNCH(TPV)                                                                                   \
+  case TPV:                                                                                                      \
+    return res ? launch(arn::push_reduce_kernel<TPV, true, U, kPolPush, kPolPoll, kPolRearm, kPolIO>, grid,     \
+                        dim3(128), stream, a)                                                                    \
+               : launch(arn::push_reduce_kernel<TPV, false, U, kPolPush, kPolPoll, kPolRearm, kPolIO>, grid,    \
+                        dim3(128), stream, a);
+  switch (tp) {
+    ARNORM_STEP_LAUNCH(2)
+    ARNORM_STEP_LAUNCH(3)
+    ARNORM_STEP_LAUNCH(4)
+    ARNORM_STEP_LAUNCH(5)
+    ARNORM_STEP_LAUNCH(6)
+    ARNORM_STEP_LAUNCH(7)
+    ARNORM_STEP_LAUNCH(8)
+  }
+#undef ARNORM_STEP_LAUNCH
   return ARNORM_NOT_SERVED;
 }
 
