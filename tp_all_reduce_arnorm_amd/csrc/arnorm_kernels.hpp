@@ -282,9 +282,12 @@ __device__ __forceinline__ void reduce_row(const ReduceArgs &a, const uint32_t r
   }
 }
 
+// The grid lists a row's K workgroups next to each other (id = row * K + k): with
+// workgroups dispatched in id order, the lowest unfinished row always has all of its
+// workgroups dispatched (every lower id has finished), so the exchange cannot deadlock.
 template <int TP, bool RES, bool FUSED, int NT, int K, int POL_LD, int POL_ST, int POL_IO>
 __global__ void __launch_bounds__(NT, reduce_occupancy(NT)) reduce_norm_kernel(ReduceArgs a) {
-  reduce_row<TP, RES, FUSED, NT, K, POL_LD, POL_ST, POL_IO>(a, blockIdx.x, K > 1 ? blockIdx.y : 0);
+  reduce_row<TP, RES, FUSED, NT, K, POL_LD, POL_ST, POL_IO>(a, blockIdx.x / K, blockIdx.x % K);
 }
 
 // ---------------------------------------------------------------------------------

@@ -129,7 +129,7 @@ int launch_reduce(const arn::ReduceArgs &a, int M, hipStream_t stream) {
 template <int TP, bool RES, bool FUSED, int K>
 int launch_reduce_split(const arn::ReduceArgs &a, int M, hipStream_t stream) {
   constexpr int NT = arn::kRowFrags / K;
-  return launch(arn::reduce_norm_kernel<TP, RES, FUSED, NT, K, kPolPoll, kPolRearm, kPolIO>, dim3(M, K), dim3(NT),
+  return launch(arn::reduce_norm_kernel<TP, RES, FUSED, NT, K, kPolPoll, kPolRearm, kPolIO>, dim3(M * K), dim3(NT),
                 stream, a);
 }
 
@@ -165,7 +165,10 @@ int reduce_threads(int M) {
 
 // Workgroups per row: more than one only with a norm box and a grid small enough to be
 // resident at once (every workgroup of a row waits on its peers' parts).
-constexpr int kSplitMaxGrid = 1024;
+#ifndef ARNORM_SPLIT_MAX_GRID
+#define ARNORM_SPLIT_MAX_GRID 1024
+#endif
+constexpr int kSplitMaxGrid = ARNORM_SPLIT_MAX_GRID;
 int reduce_split(int M, bool have_box) {
   if (!have_box) return 1;
   int k = g_reduce_split.load(std::memory_order_relaxed);
