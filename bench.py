@@ -137,13 +137,16 @@ def gather_bytes(tp, m, s, copy=True):
     return 2 * words * 4, (3 if copy else 1) * words * 4
 
 
-def time_gather(lib, torch, calls=1000, chunk=50, name="c4"):
-    """µs per Gather call (gather_push of the 8 ranks' shards, then gather_poll with
-    copy), graph-replayed: c4 is TP=8, M=32, S=896; ctx and logits are the drafter's
-    context-projection and lm_head shapes."""
+def time_gather(lib, torch, calls=1000, chunk=50, name="c4", one_launch=True, m=None):
+    """µs per Gather call, graph-replayed: gather_push_poll (every rank's push and the
+    copying poll, one launch for calls within 1 MiB), or with one_launch False the pair
+    gather_push + gather_poll.  c4 is TP=8, M=32, S=896; ctx and logits are the
+    drafter's context-projection and lm_head shapes; m overrides the row count."""
+    import dataclasses
+
     from tp_all_reduce_arnorm_amd import workloads as wl
 
-    cfg = wl.CONFIGS[name]
+    cfg = wl.CONFIGS[name] if m is None else dataclasses.replace(wl.CONFIGS[name], m=m)
     words = wl.gather_shards(cfg) if name == "c4" else wl.bf16_shards(cfg)
     shards = torch.from_numpy(words.view(np.int32)).cuda()
     box = torch.empty((cfg.cap, cfg.tp * cfg.s), dtype=torch.int32, device="cuda")
@@ -151,6 +154,9 @@ def time_gather(lib, torch, calls=1000, chunk=50, name="c4"):
     out = torch.empty((cfg.m, cfg.tp * cfg.s), dtype=torch.int32, device="cuda")
 
     def call():
+        if one_launch:
+            assert lib.gather_push_poll(shards, box, out=out, copy=True) is True
+            return
         assert lib.gather_push(shards, box, cfg.tp, 0) is True
         assert lib.gather_poll(box, cfg.tp, cfg.m, out=out, copy=True) is True
 
@@ -385,8 +391,10 @@ def summarize_profiles(outdir):
                     "arnorm_reduce_norm, HIP-graph replay, 2000 calls)", "arnorm_tp8_m4_kernel_stats.md"),
             ("roof", "ArNorm kernels at TP=8, M=4096, residual (one push of 8 slots + one consumer "
                      "launch, 23 times)", "arnorm_tp8_m4096_kernel_stats.md"),
-            ("gather", "Gather at TP=8, M=32, S=896 words, cap=64 (gather_push of 8 slots + gather_poll "
-                       "with copy, HIP-graph replay, 1000 calls)", "gather_tp8_m32_s896_kernel_stats.md"),
+            ("gather", "Gather at TP=8, S=896 words, cap=64, HIP-graph replay: 1000 gather_push_poll calls "
+                       "at M=32 (917504 B, so run as the pair gather_push of 8 slots + gather_poll with "
+                       "copy), 1000 calls of that pair, then 1000 one-launch gather_push_poll calls at M=4",
+             "gather_tp8_m32_s896_kernel_stats.md"),
             ("twoshot", "Two-shot all-reduce stand-in (owners = 1): TP=8, M=4 graph-replayed calls (push, "
                         "owner's reduce, read), then 23 launches at TP=8, M=4096", "twoshot_tp8_kernel_stats.md")):
         if not os.path.exists(os.path.join(outdir, f"prof_{key}", f"{key}_kernel_stats.csv")):
@@ -486,7 +494,10 @@ def main():
         return
     if args.mode == "gather":
         _, us = time_gather(lib, torch)
-        print(json.dumps({"mode": "gather", "us_per_call": us, "sources_sha": sha}), flush=True)
+        _, pair_us = time_gather(lib, torch, one_launch=False)
+        _, m4_us = time_gather(lib, torch, m=4)
+        print(json.dumps({"mode": "gather", "us_per_call": us, "two_launch_us_per_call": pair_us,
+                          "m4_one_launch_us_per_call": m4_us, "sources_sha": sha}), flush=True)
         return
     if args.mode == "twoshot":
         print(json.dumps(dict(mode="twoshot", sources_sha=sha, **time_twoshot(lib, torch))), flush=True)
@@ -498,13 +509,21 @@ def main():
     pair_us = time_latency(lib, torch, args.steps, args.warmup, one_launch=False) / args.steps * 1e6
     cfg5, red_us, push_us = time_roofline(lib, torch)
     cfg4, gather_us = time_gather(lib, torch)
+    _, gather_pair_us = time_gather(lib, torch, one_launch=False)
     ts = time_twoshot(lib, torch)
     shapes = {}
     for name in ("ctx", "logits"):
         c, us = time_gather(lib, torch, name=name)
+        _, pus = time_gather(lib, torch, name=name, one_launch=False)
         shapes[name] = {"tp": c.tp, "m": c.m, "s_words": c.s, "us_per_call": round(us, 3),
+                        "two_launch_us_per_call": round(pus, 3),
                         "push_algorithmic_bytes": gather_bytes(c.tp, c.m, c.s)[0],
                         "poll_algorithmic_bytes": gather_bytes(c.tp, c.m, c.s)[1]}
+    for name, m in (("c4", 4), ("logits", 1)):  # decode-sized calls, one launch
+        c, us = time_gather(lib, torch, name=name, m=m)
+        _, pus = time_gather(lib, torch, name=name, m=m, one_launch=False)
+        shapes[f"{name}_m{m}"] = {"tp": c.tp, "m": c.m, "s_words": c.s, "us_per_call": round(us, 3),
+                                  "two_launch_us_per_call": round(pus, 3)}
     tsr, tsq = twoshot_bytes(8, 4096)
     gpb, gqb = gather_bytes(cfg4.tp, cfg4.m, cfg4.s)
     rb = reduce_bytes(cfg5.tp, cfg5.m, True)
@@ -556,9 +575,11 @@ def main():
             "frac": round(pb / (push_us * 1e-6) / 1e9 / PEAK_HBM_GBPS, 4),
         },
         "gather": {
-            "workload": "Gather TP=8 M=32 S=896 words cap=64, gather_push of 8 slots + gather_poll "
-                        "with copy, HIP-graph replay",
-            "us_per_call": round(gather_us, 3), "push_algorithmic_bytes": gpb, "poll_algorithmic_bytes": gqb,
+            "workload": "Gather TP=8 M=32 S=896 words cap=64: gather_push_poll with copy, HIP-graph replay "
+                        "(917504 B of gathered rows, above the 512 KiB one-launch limit, so it runs as "
+                        "the pair gather_push + gather_poll; the c4_m4 and logits_m1 drafter_shapes "
+                        "entries are one-launch calls); two_launch_us_per_call is the pair itself",
+            "us_per_call": round(gather_us, 3), "two_launch_us_per_call": round(gather_pair_us, 3), "push_algorithmic_bytes": gpb, "poll_algorithmic_bytes": gqb,
             "drafter_shapes": shapes,
         },
         "twoshot": {

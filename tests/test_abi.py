@@ -139,6 +139,17 @@ def test_gather_checks(L):
     assert L.gather_poll(FAKE, None, 8, 64, 896, 0, 0, None) == 1
 
 
+def test_gather_push_poll_checks(L):
+    assert L.gather_push_poll(FAKE, FAKE + 0x100000, FAKE + 0x200000, 1, 64, 896, 32, 1, None) == 1
+    assert L.gather_push_poll(FAKE, FAKE + 0x100000, FAKE + 0x200000, 8, 64, 6, 32, 1, None) == 1
+    assert L.gather_push_poll(FAKE, FAKE + 0x100000, FAKE + 0x200000, 8, 64, 896, 65, 1, None) == 1
+    for m in (4, 32):  # one launch, and the pair
+        assert L.gather_push_poll(MIS, FAKE + 0x100000, FAKE + 0x200000, 8, 64, 896, m, 1, None) == 2
+        assert L.gather_push_poll(FAKE, FAKE + 0x100000, FAKE + 0x100000, 8, 64, 896, m, 1, None) == 2
+        assert L.gather_push_poll(FAKE, FAKE + 0x100000, FAKE, 8, 64, 896, m, 1, None) == 2
+        assert L.gather_push_poll(FAKE, FAKE + 0x100000, None, 8, 64, 896, m, 1, None) == 2
+
+
 def test_twoshot_checks(L):
     assert L.twoshot_push(FAKE, FAKE, 2, 1, 64, 7168, 0, 0, 1, 4, None) == 1   # tp 1
     assert L.twoshot_push(FAKE, FAKE, 2, 8, 64, 7164, 0, 0, 8, 4, None) == 1   # width % 8
@@ -173,5 +184,5 @@ def test_binding_mirrors_the_abi():
     from tp_all_reduce_arnorm_amd import _lib
 
     for n in ("lamport_arm", "arnorm_push", "arnorm_reduce_norm", "arnorm_push_reduce_norm", "gather_push",
-              "gather_poll", "twoshot_push", "twoshot_reduce", "twoshot_read"):
+              "gather_poll", "gather_push_poll", "twoshot_push", "twoshot_reduce", "twoshot_read"):
         assert callable(getattr(_lib, n))

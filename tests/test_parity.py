@@ -240,6 +240,37 @@ def test_drafter_gather_shapes(lib, name, m, tp):
         assert np.array_equal(blk[:, 1::2][~sent], src[:, 1::2][~sent]) and np.all(blk[:, 1::2][sent] == 0)
 
 
+@pytest.mark.parametrize("name,m", [("c4", 32), ("c4", 16), ("c4", 1), ("ctx", 64), ("logits", 4),
+                                    ("logits", 2), ("logits", 1)])
+def test_gather_push_poll_one_call(lib, name, m):
+    """gather_push_poll (one launch for calls within 512 KiB, else the pair) against the
+    oracle's push of every rank followed by its poll: copy, then no-copy followed by a
+    copying poll."""
+    import dataclasses
+
+    import torch
+
+    say(f"[parity] gather_push_poll {name} M={m}")
+    cfg = dataclasses.replace(wl.CONFIGS[name], m=m)
+    shards = wl.gather_shards(cfg) if name == "c4" else wl.bf16_shards(cfg)
+    gshape = (cfg.cap, cfg.tp * cfg.s)
+    gbox_d, gbox_h = armed_box(gshape), oracle.arm(np.empty(gshape, dtype=np.uint32))
+    sh_d = dev32(shards)
+    for copy in (True, False):
+        out_d = torch.empty((m, cfg.tp * cfg.s), dtype=torch.int32, device="cuda")
+        assert lib.gather_push_poll(sh_d, gbox_d, out=out_d, copy=copy) is True
+        oracle.gather_push(gbox_h, shards, 0)
+        want = oracle.gather_poll(gbox_h, m, copy)
+        if copy:
+            assert_bits_equal(host32(out_d), want, "gathered words")
+        assert_bits_equal(host32(gbox_d), gbox_h, f"gather mailbox (copy={copy})")
+        assert lib.status() == lib.OK
+    out_d = torch.empty((m, cfg.tp * cfg.s), dtype=torch.int32, device="cuda")
+    assert lib.gather_poll(gbox_d, cfg.tp, m, out=out_d, copy=True) is True  # the later reader
+    assert_bits_equal(host32(out_d), oracle.gather_poll(gbox_h, m, True), "later reader")
+    assert_bits_equal(host32(gbox_d), gbox_h, "gather mailbox re-armed")
+
+
 def test_c5_full_size_sampled_rows(lib):
     """M = 4096, TP = 8, in the launch configuration the benchmark times; the oracle
     checks a sample of rows one by one (rows are independent), and the whole mailbox

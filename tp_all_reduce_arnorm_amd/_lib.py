@@ -33,6 +33,7 @@ _SIGNATURES = {
                                          _c_int, _c_int, _c_int, _c_float, _c_ptr]),
     "gather_push": (_c_int, [_c_ptr, _c_ptr, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_ptr]),
     "gather_poll": (_c_int, [_c_ptr, _c_ptr, _c_int, _c_int, _c_int, _c_int, _c_int, _c_ptr]),
+    "gather_push_poll": (_c_int, [_c_ptr, _c_ptr, _c_ptr, _c_int, _c_int, _c_int, _c_int, _c_int, _c_ptr]),
     "twoshot_push": (_c_int, [_c_ptr, _c_ptr, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
                               _c_ptr]),
     "twoshot_reduce": (_c_int, [_c_ptr, _c_ptr, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_ptr]),
@@ -161,6 +162,18 @@ def gather_poll(mailbox, tp, m, out=None, copy=True, stream=None):
     return _check("gather_poll", LIB.gather_poll(
         _ptr(mailbox, 4, "mailbox"), _ptr(out, 4, "out") if copy else None, tp, cap, s, m, 1 if copy else 0,
         _stream(stream)))
+
+
+def gather_push_poll(shard, mailbox, out=None, copy=True, stream=None):
+    """One Gather call: every rank's shard (int32 [tp, M, S]) pushed and the M gathered
+    rows polled (copied into out and re-armed, or left published), in one launch for
+    small calls."""
+    tp, m, s = shard.shape
+    cap, width = mailbox.shape
+    assert width == tp * s
+    return _check("gather_push_poll", LIB.gather_push_poll(
+        _ptr(shard, 4, "shard"), _ptr(mailbox, 4, "mailbox"), _ptr(out, 4, "out") if copy else None, tp, cap, s, m,
+        1 if copy else 0, _stream(stream)))
 
 
 def twoshot_push(partial, recv, parity, rank, stream=None):

@@ -26,39 +26,39 @@ gather_push_kernel(const u32x4 *__restrict__ shard, uint8_t *__restrict__ box, u
     buf_store<POL>(clean4(nt_load(src + i)), dst, i * 16u);
 }
 
-// gather_poll: grid (ctas, M); workgroup `cta` of row m takes fragments
-// cta*256 + t, strided by ctas*256, over the row's TP*S/4 fragments.
+// The poll of one row's fragments by workgroup `cta` of `ctas` (cta*256 + t, strided by
+// ctas*256), with copy and re-arm.  Waiting must not steal the producers' bandwidth: a
+// wave with unpublished fragments watches one witness (the fragment of its lowest
+// waiting lane; every lane loads the same 16 B) and its lanes re-read their own
+// fragments only once that is published; a small grid (poll_all) re-reads every
+// pending fragment on each pass instead, so the data arrives with the news.  The loop
+// trip count is uniform per wave (the step is a multiple of 64).
 template <int POL_LD, int POL_ST>
-__global__ void __launch_bounds__(256)
-gather_poll_kernel(uint8_t *__restrict__ box, u32x4 *__restrict__ out, uint32_t row_frags,
-                   int copy, uint64_t spin_limit) {
-  const uint32_t m = blockIdx.y;
-  uint8_t *row = box + (size_t)m * row_frags * 16u;
+__device__ __forceinline__ void poll_row(uint8_t *row, u32x4 *out_row, uint32_t row_frags, uint32_t cta,
+                                         uint32_t ctas, int copy, uint64_t spin_limit, int poll_all) {
   const __amdgpu_buffer_rsrc_t r = make_rsrc(row, row_frags * 16u);
-  // Waiting must not steal the producers' bandwidth: a wave with unpublished fragments
-  // watches one witness (the fragment of its lowest waiting lane; every lane loads the
-  // same 16 B) and its lanes re-read their own fragments only once that is published.
-  // The loop trip count is uniform per wave (the step is a multiple of 64).
   const int lane = threadIdx.x & 63;
-  for (uint32_t base = blockIdx.x * 256u + (threadIdx.x & ~63u); base < row_frags; base += gridDim.x * 256u) {
+  for (uint32_t base = cta * 256u + (threadIdx.x & ~63u); base < row_frags; base += ctas * 256u) {
     const uint32_t i = base + lane;
     const bool mine = i < row_frags;
     u32x4 w = buf_load<POL_LD>(r, mine ? i * 16u : 0x80000000u);
     bool ok = !mine || published(w);
-    bool gave_up = false;
     for (uint64_t polls = 0;; ++polls) {
       const uint64_t waiting = __ballot(!ok);
       if (waiting == 0) break;
       if (polls >= spin_limit) {
         if (!ok) atomicOr(&g_status, 1u);
-        gave_up = true;
         break;
       }
-      const int wl = __ffsll((unsigned long long)waiting) - 1;
-      const uint32_t *wp = reinterpret_cast<const uint32_t *>(row + (size_t)(base + wl) * 16u);
-      if (!published(load_fragment_coherent(wp))) {
-        __builtin_amdgcn_s_sleep(8);
-        continue;
+      if (poll_all) {
+        __builtin_amdgcn_s_sleep(1);
+      } else {
+        const int wl = __ffsll((unsigned long long)waiting) - 1;
+        const uint32_t *wp = reinterpret_cast<const uint32_t *>(row + (size_t)(base + wl) * 16u);
+        if (!published(load_fragment_coherent(wp))) {
+          __builtin_amdgcn_s_sleep(8);
+          continue;
+        }
       }
       asm volatile("" ::: "memory");
       if (!ok) {
@@ -66,12 +66,56 @@ gather_poll_kernel(uint8_t *__restrict__ box, u32x4 *__restrict__ out, uint32_t 
         ok = published(w);
       }
     }
-    (void)gave_up;
     if (copy && mine && ok) {
-      nt_store(w, out + (size_t)m * row_frags + i);
+      nt_store(w, out_row + i);
       buf_store<POL_ST>(sentinel4(), r, i * 16u);
     }
   }
+}
+
+// gather_poll: grid (ctas, M); workgroup `cta` of row m.
+template <int POL_LD, int POL_ST>
+__global__ void __launch_bounds__(256)
+gather_poll_kernel(uint8_t *__restrict__ box, u32x4 *__restrict__ out, uint32_t row_frags,
+                   int copy, uint64_t spin_limit, int poll_all) {
+  const uint32_t m = blockIdx.y;
+  poll_row<POL_LD, POL_ST>(box + (size_t)m * row_frags * 16u, out + (size_t)m * row_frags, row_frags, blockIdx.x,
+                           gridDim.x, copy, spin_limit, poll_all);
+}
+
+// gather_push_poll in one launch, as the pages' Gather kernel pushes its shard and then
+// polls the gathered row: workgroups [0, TP*M*per_row) are the producers of every rank's
+// shard rows (the lowest ids, dispatched first), the rest poll the M gathered rows.
+struct GatherStepArgs {
+  const u32x4 *shard;  // [TP, M, F]
+  uint8_t *box;        // [cap, TP*F*16 B]
+  u32x4 *out;          // [M, TP*F]
+  uint32_t frags;      // F = S/4 fragments of one rank's row
+  uint32_t M;
+  uint32_t per_row;    // producer workgroups per (rank, row)
+  uint32_t ctas;       // poller workgroups per row
+  int copy;
+  uint64_t spin_limit;
+  int poll_all;
+};
+
+template <int TP, int POL_PUSH, int POL_LD, int POL_ST>
+__global__ void __launch_bounds__(256) gather_push_poll_kernel(GatherStepArgs a) {
+  const uint32_t row_frags = TP * a.frags;
+  const uint32_t producers = TP * a.M * a.per_row;
+  if (blockIdx.x < producers) {
+    const uint32_t sm = blockIdx.x / a.per_row, chunk = blockIdx.x - sm * a.per_row;  // sm = s * M + m
+    const uint32_t s = sm / a.M, m = sm - s * a.M;
+    const u32x4 *src = a.shard + (size_t)sm * a.frags;
+    const __amdgpu_buffer_rsrc_t dst =
+        make_rsrc(a.box + ((size_t)m * row_frags + (size_t)s * a.frags) * 16u, a.frags * 16u);
+    for (uint32_t i = chunk * 256u + threadIdx.x; i < a.frags; i += a.per_row * 256u)
+      buf_store<POL_PUSH>(clean4(nt_load(src + i)), dst, i * 16u);
+    return;
+  }
+  const uint32_t c = blockIdx.x - producers, m = c / a.ctas, cta = c - m * a.ctas;
+  poll_row<POL_LD, POL_ST>(a.box + (size_t)m * row_frags * 16u, a.out + (size_t)m * row_frags, row_frags, cta, a.ctas,
+                           a.copy, a.spin_limit, a.poll_all);
 }
 
 }  // namespace arn

@@ -62,6 +62,15 @@ std::atomic<int> g_reduce_split{0};
 #ifndef ARNORM_POLL_ALL_MAX_BYTES
 #define ARNORM_POLL_ALL_MAX_BYTES (1u << 20)
 #endif
+// gather_push_poll runs as one launch when the gathered rows total at most this many
+// bytes, its pollers re-reading every pending fragment per pass, else as the pair
+// gather_push + gather_poll.  Measured on MI355X at TP=8 (HIP-graph replay, µs per
+// call, one launch vs pair): M=1 S=896 3.0 vs 3.9+, M=16 S=896 3.9 vs 4.8, M=1 S=10240
+// 3.2 vs 3.8, M=2 S=10240 4.1 vs 4.1, M=32 S=896 4.6 vs 4.4; above about half a MiB
+// the pollers' re-reads cost more than the launch they save.
+#ifndef ARNORM_GATHER_STEP_MAX_BYTES
+#define ARNORM_GATHER_STEP_MAX_BYTES (1u << 19)
+#endif
 constexpr int kPolPoll = ARNORM_POL_POLL;
 constexpr int kPolRearm = ARNORM_POL_REARM;
 constexpr int kPolPush = ARNORM_POL_PUSH;
@@ -177,13 +186,18 @@ int reduce_split(int M, bool have_box) {
   return k;
 }
 
-int launch_poll(uint8_t *box, u32x4 *out, uint32_t row_frags, int M, int copy, hipStream_t stream) {
-  // about one fragment per thread, the whole grid resident at once (at most 2048
-  // workgroups of 256 threads over 256 CUs), at least one workgroup per row
+// Poller workgroups per row: about one fragment per thread, the whole grid resident at
+// once (at most 2048 workgroups of 256 threads over 256 CUs), at least one per row.
+uint32_t poll_ctas(uint32_t row_frags, int M) {
   const uint32_t want = (row_frags + 255) / 256;
-  const uint32_t ctas = std::max(1u, std::min(want, 2048u / (uint32_t)M));
-  return launch(arn::gather_poll_kernel<kPolPoll, kPolRearm>, dim3(ctas, (unsigned)M), dim3(256), stream, box, out,
-                row_frags, copy ? 1 : 0, (uint64_t)g_spin_limit.load(std::memory_order_relaxed));
+  return std::max(1u, std::min(want, 2048u / (uint32_t)M));
+}
+
+int launch_poll(uint8_t *box, u32x4 *out, uint32_t row_frags, int M, int copy, hipStream_t stream) {
+  const int poll_all = (uint64_t)M * row_frags * 16u <= ARNORM_POLL_ALL_MAX_BYTES;
+  return launch(arn::gather_poll_kernel<kPolPoll, kPolRearm>, dim3(poll_ctas(row_frags, M), (unsigned)M), dim3(256),
+                stream, box, out, row_frags, copy ? 1 : 0, (uint64_t)g_spin_limit.load(std::memory_order_relaxed),
+                poll_all);
 }
 
 }  // namespace
@@ -351,6 +365,45 @@ int gather_poll(int32_t *mailbox, int32_t *out, int tp, int cap, int S, int M, i
   if (copy && static_cast<void *>(out) == static_cast<void *>(mailbox)) return ARNORM_BAD_ARG;
   return launch_poll(reinterpret_cast<uint8_t *>(mailbox), reinterpret_cast<u32x4 *>(out), (uint32_t)tp * S / 4, M,
                      copy, stream);
+}
+
+int gather_push_poll(const int32_t *shard, int32_t *mailbox, int32_t *out, int tp, int cap, int S, int M, int copy,
+                     hipStream_t stream) {
+  int rc = check_gather(tp, cap, S, M);
+  if (rc != ARNORM_OK) return rc;
+  if (!aligned16(shard) || !aligned16(mailbox) || (copy && !aligned16(out))) return ARNORM_BAD_ARG;
+  if (copy && (static_cast<void *>(out) == static_cast<void *>(mailbox) ||
+               static_cast<const void *>(out) == static_cast<const void *>(shard)))
+    return ARNORM_BAD_ARG;
+  const uint32_t frags = (uint32_t)S / 4;
+  if ((uint64_t)M * tp * S * 4 > ARNORM_GATHER_STEP_MAX_BYTES) {
+    // a larger grid: the same call as the pair of launches
+    rc = gather_push(shard, mailbox, tp, cap, S, 0, tp, M, stream);
+    if (rc != ARNORM_OK) return rc;
+    return gather_poll(mailbox, out, tp, cap, S, M, copy, stream);
+  }
+  arn::GatherStepArgs a;
+  a.shard = reinterpret_cast<const u32x4 *>(shard);
+  a.box = reinterpret_cast<uint8_t *>(mailbox);
+  a.out = reinterpret_cast<u32x4 *>(out);
+  a.frags = frags;
+  a.M = (uint32_t)M;
+  a.per_row = (frags + 255) / 256;
+  a.ctas = poll_ctas((uint32_t)tp * frags, M);
+  a.copy = copy ? 1 : 0;
+  a.spin_limit = g_spin_limit.load(std::memory_order_relaxed);
+  a.poll_all = 1;
+  const dim3 grid(tp * M * a.per_row + M * a.ctas);
+  switch (tp) {
+    case 2: return launch(arn::gather_push_poll_kernel<2, kPolPush, kPolPoll, kPolRearm>, grid, dim3(256), stream, a);
+    case 3: return launch(arn::gather_push_poll_kernel<3, kPolPush, kPolPoll, kPolRearm>, grid, dim3(256), stream, a);
+    case 4: return launch(arn::gather_push_poll_kernel<4, kPolPush, kPolPoll, kPolRearm>, grid, dim3(256), stream, a);
+    case 5: return launch(arn::gather_push_poll_kernel<5, kPolPush, kPolPoll, kPolRearm>, grid, dim3(256), stream, a);
+    case 6: return launch(arn::gather_push_poll_kernel<6, kPolPush, kPolPoll, kPolRearm>, grid, dim3(256), stream, a);
+    case 7: return launch(arn::gather_push_poll_kernel<7, kPolPush, kPolPoll, kPolRearm>, grid, dim3(256), stream, a);
+    case 8: return launch(arn::gather_push_poll_kernel<8, kPolPush, kPolPoll, kPolRearm>, grid, dim3(256), stream, a);
+  }
+  return ARNORM_NOT_SERVED;
 }
 
 int twoshot_push(const uint16_t *partial, int32_t *recv, int parities, int tp, int cap, int width, int parity,
