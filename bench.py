@@ -187,7 +187,8 @@ def twoshot_bytes(tp, m, width=HIDDEN):
 
 def time_twoshot(lib, torch, calls=1000, chunk=50, launches=20):
     """Two-shot stand-in: µs per graph-replayed call at TP=8, M=4 (push of 8 slots,
-    owner's reduce, read of the gather row), and the reduce / read kernels at M=4096."""
+    owner's reduce, read of the gather row) as one twoshot_push_reduce_read launch and
+    as the three launches, and the reduce / read kernels at M=4096."""
     from tp_all_reduce_arnorm_amd import workloads as wl
 
     res = {}
@@ -199,27 +200,31 @@ def time_twoshot(lib, torch, calls=1000, chunk=50, launches=20):
     parts = [torch.from_numpy(src.partials().view(np.int16)).cuda() for _ in range(2)]
     outs = [torch.empty((cfg.m, HIDDEN), dtype=torch.int16, device="cuda") for _ in range(2)]
 
-    def call(i):
+    def call(i, one_launch):
         p = i % 2
+        if one_launch:
+            assert lib.twoshot_push_reduce_read(parts[p], recv, gath, p, outs[p]) is True
+            return
         assert lib.twoshot_push(parts[p], recv, p, 0) is True
         assert lib.twoshot_reduce(recv, gath, p, cfg.m) is True
         assert lib.twoshot_read(gath, p, outs[p]) is True
 
-    for i in range(4):
-        call(i)
-    torch.cuda.synchronize()
-    g = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g):
-        for i in range(chunk):
-            call(i)
-    g.replay()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(calls // chunk):
+    for key, one_launch in (("us_per_call_m4", True), ("three_launch_us_per_call_m4", False)):
+        for i in range(4):
+            call(i, one_launch)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(chunk):
+                call(i, one_launch)
         g.replay()
-    torch.cuda.synchronize()
-    res["us_per_call_m4"] = (time.perf_counter() - t0) / (calls // chunk * chunk) * 1e6
-    del g
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(calls // chunk):
+            g.replay()
+        torch.cuda.synchronize()
+        res[key] = (time.perf_counter() - t0) / (calls // chunk * chunk) * 1e6
+        del g
 
     cfg = wl.CONFIGS["c5"]
     p5 = torch.from_numpy(wl.ArNormInputs(cfg).partials().view(np.int16)).cuda()
@@ -395,7 +400,8 @@ def summarize_profiles(outdir):
                        "at M=32 (917504 B, so run as the pair gather_push of 8 slots + gather_poll with "
                        "copy), 1000 calls of that pair, then 1000 one-launch gather_push_poll calls at M=4",
              "gather_tp8_m32_s896_kernel_stats.md"),
-            ("twoshot", "Two-shot all-reduce stand-in (owners = 1): TP=8, M=4 graph-replayed calls (push, "
+            ("twoshot", "Two-shot all-reduce stand-in (owners = 1): TP=8, M=4 graph-replayed calls, 1000 as "
+                        "one twoshot_push_reduce_read launch each, then 1000 as the three launches (push, "
                         "owner's reduce, read), then 23 launches at TP=8, M=4096", "twoshot_tp8_kernel_stats.md")):
         if not os.path.exists(os.path.join(outdir, f"prof_{key}", f"{key}_kernel_stats.csv")):
             continue
@@ -584,8 +590,10 @@ def main():
         },
         "twoshot": {
             "workload": "two-shot all-reduce, owners = 1: push of 8 slots + owner's reduce + read of the "
-                        "gather row; TP=8 M=4 graph-replayed, and the kernels at TP=8 M=4096",
+                        "gather row; TP=8 M=4 graph-replayed as one twoshot_push_reduce_read launch per "
+                        "call (and as the three launches), and the kernels at TP=8 M=4096",
             "us_per_call_m4": round(ts["us_per_call_m4"], 3),
+            "three_launch_us_per_call_m4": round(ts["three_launch_us_per_call_m4"], 3),
             "reduce_us_m4096": round(ts["reduce_us_m4096"], 2),
             "reduce_frac": round(tsr / (ts["reduce_us_m4096"] * 1e-6) / 1e9 / PEAK_HBM_GBPS, 4),
             "read_us_m4096": round(ts["read_us_m4096"], 2),

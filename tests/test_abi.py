@@ -165,6 +165,24 @@ def test_twoshot_checks(L):
     assert L.twoshot_read(FAKE, FAKE + 0x100000, 2, 64, 7168, 0, 0, None) == 1
 
 
+def test_twoshot_push_reduce_read_checks(L):
+    P, R, G, O = FAKE, FAKE + 0x1000000, FAKE + 0x2000000, FAKE + 0x3000000
+    f = L.twoshot_push_reduce_read
+    assert f(P, R, G, O, 2, 1, 64, 7168, 0, 4, None) == 1    # tp 1
+    assert f(P, R, G, O, 2, 9, 64, 7168, 0, 4, None) == 1    # tp 9
+    assert f(P, R, G, O, 2, 8, 64, 7164, 0, 4, None) == 1    # width % 8
+    assert f(P, R, G, O, 2, 8, 64, 7168, 0, 65, None) == 1   # M > cap
+    assert f(P, R, G, O, 2, 8, 64, 7168, 2, 4, None) == 2    # parity
+    for m in (4, 64):  # one launch, and the three launches
+        assert f(MIS, R, G, O, 2, 8, 64, 7168, 0, m, None) == 2
+        assert f(P, R, G, MIS, 2, 8, 64, 7168, 0, m, None) == 2
+        assert f(P, R, R, O, 2, 8, 64, 7168, 0, m, None) == 2   # recv == gather
+        assert f(P, R, G, G, 2, 8, 64, 7168, 0, m, None) == 2   # out == gather
+        assert f(P, R, G, R, 2, 8, 64, 7168, 0, m, None) == 2   # out == recv
+        assert f(P, R, G, P, 2, 8, 64, 7168, 0, m, None) == 2   # out == partial
+        assert f(P, R, G, None, 2, 8, 64, 7168, 0, m, None) == 2
+
+
 def test_spin_limit_and_threads(L):
     old = L.arnorm_get_spin_limit()
     assert L.arnorm_set_spin_limit(0) == 2
@@ -184,5 +202,6 @@ def test_binding_mirrors_the_abi():
     from tp_all_reduce_arnorm_amd import _lib
 
     for n in ("lamport_arm", "arnorm_push", "arnorm_reduce_norm", "arnorm_push_reduce_norm", "gather_push",
-              "gather_poll", "gather_push_poll", "twoshot_push", "twoshot_reduce", "twoshot_read"):
+              "gather_poll", "gather_push_poll", "twoshot_push", "twoshot_reduce", "twoshot_read",
+              "twoshot_push_reduce_read"):
         assert callable(getattr(_lib, n))

@@ -151,3 +151,93 @@ def test_concurrent_owner_and_reader(lib, m):
             assert_bits_equal(host32(gath_d), gath_h, f"call {call} gather row")
     finally:
         lib.set_spin_limit(old)
+
+
+def tsr_call(lib, recv_d, gath_d, recv_h, gath_h, partials, parity):
+    """twoshot_push_reduce_read of every rank against the oracle's push, reduce and read;
+    both mailboxes bit-exact afterwards."""
+    tp, m, width = partials.shape
+    out_d = empty16((m, width))
+    assert lib.twoshot_push_reduce_read(dev16(partials), recv_d, gath_d, parity, out_d) is True
+    oracle.twoshot_push(recv_h, partials, parity, 0)
+    want = oracle.twoshot_reduce(recv_h, gath_h, parity, m)
+    assert_bits_equal(oracle.twoshot_read(gath_h, parity, m), want, "oracle read vs reduce")
+    got = host16(out_d)
+    assert_bits_equal(got, want, "one-call out")
+    assert_bits_equal(host32(recv_d), recv_h, "recv after the call")
+    assert_bits_equal(host32(gath_d), gath_h, "gather row after the call")
+    assert lib.status() == lib.OK
+    return got
+
+
+@pytest.mark.parametrize("name,calls", [("c2", 8), ("c3", 4)])
+def test_one_call_workloads(lib, name, calls):
+    """c2 (TP=8, M=4: one launch) and c3 (M=64: the three launches)."""
+    cfg = wl.CONFIGS[name]
+    say(f"[twoshot] one call {name}")
+    src = wl.ArNormInputs(cfg)
+    recv_d, gath_d, recv_h, gath_h = boxes(2, cfg.tp, cfg.cap, W)
+    for call in range(calls):
+        tsr_call(lib, recv_d, gath_d, recv_h, gath_h, src.partials(), call % 2)
+
+
+@pytest.mark.parametrize("tp,m", [(2, 13), (3, 13), (4, 13), (5, 13), (6, 9), (7, 9), (8, 9), (8, 13), (8, 1)])
+def test_one_call_torture(lib, tp, m):
+    """Torture rows through the one call, one launch where the TP slots of rows < M fit
+    1 MiB (all but TP=8, M=13), with the other parity published and left untouched."""
+    say(f"[twoshot] one call torture tp={tp} m={m}")
+    rng = np.random.default_rng(400 + 16 * tp + m)
+    cap = 17
+    recv_d, gath_d, recv_h, gath_h = boxes(2, tp, cap, W)
+    other = torture_partials(rng, tp, m)
+    assert lib.twoshot_push(dev16(other), recv_d, 1, 0) is True
+    oracle.twoshot_push(recv_h, other, 1, 0)
+    for _ in range(2):
+        got = tsr_call(lib, recv_d, gath_d, recv_h, gath_h, torture_partials(rng, tp, m), 0)
+        assert not np.any(got == 0x8000), "no negative zero in the reduced row"
+
+
+@pytest.mark.parametrize("width,m", [(8, 1), (64, 7), (7176, 3), (2 * 7168, 4)])
+def test_one_call_widths(lib, width, m):
+    say(f"[twoshot] one call width={width} m={m}")
+    rng = np.random.default_rng(500 + width + m)
+    tp, cap = 8, 9
+    recv_d, gath_d, recv_h, gath_h = boxes(3, tp, cap, width)
+    for call in range(4):
+        p = (rng.standard_normal((tp, m, width), dtype=np.float32).view(np.uint32) >> 16).astype(np.uint16)
+        p[:, :, 1::7] = 0x8000
+        tsr_call(lib, recv_d, gath_d, recv_h, gath_h, p, call % 3)
+
+
+def test_one_call_graph_replay(lib):
+    """Captured one-call two-shot calls over two parities, replayed three times with
+    eager work between the replays; every replay matches the oracle."""
+    import torch
+
+    say("[twoshot] one call graph replay")
+    rng = np.random.default_rng(600)
+    tp, m, cap = 8, 4, 64
+    recv_d, gath_d, recv_h, gath_h = boxes(2, tp, cap, W)
+    parts = [(rng.standard_normal((tp, m, W), dtype=np.float32).view(np.uint32) >> 16).astype(np.uint16)
+             for _ in range(2)]
+    parts_d = [dev16(p) for p in parts]
+    outs = [empty16((m, W)) for _ in range(2)]
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for k in range(2):
+            assert lib.twoshot_push_reduce_read(parts_d[k], recv_d, gath_d, k, outs[k]) is True
+    for rep in range(3):
+        for o in outs:
+            o.fill_(0x1234)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert lib.status() == lib.OK
+        for k in range(2):
+            oracle.twoshot_push(recv_h, parts[k], k, 0)
+            want = oracle.twoshot_reduce(recv_h, gath_h, k, m)
+            oracle.twoshot_read(gath_h, k, m)
+            assert_bits_equal(host16(outs[k]), want, f"replay {rep} parity {k}")
+        assert_bits_equal(host32(recv_d), recv_h, f"replay {rep} recv")
+        assert_bits_equal(host32(gath_d), gath_h, f"replay {rep} gather row")

@@ -38,6 +38,8 @@ _SIGNATURES = {
                               _c_ptr]),
     "twoshot_reduce": (_c_int, [_c_ptr, _c_ptr, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_ptr]),
     "twoshot_read": (_c_int, [_c_ptr, _c_ptr, _c_int, _c_int, _c_int, _c_int, _c_int, _c_ptr]),
+    "twoshot_push_reduce_read": (_c_int, [_c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_int, _c_int, _c_int, _c_int, _c_int,
+                                          _c_int, _c_ptr]),
     "arnorm_set_spin_limit": (_c_int, [_c_u64]),
     "arnorm_get_spin_limit": (_c_u64, []),
     "arnorm_set_reduce_threads": (_c_int, [_c_int]),
@@ -202,6 +204,19 @@ def twoshot_read(gather, parity, out, stream=None):
     assert width == 2 * words
     return _check("twoshot_read", LIB.twoshot_read(
         _ptr(gather, 4, "gather"), _ptr(out, 2, "out"), p, cap, width, parity, m, _stream(stream)))
+
+
+def twoshot_push_reduce_read(partial, recv, gather, parity, out, stream=None):
+    """One two-shot call of every rank: partial BF16 [tp, M, width] pushed into recv,
+    reduced by the owner into the gather row, read into out (BF16 [M, width]); one
+    launch for small calls."""
+    tp, m, width = partial.shape
+    p, tp2, cap, words = recv.shape
+    assert tp2 == tp and words * 2 == width and tuple(gather.shape) == (p, 1, cap, words)
+    assert tuple(out.shape) == (m, width)
+    return _check("twoshot_push_reduce_read", LIB.twoshot_push_reduce_read(
+        _ptr(partial, 2, "partial"), _ptr(recv, 4, "recv"), _ptr(gather, 4, "gather"), _ptr(out, 2, "out"), p, tp,
+        cap, width, parity, m, _stream(stream)))
 
 
 def set_spin_limit(polls):

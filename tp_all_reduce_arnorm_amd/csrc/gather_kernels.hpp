@@ -4,8 +4,9 @@
 // kernel): rank r's [M, S] shard of 32-bit words lands, cleaned, at columns r*S .. of
 // the [cap, TP*S] mailbox rows; the reader polls every fragment of its rows and either
 // copies them to a dense output and re-arms them, or leaves them published for a later
-// reader.  One-GPU stand-in: the ranks' shards are pushed by gather_push calls on the
-// same GPU, the pages' push-then-poll kernel is split into two kernels.
+// reader.  One-GPU stand-in: the ranks' shards are pushed on the same GPU, by
+// gather_push calls followed by gather_poll, or by the producer workgroups of one
+// gather_push_poll launch ahead of its pollers.
 #pragma once
 
 #include "device.hpp"
@@ -24,6 +25,16 @@ gather_push_kernel(const u32x4 *__restrict__ shard, uint8_t *__restrict__ box, u
       make_rsrc(box + (size_t)m * row_bytes + first_col_bytes + (size_t)s * frags * 16u, frags * 16u);
   for (uint32_t i = blockIdx.x * 256u + threadIdx.x; i < frags; i += gridDim.x * 256u)
     buf_store<POL>(clean4(nt_load(src + i)), dst, i * 16u);
+}
+
+// One producer workgroup's share of a cleaned copy: fragments chunk*256 + t, strided
+// by chunks*256, of `frags` contiguous source fragments into the buffer at dst.
+template <int POL>
+__device__ __forceinline__ void push_frags(const u32x4 *__restrict__ src, uint8_t *dst, uint32_t frags,
+                                           uint32_t chunk, uint32_t chunks) {
+  const __amdgpu_buffer_rsrc_t r = make_rsrc(dst, frags * 16u);
+  for (uint32_t i = chunk * 256u + threadIdx.x; i < frags; i += chunks * 256u)
+    buf_store<POL>(clean4(nt_load(src + i)), r, i * 16u);
 }
 
 // The poll of one row's fragments by workgroup `cta` of `ctas` (cta*256 + t, strided by
@@ -106,11 +117,8 @@ __global__ void __launch_bounds__(256) gather_push_poll_kernel(GatherStepArgs a)
   if (blockIdx.x < producers) {
     const uint32_t sm = blockIdx.x / a.per_row, chunk = blockIdx.x - sm * a.per_row;  // sm = s * M + m
     const uint32_t s = sm / a.M, m = sm - s * a.M;
-    const u32x4 *src = a.shard + (size_t)sm * a.frags;
-    const __amdgpu_buffer_rsrc_t dst =
-        make_rsrc(a.box + ((size_t)m * row_frags + (size_t)s * a.frags) * 16u, a.frags * 16u);
-    for (uint32_t i = chunk * 256u + threadIdx.x; i < a.frags; i += a.per_row * 256u)
-      buf_store<POL_PUSH>(clean4(nt_load(src + i)), dst, i * 16u);
+    push_frags<POL_PUSH>(a.shard + (size_t)sm * a.frags, a.box + ((size_t)m * row_frags + (size_t)s * a.frags) * 16u,
+                         a.frags, chunk, a.per_row);
     return;
   }
   const uint32_t c = blockIdx.x - producers, m = c / a.ctas, cta = c - m * a.ctas;

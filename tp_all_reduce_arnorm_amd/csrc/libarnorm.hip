@@ -71,6 +71,11 @@ std::atomic<int> g_reduce_split{0};
 #ifndef ARNORM_GATHER_STEP_MAX_BYTES
 #define ARNORM_GATHER_STEP_MAX_BYTES (1u << 19)
 #endif
+// twoshot_push_reduce_read runs as one launch when the TP slots of rows < M total at
+// most this many bytes, else as its three launches.
+#ifndef ARNORM_TWOSHOT_STEP_MAX_BYTES
+#define ARNORM_TWOSHOT_STEP_MAX_BYTES (1u << 20)
+#endif
 constexpr int kPolPoll = ARNORM_POL_POLL;
 constexpr int kPolRearm = ARNORM_POL_REARM;
 constexpr int kPolPush = ARNORM_POL_PUSH;
@@ -436,6 +441,7 @@ int twoshot_reduce(int32_t *recv, int32_t *gather, int parities, int tp, int cap
   a.slot_stride = (size_t)cap * row_bytes;
   a.frags = (uint32_t)((size_t)M * row_bytes / 16);
   a.spin_limit = g_spin_limit.load(std::memory_order_relaxed);
+  a.poll_all = (uint64_t)tp * a.frags * 16u <= ARNORM_POLL_ALL_MAX_BYTES;
   const dim3 grid(std::max(1u, std::min((a.frags + 255) / 256, 16384u)));
   switch (tp) {
     case 2: return launch(arn::twoshot_reduce_kernel<2, kPolPoll, kPolRearm, kPolPush>, grid, dim3(256), stream, a);
@@ -458,6 +464,49 @@ int twoshot_read(int32_t *gather, uint16_t *out, int parities, int cap, int widt
   const size_t row_bytes = (size_t)width * 2;
   return launch_poll(reinterpret_cast<uint8_t *>(gather) + (size_t)parity * cap * row_bytes,
                      reinterpret_cast<u32x4 *>(out), (uint32_t)(row_bytes / 16), M, 1, stream);
+}
+
+int twoshot_push_reduce_read(const uint16_t *partial, int32_t *recv, int32_t *gather, uint16_t *out, int parities,
+                             int tp, int cap, int width, int parity, int M, hipStream_t stream) {
+  if (tp < 2 || tp > 8) return ARNORM_NOT_SERVED;
+  int rc = check_twoshot(parities, cap, width, parity, M);
+  if (rc != ARNORM_OK) return rc;
+  if (!aligned16(partial) || !aligned16(recv) || !aligned16(gather) || !aligned16(out)) return ARNORM_BAD_ARG;
+  const void *p = partial, *r = recv, *g = gather, *o = out;
+  if (r == g || o == g || o == r || o == p) return ARNORM_BAD_ARG;
+  const size_t row_bytes = (size_t)width * 2;
+  const uint32_t frags = (uint32_t)((size_t)M * row_bytes / 16);
+  if ((uint64_t)tp * frags * 16u > ARNORM_TWOSHOT_STEP_MAX_BYTES) {
+    rc = twoshot_push(partial, recv, parities, tp, cap, width, parity, 0, tp, M, stream);
+    if (rc == ARNORM_OK) rc = twoshot_reduce(recv, gather, parities, tp, cap, width, parity, M, stream);
+    if (rc == ARNORM_OK) rc = twoshot_read(gather, out, parities, cap, width, parity, M, stream);
+    return rc;
+  }
+  arn::TwoShotStepArgs a;
+  a.r.recv = reinterpret_cast<uint8_t *>(recv) + (size_t)parity * tp * cap * row_bytes;
+  a.r.gather = reinterpret_cast<uint8_t *>(gather) + (size_t)parity * cap * row_bytes;
+  a.r.slot_stride = (size_t)cap * row_bytes;
+  a.r.frags = frags;
+  a.r.spin_limit = g_spin_limit.load(std::memory_order_relaxed);
+  a.r.poll_all = (uint64_t)tp * frags * 16u <= ARNORM_POLL_ALL_MAX_BYTES;
+  a.partial = reinterpret_cast<const u32x4 *>(partial);
+  a.out = reinterpret_cast<u32x4 *>(out);
+  a.per_slot = a.red_ctas = a.read_ctas = (frags + 255) / 256;
+  const dim3 grid(tp * a.per_slot + a.red_ctas + a.read_ctas);
+  switch (tp) {
+#define ARNORM_TWOSHOT_STEP(T)                                                                                      \
+  case T:                                                                                                           \
+    return launch(arn::twoshot_step_kernel<T, kPolPush, kPolPoll, kPolRearm, kPolPush>, grid, dim3(256), stream, a);
+    ARNORM_TWOSHOT_STEP(2)
+    ARNORM_TWOSHOT_STEP(3)
+    ARNORM_TWOSHOT_STEP(4)
+    ARNORM_TWOSHOT_STEP(5)
+    ARNORM_TWOSHOT_STEP(6)
+    ARNORM_TWOSHOT_STEP(7)
+    ARNORM_TWOSHOT_STEP(8)
+#undef ARNORM_TWOSHOT_STEP
+  }
+  return ARNORM_NOT_SERVED;
 }
 
 int arnorm_set_spin_limit(uint64_t polls) {
