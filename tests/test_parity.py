@@ -103,12 +103,15 @@ def test_split_rows(lib, name, split):
     run_config(lib, name, calls=min(wl.CONFIGS[name].calls, 12), split=split)
 
 
-@pytest.mark.parametrize("name,with_box", [("c1", True), ("c2", True), ("c3", True), ("c2", False)])
-def test_push_reduce_norm_one_call(lib, name, with_box):
-    """arnorm_push_reduce_norm (one launch with a norm box at M <= 64, else the pair of
-    launches) against the oracle's push of every slot followed by its consumer."""
+@pytest.mark.parametrize("name,with_box,split", [("c1", True, 0), ("c2", True, 0), ("c3", True, 0), ("c2", False, 0),
+                                                ("c1", True, 14), ("c2", True, 14)])
+def test_push_reduce_norm_one_call(lib, name, with_box, split):
+    """arnorm_push_reduce_norm (one launch with a norm box where the TP slots of rows < M
+    fit 1 MiB, rows split 7 or 14 ways; else the pair of launches) against the oracle's
+    push of every slot followed by its consumer."""
     cfg = wl.CONFIGS[name]
-    say(f"[parity] push_reduce_norm {name} norm_box={with_box}")
+    say(f"[parity] push_reduce_norm {name} norm_box={with_box} split={split}")
+    lib.set_reduce_split(split)
     src = wl.ArNormInputs(cfg)
     shape = (cfg.parities, cfg.tp, cfg.cap, W // 2)
     box_d, box_h = armed_box(shape), oracle.arm(np.empty(shape, dtype=np.uint32))
@@ -131,9 +134,10 @@ def test_push_reduce_norm_one_call(lib, name, with_box):
         assert lib.status() == lib.OK
 
 
-@pytest.mark.parametrize("tp", [2, 3, 8])
-def test_push_reduce_norm_torture(lib, tp):
-    say(f"[parity] push_reduce_norm torture tp={tp}")
+@pytest.mark.parametrize("tp,split", [(2, 0), (3, 0), (8, 0), (3, 14), (8, 14)])
+def test_push_reduce_norm_torture(lib, tp, split):
+    say(f"[parity] push_reduce_norm torture tp={tp} split={split}")
+    lib.set_reduce_split(split)
     rng = np.random.default_rng(170 + tp)
     m, cap = 13, 17
     shape = (2, tp, cap, W // 2)

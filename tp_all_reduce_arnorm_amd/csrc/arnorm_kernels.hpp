@@ -296,7 +296,7 @@ __global__ void __launch_bounds__(NT, reduce_occupancy(NT)) reduce_norm_kernel(R
 // reader.  The one-GPU stand-in of such a call puts every rank's push in the same grid:
 // workgroups [0, TP * per_slot) are the producers (per_slot of them per slot, the
 // lowest workgroup ids, which the dispatcher places first), the others are the row
-// consumers, split 7 ways (128 threads each), which poll until the producers' stores
+// consumers, split K ways (896/K threads each), which poll until the producers' stores
 // land, re-arm and reduce.
 struct StepArgs {
   ReduceArgs r;
@@ -305,9 +305,9 @@ struct StepArgs {
   uint32_t per_slot;      // producer workgroups per slot
 };
 
-template <int TP, bool RES, int U, int POL_PUSH, int POL_LD, int POL_ST, int POL_IO>
-__global__ void __launch_bounds__(128) push_reduce_kernel(StepArgs a) {
-  constexpr int K = 7, NT = kRowFrags / K;
+template <int TP, bool RES, int K, int U, int POL_PUSH, int POL_LD, int POL_ST, int POL_IO>
+__global__ void __launch_bounds__(kRowFrags / K) push_reduce_kernel(StepArgs a) {
+  constexpr int NT = kRowFrags / K;
   const uint32_t producers = TP * a.per_slot;
   if (blockIdx.x < producers) {
     const uint32_t s = blockIdx.x / a.per_slot, p = blockIdx.x - s * a.per_slot;

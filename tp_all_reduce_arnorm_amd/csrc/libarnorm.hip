@@ -291,9 +291,10 @@ int arnorm_push_reduce_norm(const uint16_t *partials, const uint16_t *residual, 
   if (!aligned16(partials) || (residual && !aligned16(residual))) return ARNORM_BAD_ARG;
   // One launch only where its consumer may re-read every slot on each poll pass (a small
   // grid): measured at TP=8 it is then faster than the pair (M=4: 4.8 against 5.3 us),
-  // while with witness polling (larger M) the pair of launches is faster.
-  const bool one_launch = norm_box != nullptr && reduce_split(M, true) == 7 &&
-                          (uint64_t)tp * M * arn::kRowBytes <= ARNORM_POLL_ALL_MAX_BYTES;
+  // while with witness polling (larger M) the pair of launches is faster.  Rows split 7
+  // ways beat 14 (M=4: 4.8 against 5.3 us) and one workgroup per row (6.5 us).
+  const int K = norm_box != nullptr ? reduce_split(M, true) : 1;
+  const bool one_launch = (K == 7 || K == 14) && (uint64_t)tp * M * arn::kRowBytes <= ARNORM_POLL_ALL_MAX_BYTES;
   if (!one_launch) {
     // the same call as two launches: every rank's push, then the consumer
     rc = arnorm_push(partials, mailbox, parities, tp, cap, parity, 0, tp, M, stream);
@@ -328,15 +329,19 @@ int arnorm_push_reduce_norm(const uint16_t *partials, const uint16_t *residual, 
   a.partials = reinterpret_cast<const u32x4 *>(partials);
   a.frags = (uint32_t)M * arn::kRowFrags;
   constexpr int U = ARNORM_STEP_PUSH_U;
-  a.per_slot = (a.frags + 128 * U - 1) / (128 * U);
-  const dim3 grid(tp * a.per_slot + M * 7);
+  const uint32_t nt = arn::kRowFrags / K;
+  a.per_slot = (a.frags + nt * U - 1) / (nt * U);
+  const dim3 grid(tp * a.per_slot + M * K);
   const bool res = residual != nullptr;
+#define ARNORM_STEP_LAUNCH_K(TPV, KV)                                                                              \
+  return res ? launch(arn::push_reduce_kernel<TPV, true, KV, U, kPolPush, kPolPoll, kPolRearm, kPolIO>, grid,     \
+                      dim3(nt), stream, a)                                                                         \
+             : launch(arn::push_reduce_kernel<TPV, false, KV, U, kPolPush, kPolPoll, kPolRearm, kPolIO>, grid,    \
+                      dim3(nt), stream, a);
 #define ARNORM_STEP_LAUNCH(TPV)                                                                                   \
   case TPV:                                                                                                      \
-    return res ? launch(arn::push_reduce_kernel<TPV, true, U, kPolPush, kPolPoll, kPolRearm, kPolIO>, grid,     \
-                        dim3(128), stream, a)                                                                    \
-               : launch(arn::push_reduce_kernel<TPV, false, U, kPolPush, kPolPoll, kPolRearm, kPolIO>, grid,    \
-                        dim3(128), stream, a);
+    if (K == 7) ARNORM_STEP_LAUNCH_K(TPV, 7)                                                                     \
+    ARNORM_STEP_LAUNCH_K(TPV, 14)
   switch (tp) {
     ARNORM_STEP_LAUNCH(2)
     ARNORM_STEP_LAUNCH(3)
@@ -347,6 +352,7 @@ int arnorm_push_reduce_norm(const uint16_t *partials, const uint16_t *residual, 
     ARNORM_STEP_LAUNCH(8)
   }
 #undef ARNORM_STEP_LAUNCH
+#undef ARNORM_STEP_LAUNCH_K
   return ARNORM_NOT_SERVED;
 }
 
