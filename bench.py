@@ -392,8 +392,9 @@ def summarize_profiles(outdir):
     prof = os.path.join(ROOT, "profiles")
     os.makedirs(prof, exist_ok=True)
     for key, title, fname in (
-            ("lat", "Stand-in ArNorm call at TP=8, M=4, no residual (arnorm_push of 8 slots + "
-                    "arnorm_reduce_norm, HIP-graph replay, 2000 calls)", "arnorm_tp8_m4_kernel_stats.md"),
+            ("lat", "Stand-in ArNorm call at TP=8, M=4, no residual: one arnorm_push_reduce_norm launch per "
+                    "call (the 8 ranks' pushes and the consumer, rows split 7 ways through the norm box), "
+                    "HIP-graph replay, 2000 calls", "arnorm_tp8_m4_kernel_stats.md"),
             ("roof", "ArNorm kernels at TP=8, M=4096, residual (one push of 8 slots + one consumer "
                      "launch, 23 times)", "arnorm_tp8_m4096_kernel_stats.md"),
             ("gather", "Gather at TP=8, S=896 words, cap=64, HIP-graph replay: 1000 gather_push_poll calls "
