@@ -72,13 +72,16 @@ def committed_traffic(kernel_key):
     return entry.get("bytes_per_launch")
 
 
-def time_latency(lib, torch, steps, warmup, chunk=50, one_launch=True):
-    """µs per stand-in call at TP=8, M=4 (no residual), graph-replayed.  one_launch:
-    arnorm_push_reduce_norm (every rank's push and the consumer in one launch); else the
-    pair arnorm_push + arnorm_reduce_norm."""
+def time_latency(lib, torch, steps, warmup, chunk=50, one_launch=True, m=None):
+    """Seconds for `steps` stand-in calls at TP=8, M=4 (or M=m), no residual,
+    graph-replayed.  one_launch: arnorm_push_reduce_norm (every rank's push and the
+    consumer in one launch where the slots fit 1 MiB, else the pair); else the pair
+    arnorm_push + arnorm_reduce_norm."""
+    import dataclasses
+
     from tp_all_reduce_arnorm_amd import workloads as wl
 
-    cfg = wl.CONFIGS["c2"]
+    cfg = wl.CONFIGS["c2"] if m is None else dataclasses.replace(wl.CONFIGS["c2"], m=m)
     src = wl.ArNormInputs(cfg)
     box = torch.empty((2, cfg.tp, cfg.cap, HIDDEN // 2), dtype=torch.int32, device="cuda")
     nbox = torch.empty((2, cfg.cap, 256), dtype=torch.int32, device="cuda")
@@ -185,10 +188,11 @@ def twoshot_bytes(tp, m, width=HIDDEN):
     return 2 * tp * m * row + m * row, 3 * m * row
 
 
-def time_twoshot(lib, torch, calls=1000, chunk=50, launches=20):
+def time_twoshot(lib, torch, calls=1000, chunk=50, launches=20, modes=("cold", "warm")):
     """Two-shot stand-in: µs per graph-replayed call at TP=8, M=4 (push of 8 slots,
     owner's reduce, read of the gather row) as one twoshot_push_reduce_read launch and
-    as the three launches, and the reduce / read kernels at M=4096."""
+    as the three launches, and the reduce / read kernels at M=4096 (cold and warm, as
+    in time_roofline)."""
     from tp_all_reduce_arnorm_amd import workloads as wl
 
     res = {}
@@ -232,28 +236,41 @@ def time_twoshot(lib, torch, calls=1000, chunk=50, launches=20):
     gath = torch.empty((1, 1, cfg.cap, HIDDEN // 2), dtype=torch.int32, device="cuda")
     assert lib.lamport_arm(recv) is True and lib.lamport_arm(gath) is True
     out = torch.empty((cfg.m, HIDDEN), dtype=torch.int16, device="cuda")
-    red, rd = [], []
-    for i in range(launches + 3):
-        e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
-        assert lib.twoshot_push(p5, recv, 0, 0) is True
-        e[0].record()
-        assert lib.twoshot_reduce(recv, gath, 0, cfg.m) is True
-        e[1].record()
-        e[2].record()
-        assert lib.twoshot_read(gath, 0, out) is True
-        e[3].record()
-        if i >= 3:
-            red.append((e[0], e[1]))
-            rd.append((e[2], e[3]))
-    torch.cuda.synchronize()
-    assert lib.status() == lib.OK
-    res["reduce_us_m4096"] = float(np.mean([a.elapsed_time(b) for a, b in red])) * 1e3
-    res["read_us_m4096"] = float(np.mean([a.elapsed_time(b) for a, b in rd])) * 1e3
+    evict = torch.ones(1 << 28, dtype=torch.float32, device="cuda") if "cold" in modes else None
+    for mode in modes:  # as time_roofline: "cold" evicts the last-level cache before each timed launch
+        red, rd = [], []
+        for i in range(launches + 3):
+            e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+            assert lib.twoshot_push(p5, recv, 0, 0) is True
+            if mode == "cold":
+                evict.sum()
+            e[0].record()
+            assert lib.twoshot_reduce(recv, gath, 0, cfg.m) is True
+            e[1].record()
+            if mode == "cold":
+                evict.sum()
+            e[2].record()
+            assert lib.twoshot_read(gath, 0, out) is True
+            e[3].record()
+            if i >= 3:
+                red.append((e[0], e[1]))
+                rd.append((e[2], e[3]))
+        torch.cuda.synchronize()
+        assert lib.status() == lib.OK
+        sfx = "" if mode == "cold" else "_warm"
+        res["reduce_us_m4096" + sfx] = float(np.mean([a.elapsed_time(b) for a, b in red])) * 1e3
+        res["read_us_m4096" + sfx] = float(np.mean([a.elapsed_time(b) for a, b in rd])) * 1e3
     return res
 
 
-def time_roofline(lib, torch, launches=20):
-    """Consumer and producer kernels at TP=8, M=4096 with residual."""
+def time_roofline(lib, torch, launches=20, modes=("cold", "warm")):
+    """Consumer and producer kernels at TP=8, M=4096 with residual, each launch timed
+    with HIP events on the launch stream.  "cold": before every timed launch a 1 GiB
+    read-only pass over an unrelated buffer leaves MI355X's 256 MB last-level cache
+    holding clean lines of that buffer, so the kernel's bytes come from HBM.  "warm": the
+    push and the consumer back to back, as the call runs, where the consumer finds part of
+    what the push just wrote still in that cache.  Returns cfg and {mode: (reduce_us,
+    push_us)}."""
     from tp_all_reduce_arnorm_amd import workloads as wl
 
     cfg = wl.CONFIGS["c5"]
@@ -267,31 +284,39 @@ def time_roofline(lib, torch, launches=20):
     del p, r
     out = torch.empty((cfg.m, HIDDEN), dtype=torch.int16, device="cuda")
     rout = torch.empty((cfg.m, HIDDEN), dtype=torch.int16, device="cuda")
-    red, push = [], []
-    for i in range(launches + 3):
-        a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        b0, b1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a0.record()
-        assert lib.arnorm_push(p_d, box, 0, 0) is True
-        a1.record()
-        b0.record()
-        assert lib.arnorm_reduce_norm(r_d, g_d, box, 0, EPS, out, rout) is True
-        b1.record()
-        if i >= 3:
-            push.append((a0, a1))
-            red.append((b0, b1))
-    torch.cuda.synchronize()
-    assert lib.status() == lib.OK
-    red_us = float(np.mean([a.elapsed_time(b) for a, b in red])) * 1e3
-    push_us = float(np.mean([a.elapsed_time(b) for a, b in push])) * 1e3
-    return cfg, red_us, push_us
+    evict = torch.ones(1 << 28, dtype=torch.float32, device="cuda") if "cold" in modes else None
+    res = {}
+    for mode in modes:
+        red, push = [], []
+        for i in range(launches + 3):
+            a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            b0, b1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            if mode == "cold":
+                evict.sum()
+            a0.record()
+            assert lib.arnorm_push(p_d, box, 0, 0) is True
+            a1.record()
+            if mode == "cold":
+                evict.sum()
+            b0.record()
+            assert lib.arnorm_reduce_norm(r_d, g_d, box, 0, EPS, out, rout) is True
+            b1.record()
+            if i >= 3:
+                push.append((a0, a1))
+                red.append((b0, b1))
+        torch.cuda.synchronize()
+        assert lib.status() == lib.OK
+        res[mode] = (float(np.mean([a.elapsed_time(b) for a, b in red])) * 1e3,
+                     float(np.mean([a.elapsed_time(b) for a, b in push])) * 1e3)
+    return cfg, res
 
 
 def pmc_workload(lib, torch, launches=3):
     """What the rocprofv3 counter runs profile: the consumer and producer kernels at
     TP=8, M=4096 with residual, and a plain 1 GiB device copy (torch's copy kernel)
     whose FETCH_SIZE / WRITE_SIZE calibrate the counters against known bytes."""
-    cfg, red_us, push_us = time_roofline(lib, torch, launches=launches)
+    cfg, t = time_roofline(lib, torch, launches=launches, modes=("warm",))
+    red_us, push_us = t["warm"]
     # the two-shot owner's reduce and the gather-row read at the same size
     from tp_all_reduce_arnorm_amd import workloads as wl
 
@@ -392,18 +417,22 @@ def summarize_profiles(outdir):
     prof = os.path.join(ROOT, "profiles")
     os.makedirs(prof, exist_ok=True)
     for key, title, fname in (
-            ("lat", "Stand-in ArNorm call at TP=8, M=4, no residual: one arnorm_push_reduce_norm launch per "
-                    "call (the 8 ranks' pushes and the consumer, rows split 7 ways through the norm box), "
-                    "HIP-graph replay, 2000 calls", "arnorm_tp8_m4_kernel_stats.md"),
-            ("roof", "ArNorm kernels at TP=8, M=4096, residual (one push of 8 slots + one consumer "
-                     "launch, 23 times)", "arnorm_tp8_m4096_kernel_stats.md"),
+            ("lat", "Stand-in ArNorm call at TP=8, M=4, no residual, HIP-graph replay: 2000 calls of one "
+                    "arnorm_push_reduce_norm launch each (the 8 ranks' pushes and the consumer, rows split "
+                    "7 ways through the norm box), then 2000 calls as the pair arnorm_push of 8 slots + "
+                    "arnorm_reduce_norm", "arnorm_tp8_m4_kernel_stats.md"),
+            ("roof", "ArNorm kernels at TP=8, M=4096, residual: one push of 8 slots + one consumer launch, "
+                     "23 times, each launch after a 1 GiB read-only pass (torch's float32 sum) that evicts the "
+                     "last-level cache", "arnorm_tp8_m4096_kernel_stats.md"),
             ("gather", "Gather at TP=8, S=896 words, cap=64, HIP-graph replay: 1000 gather_push_poll calls "
                        "at M=32 (917504 B, so run as the pair gather_push of 8 slots + gather_poll with "
                        "copy), 1000 calls of that pair, then 1000 one-launch gather_push_poll calls at M=4",
              "gather_tp8_m32_s896_kernel_stats.md"),
             ("twoshot", "Two-shot all-reduce stand-in (owners = 1): TP=8, M=4 graph-replayed calls, 1000 as "
                         "one twoshot_push_reduce_read launch each, then 1000 as the three launches (push, "
-                        "owner's reduce, read), then 23 launches at TP=8, M=4096", "twoshot_tp8_kernel_stats.md")):
+                        "owner's reduce, read), then 23 calls at TP=8, M=4096 whose reduce and read each follow "
+                        "a 1 GiB read-only pass (torch's float32 sum) that evicts the last-level cache",
+             "twoshot_tp8_kernel_stats.md")):
         if not os.path.exists(os.path.join(outdir, f"prof_{key}", f"{key}_kernel_stats.csv")):
             continue
         rows, table = _stats_table(os.path.join(outdir, f"prof_{key}", f"{key}_kernel_stats.csv"))
@@ -491,13 +520,14 @@ def main():
     sha = kernel_sources_hash()
     if args.mode == "latency":
         elapsed = time_latency(lib, torch, args.steps, args.warmup)
-        print(json.dumps({"mode": "latency", "us_per_call": elapsed / args.steps * 1e6, "sources_sha": sha}),
-              flush=True)
+        pair = time_latency(lib, torch, args.steps, args.warmup, one_launch=False)
+        print(json.dumps({"mode": "latency", "us_per_call": elapsed / args.steps * 1e6,
+                          "two_launch_us_per_call": pair / args.steps * 1e6, "sources_sha": sha}), flush=True)
         return
     if args.mode == "roofline":
-        _, red_us, push_us = time_roofline(lib, torch)
-        print(json.dumps({"mode": "roofline", "reduce_us": red_us, "push_us": push_us, "sources_sha": sha}),
-              flush=True)
+        _, t = time_roofline(lib, torch, modes=("cold",))
+        print(json.dumps({"mode": "roofline", "reduce_us": t["cold"][0], "push_us": t["cold"][1],
+                          "sources_sha": sha}), flush=True)
         return
     if args.mode == "gather":
         _, us = time_gather(lib, torch)
@@ -507,14 +537,18 @@ def main():
                           "m4_one_launch_us_per_call": m4_us, "sources_sha": sha}), flush=True)
         return
     if args.mode == "twoshot":
-        print(json.dumps(dict(mode="twoshot", sources_sha=sha, **time_twoshot(lib, torch))), flush=True)
+        print(json.dumps(dict(mode="twoshot", sources_sha=sha, **time_twoshot(lib, torch, modes=("cold",)))),
+              flush=True)
         return
     if args.mode == "pmc":
         print(json.dumps(dict(mode="pmc", sources_sha=sha, **pmc_workload(lib, torch))), flush=True)
         return
     elapsed = time_latency(lib, torch, args.steps, args.warmup)
     pair_us = time_latency(lib, torch, args.steps, args.warmup, one_launch=False) / args.steps * 1e6
-    cfg5, red_us, push_us = time_roofline(lib, torch)
+    m_us = {m: time_latency(lib, torch, args.steps, args.warmup, m=m) / args.steps * 1e6 for m in (1, 64)}
+    cfg5, troof = time_roofline(lib, torch)
+    red_us, push_us = troof["cold"]
+    warm_red_us, warm_push_us = troof["warm"]
     cfg4, gather_us = time_gather(lib, torch)
     _, gather_pair_us = time_gather(lib, torch, one_launch=False)
     ts = time_twoshot(lib, torch)
@@ -563,6 +597,7 @@ def main():
                         "launch, rows split over 7 workgroups through the norm box); HIP-graph replay",
             "tp": 8, "m": 4, "hidden": HIDDEN, "parities": 2, "residual": False,
             "two_launch_us_per_call": round(pair_us, 3),
+            "m1_us_per_call": round(m_us[1], 3), "m64_us_per_call": round(m_us[64], 3),
         },
         "roofline": {
             "bound": "hbm",
@@ -575,30 +610,42 @@ def main():
             "workload": "ArNorm TP=8 M=4096 width 7168, residual=True",
             "algorithmic_bytes": rb,
             "kernel_us": round(red_us, 2),
+            "cache": "cold: before each timed launch a 1 GiB read of an unrelated buffer leaves the 256 MB "
+                     "last-level cache holding none of the kernel's data, so its bytes come from HBM",
+            "warm": {"kernel_us": round(warm_red_us, 2), "frac": round(rb / (warm_red_us * 1e-6) / 1e9 / PEAK_HBM_GBPS, 4),
+                     "note": "right after the push, as the call runs: part of the slots the push just wrote "
+                             "are still in the last-level cache"},
         },
         "push": {
-            "kernel": "arnorm_push", "workload": "8 slots, M=4096", "algorithmic_bytes": pb,
+            "kernel": "arnorm_push", "workload": "8 slots, M=4096, cold as the roofline", "algorithmic_bytes": pb,
             "kernel_us": round(push_us, 2), "achieved_gbps": round(pb / (push_us * 1e-6) / 1e9, 1),
             "frac": round(pb / (push_us * 1e-6) / 1e9 / PEAK_HBM_GBPS, 4),
+            "warm": {"kernel_us": round(warm_push_us, 2),
+                     "frac": round(pb / (warm_push_us * 1e-6) / 1e9 / PEAK_HBM_GBPS, 4),
+                     "note": "right after the previous consumer, whose written lines the cache still holds"},
         },
         "gather": {
             "workload": "Gather TP=8 M=32 S=896 words cap=64: gather_push_poll with copy, HIP-graph replay "
                         "(917504 B of gathered rows, above the 512 KiB one-launch limit, so it runs as "
                         "the pair gather_push + gather_poll; the c4_m4 and logits_m1 drafter_shapes "
                         "entries are one-launch calls); two_launch_us_per_call is the pair itself",
-            "us_per_call": round(gather_us, 3), "two_launch_us_per_call": round(gather_pair_us, 3), "push_algorithmic_bytes": gpb, "poll_algorithmic_bytes": gqb,
+            "us_per_call": round(gather_us, 3), "two_launch_us_per_call": round(gather_pair_us, 3),
+            "push_algorithmic_bytes": gpb, "poll_algorithmic_bytes": gqb,
             "drafter_shapes": shapes,
         },
         "twoshot": {
             "workload": "two-shot all-reduce, owners = 1: push of 8 slots + owner's reduce + read of the "
                         "gather row; TP=8 M=4 graph-replayed as one twoshot_push_reduce_read launch per "
-                        "call (and as the three launches), and the kernels at TP=8 M=4096",
+                        "call (and as the three launches), and the kernels at TP=8 M=4096, cold as the "
+                        "roofline (warm: right after the push / the reduce)",
             "us_per_call_m4": round(ts["us_per_call_m4"], 3),
             "three_launch_us_per_call_m4": round(ts["three_launch_us_per_call_m4"], 3),
             "reduce_us_m4096": round(ts["reduce_us_m4096"], 2),
             "reduce_frac": round(tsr / (ts["reduce_us_m4096"] * 1e-6) / 1e9 / PEAK_HBM_GBPS, 4),
             "read_us_m4096": round(ts["read_us_m4096"], 2),
             "read_frac": round(tsq / (ts["read_us_m4096"] * 1e-6) / 1e9 / PEAK_HBM_GBPS, 4),
+            "warm_reduce_frac": round(tsr / (ts["reduce_us_m4096_warm"] * 1e-6) / 1e9 / PEAK_HBM_GBPS, 4),
+            "warm_read_frac": round(tsq / (ts["read_us_m4096_warm"] * 1e-6) / 1e9 / PEAK_HBM_GBPS, 4),
             "reduce_algorithmic_bytes": tsr, "read_algorithmic_bytes": tsq,
         },
         "cpu_baseline": cpu,
