@@ -275,6 +275,38 @@ def test_gather_push_poll_one_call(lib, name, m):
     assert_bits_equal(host32(gbox_d), gbox_h, "gather mailbox re-armed")
 
 
+@pytest.mark.parametrize("tp,m,s", [(8, 4096, 896), (2, 4096, 4), (4, 1024, 10240)])
+def test_gather_large(lib, tp, m, s):
+    """Large gathers with M = cap: up to 168 MB of shards as the pair of launches, and at
+    S=4 one launch of 12288 workgroups; through gather_push_poll with copy, then no copy
+    followed by a copying gather_poll; every word and the whole mailbox compared with the
+    oracle."""
+    import dataclasses
+
+    import torch
+
+    say(f"[parity] gather large tp={tp} M={m} S={s}")
+    cfg = dataclasses.replace(wl.CONFIGS["c4"], tp=tp, m=m, s=s, cap=m, seed=40 + tp)
+    shards = wl.gather_shards(cfg)
+    gshape = (cfg.cap, tp * s)
+    gbox_d, gbox_h = armed_box(gshape), oracle.arm(np.empty(gshape, dtype=np.uint32))
+    sh_d = dev32(shards)
+    out_d = torch.empty((m, tp * s), dtype=torch.int32, device="cuda")
+    assert lib.gather_push_poll(sh_d, gbox_d, out=out_d, copy=True) is True
+    oracle.gather_push(gbox_h, shards, 0)
+    assert_bits_equal(host32(out_d), oracle.gather_poll(gbox_h, m, True), "gathered words")
+    assert_bits_equal(host32(gbox_d), gbox_h, "mailbox re-armed")
+    assert lib.gather_push_poll(sh_d, gbox_d, copy=False) is True
+    oracle.gather_push(gbox_h, shards, 0)
+    assert oracle.gather_poll(gbox_h, m, False) is None
+    assert_bits_equal(host32(gbox_d), gbox_h, "mailbox left published")
+    out_d.fill_(0x1234)
+    assert lib.gather_poll(gbox_d, tp, m, out=out_d, copy=True) is True
+    assert_bits_equal(host32(out_d), oracle.gather_poll(gbox_h, m, True), "later reader")
+    assert_bits_equal(host32(gbox_d), gbox_h, "mailbox re-armed by the later reader")
+    assert lib.status() == lib.OK
+
+
 def test_c5_full_size_sampled_rows(lib):
     """M = 4096, TP = 8, in the launch configuration the benchmark times; the oracle
     checks a sample of rows one by one (rows are independent), and the whole mailbox
