@@ -183,6 +183,15 @@ def test_twoshot_push_reduce_read_checks(L):
         assert f(P, R, G, None, 2, 8, 64, 7168, 0, m, None) == 2
 
 
+def test_poll_knob(L):
+    for u, mode in ((3, 0), (2, 0), (0, 3), (0, -1), (8, 1)):
+        assert L.arnorm_set_poll(u, mode) == 2
+    for u in (0, 1, 4):
+        for mode in (0, 1, 2):
+            assert L.arnorm_set_poll(u, mode) == 0
+    assert L.arnorm_set_poll(0, 0) == 0
+
+
 def test_spin_limit_and_threads(L):
     old = L.arnorm_get_spin_limit()
     assert L.arnorm_set_spin_limit(0) == 2

@@ -19,9 +19,11 @@ EPS = 1e-6
 def _defaults(lib):
     lib.set_reduce_threads(0)
     lib.set_reduce_split(0)
+    lib.set_poll(0, 0)
     yield
     lib.set_reduce_threads(0)
     lib.set_reduce_split(0)
+    lib.set_poll(0, 0)
 
 
 def norm_box_for(box_shape):
@@ -273,6 +275,32 @@ def test_gather_push_poll_one_call(lib, name, m):
     assert lib.gather_poll(gbox_d, cfg.tp, m, out=out_d, copy=True) is True  # the later reader
     assert_bits_equal(host32(out_d), oracle.gather_poll(gbox_h, m, True), "later reader")
     assert_bits_equal(host32(gbox_d), gbox_h, "gather mailbox re-armed")
+
+
+@pytest.mark.parametrize("u,mode", [(1, 2), (4, 1), (4, 2)])
+@pytest.mark.parametrize("name,m", [("c4", 16), ("c4", 1), ("logits", 1)])
+def test_gather_poll_layouts_one_launch(lib, name, m, u, mode):
+    """gather_push_poll in one launch, its pollers forced to 1 or 4 fragments per thread and
+    to re-read or witness waits: the producers in the same grid are still writing when
+    the pollers start, so every wait path runs; out and mailbox bit-exact."""
+    import dataclasses
+
+    import torch
+
+    say(f"[parity] gather one launch {name} M={m} frags/thread={u} mode={mode}")
+    lib.set_poll(u, mode)
+    cfg = dataclasses.replace(wl.CONFIGS[name], m=m)
+    shards = wl.gather_shards(cfg) if name == "c4" else wl.bf16_shards(cfg)
+    gshape = (cfg.cap, cfg.tp * cfg.s)
+    gbox_d, gbox_h = armed_box(gshape), oracle.arm(np.empty(gshape, dtype=np.uint32))
+    sh_d = dev32(shards)
+    for _ in range(3):
+        out_d = torch.empty((m, cfg.tp * cfg.s), dtype=torch.int32, device="cuda")
+        assert lib.gather_push_poll(sh_d, gbox_d, out=out_d, copy=True) is True
+        oracle.gather_push(gbox_h, shards, 0)
+        assert_bits_equal(host32(out_d), oracle.gather_poll(gbox_h, m, True), "gathered words")
+        assert_bits_equal(host32(gbox_d), gbox_h, "gather mailbox")
+        assert lib.status() == lib.OK
 
 
 @pytest.mark.parametrize("tp,m,s", [(8, 4096, 896), (2, 4096, 4), (4, 1024, 10240)])

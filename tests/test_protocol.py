@@ -116,11 +116,10 @@ def test_graph_replay_alternating_parities(lib):
 
 @pytest.mark.parametrize("m,residual,split", [(4, False, None), (64, True, None), (1, True, None),
                                               (4, False, 14), (64, True, 7)])
-def test_concurrent_consumer_polls_while_producer_pushes(lib, m, residual, split):
+def test_concurrent_consumer_polls_while_producer_pushes(lib, side_streams, m, residual, split):
     """The Lamport mode proper: the consumer is launched first on its own stream and
     spins on the mailbox while the producer, delayed on another stream, pushes; no
-    kernel boundary orders them.  Every call must match the oracle.  (A spin limit of
-    2^16 passes ends the wait early should the two streams ever be serialized.)"""
+    kernel boundary orders them.  Every call must match the oracle."""
     import torch
 
     say(f"[protocol] concurrent consumer-first M={m} residual={residual} split={split}")
@@ -138,7 +137,7 @@ def test_concurrent_consumer_polls_while_producer_pushes(lib, m, residual, split
         gamma = (gamma >> 16).astype(np.uint16)
         g_d = dev16(gamma)
         cur = torch.cuda.current_stream()
-        s_prod, s_cons = torch.cuda.Stream(), torch.cuda.Stream()
+        s_prod, s_cons = side_streams[0], side_streams[1]
         for call in range(6):
             parity = call % 2
             p = (rng.standard_normal((tp, m, W), dtype=np.float32).view(np.uint32) >> 16).astype(np.uint16)
@@ -171,12 +170,17 @@ def test_concurrent_consumer_polls_while_producer_pushes(lib, m, residual, split
         lib.set_reduce_split(0)
 
 
-def test_concurrent_gather_consumer_first(lib):
+@pytest.mark.parametrize("frags_per_thread", [0, 4])
+def test_concurrent_gather_consumer_first(lib, side_streams, frags_per_thread):
+    """The poll launched first on its own stream, the push later and delayed, at c4, with
+    the witness wait forced: one fragment per thread (automatic) or 4 in flight per
+    thread (forced)."""
     import torch
 
-    say("[protocol] concurrent gather consumer-first")
+    say(f"[protocol] concurrent gather consumer-first frags/thread={frags_per_thread}")
     old = lib.get_spin_limit()
     lib.set_spin_limit(1 << 16)
+    lib.set_poll(frags_per_thread, 2)
     try:
         cfg = wl.CONFIGS["c4"]
         shards = wl.gather_shards(cfg)
@@ -185,7 +189,7 @@ def test_concurrent_gather_consumer_first(lib):
         gbox_h = oracle.arm(np.empty(gshape, dtype=np.uint32))
         sh_d = dev32(shards)
         cur = torch.cuda.current_stream()
-        s_prod, s_cons = torch.cuda.Stream(), torch.cuda.Stream()
+        s_prod, s_cons = side_streams[0], side_streams[1]
         for _ in range(3):
             out_d = torch.empty((cfg.m, cfg.tp * cfg.s), dtype=torch.int32, device="cuda")
             torch.cuda.synchronize()
@@ -205,3 +209,4 @@ def test_concurrent_gather_consumer_first(lib):
             assert_bits_equal(host32(gbox_d), gbox_h, "gather mailbox")
     finally:
         lib.set_spin_limit(old)
+        lib.set_poll(0, 0)

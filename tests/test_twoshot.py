@@ -110,7 +110,7 @@ def test_m4096_sampled_rows(lib):
 
 
 @pytest.mark.parametrize("m", [4, 64])
-def test_concurrent_owner_and_reader(lib, m):
+def test_concurrent_owner_and_reader(lib, side_streams, m):
     """Reader first, owner second, producer last and delayed, each on its own stream:
     every wait is a Lamport poll; each call matches the oracle."""
     import torch
@@ -123,7 +123,7 @@ def test_concurrent_owner_and_reader(lib, m):
         tp, cap = 8, 64
         recv_d, gath_d, recv_h, gath_h = boxes(2, tp, cap, W)
         cur = torch.cuda.current_stream()
-        s_prod, s_own, s_read = torch.cuda.Stream(), torch.cuda.Stream(), torch.cuda.Stream()
+        s_prod, s_own, s_read = side_streams
         for call in range(4):
             parity = call % 2
             p = (rng.standard_normal((tp, m, W), dtype=np.float32).view(np.uint32) >> 16).astype(np.uint16)

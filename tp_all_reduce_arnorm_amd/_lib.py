@@ -44,6 +44,7 @@ _SIGNATURES = {
     "arnorm_get_spin_limit": (_c_u64, []),
     "arnorm_set_reduce_threads": (_c_int, [_c_int]),
     "arnorm_set_reduce_split": (_c_int, [_c_int]),
+    "arnorm_set_poll": (_c_int, [_c_int, _c_int]),
     "arnorm_status": (_c_int, [ctypes.POINTER(_c_int), _c_ptr]),
     "arnorm_strerror": (ctypes.c_char_p, [_c_int]),
 }
@@ -229,6 +230,12 @@ def get_spin_limit():
 
 def set_reduce_split(workgroups_per_row):
     return _check("arnorm_set_reduce_split", LIB.arnorm_set_reduce_split(workgroups_per_row))
+
+
+def set_poll(frags_per_thread=0, mode=0):
+    """Gather poll layout: fragments per thread in flight (0 auto, 1, 4) and the wait
+    (0 auto, 1 re-read every pending fragment, 2 one witness per wave)."""
+    return _check("arnorm_set_poll", LIB.arnorm_set_poll(frags_per_thread, mode))
 
 
 def set_reduce_threads(threads):

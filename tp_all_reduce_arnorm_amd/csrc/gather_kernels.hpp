@@ -84,14 +84,79 @@ __device__ __forceinline__ void poll_row(uint8_t *row, u32x4 *out_row, uint32_t 
   }
 }
 
-// gather_poll: grid (ctas, M); workgroup `cta` of row m.
-template <int POL_LD, int POL_ST>
+// poll_row with U fragments per thread in flight, for a grid too large to give every
+// fragment a thread of its own: workgroup `cta` of `ctas` takes blocks of 256*U
+// fragments (blk + u*256 + t), strided by ctas*256*U, issues the U loads of a thread
+// together, and waits on the thread's pending ones as poll_row does (the witness of a
+// wave is the first pending fragment of its lowest waiting lane).  The block loop is
+// uniform per workgroup; lanes past the row end load out of range (0) and store nothing.
+template <int POL_LD, int POL_ST, int U>
+__device__ __forceinline__ void poll_row_batch(uint8_t *row, u32x4 *out_row, uint32_t row_frags, uint32_t cta,
+                                               uint32_t ctas, int copy, uint64_t spin_limit, int poll_all) {
+  const __amdgpu_buffer_rsrc_t r = make_rsrc(row, row_frags * 16u);
+  for (uint32_t blk = cta * 256u * U; blk < row_frags; blk += ctas * 256u * U) {
+    uint32_t idx[U];
+    u32x4 w[U];
+    uint32_t pend = 0;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      idx[u] = blk + u * 256u + threadIdx.x;
+      w[u] = buf_load<POL_LD>(r, idx[u] < row_frags ? idx[u] * 16u : 0x80000000u);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (idx[u] < row_frags && !published(w[u])) pend |= 1u << u;
+    for (uint64_t polls = 0;; ++polls) {
+      const uint64_t waiting = __ballot(pend != 0);
+      if (waiting == 0) break;
+      if (polls >= spin_limit) {
+        if (pend) atomicOr(&g_status, 1u);
+        break;
+      }
+      if (poll_all) {
+        __builtin_amdgcn_s_sleep(1);
+      } else {
+        uint32_t first = 0;
+#pragma unroll
+        for (int u = U - 1; u >= 0; --u)
+          if ((pend >> u) & 1u) first = idx[u];
+        const uint32_t wi = __shfl(first, __ffsll((unsigned long long)waiting) - 1, 64);
+        if (!published(load_fragment_coherent(reinterpret_cast<const uint32_t *>(row + (size_t)wi * 16u)))) {
+          __builtin_amdgcn_s_sleep(8);
+          continue;
+        }
+      }
+      asm volatile("" ::: "memory");
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+        if ((pend >> u) & 1u) {
+          w[u] = buf_load<POL_LD>(r, idx[u] * 16u);
+          if (published(w[u])) pend &= ~(1u << u);
+        }
+    }
+    if (copy) {
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+        if (idx[u] < row_frags && !((pend >> u) & 1u)) {
+          nt_store(w[u], out_row + idx[u]);
+          buf_store<POL_ST>(sentinel4(), r, idx[u] * 16u);
+        }
+    }
+  }
+}
+
+// gather_poll: grid (ctas, M); workgroup `cta` of row m; U fragments per thread in flight.
+template <int POL_LD, int POL_ST, int U>
 __global__ void __launch_bounds__(256)
 gather_poll_kernel(uint8_t *__restrict__ box, u32x4 *__restrict__ out, uint32_t row_frags,
                    int copy, uint64_t spin_limit, int poll_all) {
   const uint32_t m = blockIdx.y;
-  poll_row<POL_LD, POL_ST>(box + (size_t)m * row_frags * 16u, out + (size_t)m * row_frags, row_frags, blockIdx.x,
-                           gridDim.x, copy, spin_limit, poll_all);
+  if constexpr (U == 1)
+    poll_row<POL_LD, POL_ST>(box + (size_t)m * row_frags * 16u, out + (size_t)m * row_frags, row_frags, blockIdx.x,
+                             gridDim.x, copy, spin_limit, poll_all);
+  else
+    poll_row_batch<POL_LD, POL_ST, U>(box + (size_t)m * row_frags * 16u, out + (size_t)m * row_frags, row_frags,
+                                      blockIdx.x, gridDim.x, copy, spin_limit, poll_all);
 }
 
 // gather_push_poll in one launch, as the pages' Gather kernel pushes its shard and then
@@ -110,7 +175,7 @@ struct GatherStepArgs {
   int poll_all;
 };
 
-template <int TP, int POL_PUSH, int POL_LD, int POL_ST>
+template <int TP, int U, int POL_PUSH, int POL_LD, int POL_ST>
 __global__ void __launch_bounds__(256) gather_push_poll_kernel(GatherStepArgs a) {
   const uint32_t row_frags = TP * a.frags;
   const uint32_t producers = TP * a.M * a.per_row;
@@ -122,8 +187,12 @@ __global__ void __launch_bounds__(256) gather_push_poll_kernel(GatherStepArgs a)
     return;
   }
   const uint32_t c = blockIdx.x - producers, m = c / a.ctas, cta = c - m * a.ctas;
-  poll_row<POL_LD, POL_ST>(a.box + (size_t)m * row_frags * 16u, a.out + (size_t)m * row_frags, row_frags, cta, a.ctas,
-                           a.copy, a.spin_limit, a.poll_all);
+  if constexpr (U == 1)
+    poll_row<POL_LD, POL_ST>(a.box + (size_t)m * row_frags * 16u, a.out + (size_t)m * row_frags, row_frags, cta,
+                             a.ctas, a.copy, a.spin_limit, a.poll_all);
+  else
+    poll_row_batch<POL_LD, POL_ST, U>(a.box + (size_t)m * row_frags * 16u, a.out + (size_t)m * row_frags, row_frags,
+                                      cta, a.ctas, a.copy, a.spin_limit, a.poll_all);
 }
 
 }  // namespace arn

@@ -19,6 +19,8 @@ using arn::u32x4;
 std::atomic<uint64_t> g_spin_limit{uint64_t(1) << 22};
 std::atomic<int> g_reduce_threads{0};
 std::atomic<int> g_reduce_split{0};
+std::atomic<int> g_poll_frags{0};  // Gather polls: fragments per thread in flight, 0 = automatic
+std::atomic<int> g_poll_mode{0};   // Gather polls: 0 = automatic, 1 = re-read all, 2 = witness
 
 // Cache policies (gfx950 cache bits, see device.hpp).  Slot reads, re-arm writes and
 // pushes are device-scope coherent (sc1); the re-arm writes are also non-temporal
@@ -53,6 +55,11 @@ std::atomic<int> g_reduce_split{0};
 #define ARNORM_SPLIT7_MAX_M 64
 #endif
 // arnorm_push_reduce_norm, one-launch form: fragments per producer thread per step.
+// Fragments per thread in flight in a Gather poll whose grid is capped below a thread
+// per fragment.
+#ifndef ARNORM_POLL_U
+#define ARNORM_POLL_U 4
+#endif
 #ifndef ARNORM_STEP_PUSH_U
 #define ARNORM_STEP_PUSH_U 2
 #endif
@@ -191,18 +198,41 @@ int reduce_split(int M, bool have_box) {
   return k;
 }
 
-// Poller workgroups per row: about one fragment per thread, the whole grid resident at
-// once (at most 2048 workgroups of 256 threads over 256 CUs), at least one per row.
+// Poller workgroups per row: about one fragment per thread, at least one per row, and
+// at most 1024 workgroups of 256 threads in all (half of what 256 CUs hold), so the
+// whole grid is resident at once and a producer running beside it still finds room.
 uint32_t poll_ctas(uint32_t row_frags, int M) {
   const uint32_t want = (row_frags + 255) / 256;
-  return std::max(1u, std::min(want, 2048u / (uint32_t)M));
+  return std::max(1u, std::min(want, 1024u / (uint32_t)M));
+}
+
+// The layout of a Gather poll: fragments per thread in flight (1, or ARNORM_POLL_U when
+// the grid cap leaves threads several fragments) and its workgroups per row.
+struct PollLayout {
+  int u;
+  uint32_t ctas;
+};
+PollLayout poll_layout(uint32_t row_frags, int M) {
+  const uint32_t ctas = poll_ctas(row_frags, M);
+  int u = g_poll_frags.load(std::memory_order_relaxed);
+  if (u == 0) u = (uint64_t)ctas * 256u >= row_frags ? 1 : ARNORM_POLL_U;
+  if (u == 1) return {1, ctas};
+  return {u, std::max(1u, std::min((row_frags + 256u * u - 1) / (256u * u), ctas))};
+}
+int poll_mode(int automatic) {
+  const int mode = g_poll_mode.load(std::memory_order_relaxed);
+  return mode == 0 ? automatic : mode == 1 ? 1 : 0;
 }
 
 int launch_poll(uint8_t *box, u32x4 *out, uint32_t row_frags, int M, int copy, hipStream_t stream) {
-  const int poll_all = (uint64_t)M * row_frags * 16u <= ARNORM_POLL_ALL_MAX_BYTES;
-  return launch(arn::gather_poll_kernel<kPolPoll, kPolRearm>, dim3(poll_ctas(row_frags, M), (unsigned)M), dim3(256),
-                stream, box, out, row_frags, copy ? 1 : 0, (uint64_t)g_spin_limit.load(std::memory_order_relaxed),
-                poll_all);
+  const int poll_all = poll_mode((uint64_t)M * row_frags * 16u <= ARNORM_POLL_ALL_MAX_BYTES);
+  const uint64_t spin = g_spin_limit.load(std::memory_order_relaxed);
+  const PollLayout l = poll_layout(row_frags, M);
+  if (l.u == 1)  // a fragment per thread, or a loop over them where the grid is capped
+    return launch(arn::gather_poll_kernel<kPolPoll, kPolRearm, 1>, dim3(l.ctas, (unsigned)M), dim3(256), stream, box,
+                  out, row_frags, copy ? 1 : 0, spin, poll_all);
+  return launch(arn::gather_poll_kernel<kPolPoll, kPolRearm, ARNORM_POLL_U>, dim3(l.ctas, (unsigned)M), dim3(256),
+                stream, box, out, row_frags, copy ? 1 : 0, spin, poll_all);
 }
 
 }  // namespace
@@ -400,20 +430,28 @@ int gather_push_poll(const int32_t *shard, int32_t *mailbox, int32_t *out, int t
   a.frags = frags;
   a.M = (uint32_t)M;
   a.per_row = (frags + 255) / 256;
-  a.ctas = poll_ctas((uint32_t)tp * frags, M);
+  const PollLayout l = poll_layout((uint32_t)tp * frags, M);
+  a.ctas = l.ctas;
   a.copy = copy ? 1 : 0;
   a.spin_limit = g_spin_limit.load(std::memory_order_relaxed);
-  a.poll_all = 1;
+  a.poll_all = poll_mode(1);
   const dim3 grid(tp * M * a.per_row + M * a.ctas);
+#define ARNORM_GATHER_STEP(T)                                                                                      \
+  case T:                                                                                                          \
+    if (l.u == 1) return launch(arn::gather_push_poll_kernel<T, 1, kPolPush, kPolPoll, kPolRearm>, grid, dim3(256), \
+                                stream, a);                                                                        \
+    return launch(arn::gather_push_poll_kernel<T, ARNORM_POLL_U, kPolPush, kPolPoll, kPolRearm>, grid, dim3(256),    \
+                  stream, a);
   switch (tp) {
-    case 2: return launch(arn::gather_push_poll_kernel<2, kPolPush, kPolPoll, kPolRearm>, grid, dim3(256), stream, a);
-    case 3: return launch(arn::gather_push_poll_kernel<3, kPolPush, kPolPoll, kPolRearm>, grid, dim3(256), stream, a);
-    case 4: return launch(arn::gather_push_poll_kernel<4, kPolPush, kPolPoll, kPolRearm>, grid, dim3(256), stream, a);
-    case 5: return launch(arn::gather_push_poll_kernel<5, kPolPush, kPolPoll, kPolRearm>, grid, dim3(256), stream, a);
-    case 6: return launch(arn::gather_push_poll_kernel<6, kPolPush, kPolPoll, kPolRearm>, grid, dim3(256), stream, a);
-    case 7: return launch(arn::gather_push_poll_kernel<7, kPolPush, kPolPoll, kPolRearm>, grid, dim3(256), stream, a);
-    case 8: return launch(arn::gather_push_poll_kernel<8, kPolPush, kPolPoll, kPolRearm>, grid, dim3(256), stream, a);
+    ARNORM_GATHER_STEP(2)
+    ARNORM_GATHER_STEP(3)
+    ARNORM_GATHER_STEP(4)
+    ARNORM_GATHER_STEP(5)
+    ARNORM_GATHER_STEP(6)
+    ARNORM_GATHER_STEP(7)
+    ARNORM_GATHER_STEP(8)
   }
+#undef ARNORM_GATHER_STEP
   return ARNORM_NOT_SERVED;
 }
 
@@ -527,6 +565,14 @@ int arnorm_set_reduce_split(int workgroups_per_row) {
   const int k = workgroups_per_row;
   if (k != 0 && k != 1 && k != 7 && k != 14) return ARNORM_BAD_ARG;
   g_reduce_split.store(k, std::memory_order_relaxed);
+  return ARNORM_OK;
+}
+
+int arnorm_set_poll(int frags_per_thread, int mode) {
+  if (frags_per_thread != 0 && frags_per_thread != 1 && frags_per_thread != ARNORM_POLL_U) return ARNORM_BAD_ARG;
+  if (mode < 0 || mode > 2) return ARNORM_BAD_ARG;
+  g_poll_frags.store(frags_per_thread, std::memory_order_relaxed);
+  g_poll_mode.store(mode, std::memory_order_relaxed);
   return ARNORM_OK;
 }
 
