@@ -303,12 +303,12 @@ def test_gather_poll_layouts_one_launch(lib, name, m, u, mode):
         assert lib.status() == lib.OK
 
 
-@pytest.mark.parametrize("tp,m,s", [(8, 4096, 896), (2, 4096, 4), (4, 1024, 10240)])
+@pytest.mark.parametrize("tp,m,s", [(8, 4096, 896), (2, 4096, 4), (4, 1024, 10240), (2, 70000, 4)])
 def test_gather_large(lib, tp, m, s):
-    """Large gathers with M = cap: up to 168 MB of shards as the pair of launches, and at
-    S=4 one launch of 12288 workgroups; through gather_push_poll with copy, then no copy
-    followed by a copying gather_poll; every word and the whole mailbox compared with the
-    oracle."""
+    """Large gathers with M = cap: up to 168 MB of shards as the pair of launches, at S=4
+    one launch of 12288 workgroups, and M = 70000 rows (more than a grid's second
+    dimension holds); through gather_push_poll with copy, then no copy followed by a
+    copying gather_poll; every word and the whole mailbox compared with the oracle."""
     import dataclasses
 
     import torch

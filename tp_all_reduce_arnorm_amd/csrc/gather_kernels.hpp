@@ -13,20 +13,6 @@
 
 namespace arn {
 
-// gather_push: grid (x, M, nslots); shard row m of slot s is F = S/4 contiguous
-// fragments, written to row m at word offset (rank + s) * S.
-template <int POL>
-__global__ void __launch_bounds__(256)
-gather_push_kernel(const u32x4 *__restrict__ shard, uint8_t *__restrict__ box, uint32_t frags,
-                   uint32_t M, uint32_t row_bytes, uint32_t first_col_bytes) {
-  const uint32_t m = blockIdx.y, s = blockIdx.z;
-  const u32x4 *src = shard + ((size_t)s * M + m) * frags;
-  const __amdgpu_buffer_rsrc_t dst =
-      make_rsrc(box + (size_t)m * row_bytes + first_col_bytes + (size_t)s * frags * 16u, frags * 16u);
-  for (uint32_t i = blockIdx.x * 256u + threadIdx.x; i < frags; i += gridDim.x * 256u)
-    buf_store<POL>(clean4(nt_load(src + i)), dst, i * 16u);
-}
-
 // One producer workgroup's share of a cleaned copy: fragments chunk*256 + t, strided
 // by chunks*256, of `frags` contiguous source fragments into the buffer at dst.
 template <int POL>
@@ -35,6 +21,19 @@ __device__ __forceinline__ void push_frags(const u32x4 *__restrict__ src, uint8_
   const __amdgpu_buffer_rsrc_t r = make_rsrc(dst, frags * 16u);
   for (uint32_t i = chunk * 256u + threadIdx.x; i < frags; i += chunks * 256u)
     buf_store<POL>(clean4(nt_load(src + i)), r, i * 16u);
+}
+
+// gather_push: a 1-D grid of chunks * M * nslots workgroups, id = (s * M + m) * chunks + c;
+// shard row m of slot s is F = S/4 contiguous fragments, written to row m at word offset
+// (rank + s) * S, chunk c taking fragments c*256 + t, strided by chunks*256.
+template <int POL>
+__global__ void __launch_bounds__(256)
+gather_push_kernel(const u32x4 *__restrict__ shard, uint8_t *__restrict__ box, uint32_t frags,
+                   uint32_t M, uint32_t row_bytes, uint32_t first_col_bytes, uint32_t chunks) {
+  const uint32_t sm = blockIdx.x / chunks, c = blockIdx.x - sm * chunks;  // sm = s * M + m
+  const uint32_t s = sm / M, m = sm - s * M;
+  push_frags<POL>(shard + (size_t)sm * frags, box + (size_t)m * row_bytes + first_col_bytes + (size_t)s * frags * 16u,
+                  frags, c, chunks);
 }
 
 // The poll of one row's fragments by workgroup `cta` of `ctas` (cta*256 + t, strided by
@@ -145,18 +144,19 @@ __device__ __forceinline__ void poll_row_batch(uint8_t *row, u32x4 *out_row, uin
   }
 }
 
-// gather_poll: grid (ctas, M); workgroup `cta` of row m; U fragments per thread in flight.
+// gather_poll: a 1-D grid of ctas * M workgroups, id = m * ctas + cta; U fragments per
+// thread in flight.
 template <int POL_LD, int POL_ST, int U>
 __global__ void __launch_bounds__(256)
-gather_poll_kernel(uint8_t *__restrict__ box, u32x4 *__restrict__ out, uint32_t row_frags,
+gather_poll_kernel(uint8_t *__restrict__ box, u32x4 *__restrict__ out, uint32_t row_frags, uint32_t ctas,
                    int copy, uint64_t spin_limit, int poll_all) {
-  const uint32_t m = blockIdx.y;
+  const uint32_t m = blockIdx.x / ctas, cta = blockIdx.x - m * ctas;
   if constexpr (U == 1)
-    poll_row<POL_LD, POL_ST>(box + (size_t)m * row_frags * 16u, out + (size_t)m * row_frags, row_frags, blockIdx.x,
-                             gridDim.x, copy, spin_limit, poll_all);
+    poll_row<POL_LD, POL_ST>(box + (size_t)m * row_frags * 16u, out + (size_t)m * row_frags, row_frags, cta, ctas,
+                             copy, spin_limit, poll_all);
   else
-    poll_row_batch<POL_LD, POL_ST, U>(box + (size_t)m * row_frags * 16u, out + (size_t)m * row_frags, row_frags,
-                                      blockIdx.x, gridDim.x, copy, spin_limit, poll_all);
+    poll_row_batch<POL_LD, POL_ST, U>(box + (size_t)m * row_frags * 16u, out + (size_t)m * row_frags, row_frags, cta,
+                                      ctas, copy, spin_limit, poll_all);
 }
 
 // gather_push_poll in one launch, as the pages' Gather kernel pushes its shard and then

@@ -55,13 +55,13 @@ std::atomic<int> g_poll_mode{0};   // Gather polls: 0 = automatic, 1 = re-read a
 #define ARNORM_SPLIT7_MAX_M 64
 #endif
 // arnorm_push_reduce_norm, one-launch form: fragments per producer thread per step.
+#ifndef ARNORM_STEP_PUSH_U
+#define ARNORM_STEP_PUSH_U 2
+#endif
 // Fragments per thread in flight in a Gather poll whose grid is capped below a thread
 // per fragment.
 #ifndef ARNORM_POLL_U
 #define ARNORM_POLL_U 4
-#endif
-#ifndef ARNORM_STEP_PUSH_U
-#define ARNORM_STEP_PUSH_U 2
 #endif
 // A consumer grid whose TP slots of rows < M total at most this many bytes re-reads all
 // of them on every later poll pass (the data arrives with the news); a larger one
@@ -229,10 +229,10 @@ int launch_poll(uint8_t *box, u32x4 *out, uint32_t row_frags, int M, int copy, h
   const uint64_t spin = g_spin_limit.load(std::memory_order_relaxed);
   const PollLayout l = poll_layout(row_frags, M);
   if (l.u == 1)  // a fragment per thread, or a loop over them where the grid is capped
-    return launch(arn::gather_poll_kernel<kPolPoll, kPolRearm, 1>, dim3(l.ctas, (unsigned)M), dim3(256), stream, box,
-                  out, row_frags, copy ? 1 : 0, spin, poll_all);
-  return launch(arn::gather_poll_kernel<kPolPoll, kPolRearm, ARNORM_POLL_U>, dim3(l.ctas, (unsigned)M), dim3(256),
-                stream, box, out, row_frags, copy ? 1 : 0, spin, poll_all);
+    return launch(arn::gather_poll_kernel<kPolPoll, kPolRearm, 1>, dim3(l.ctas * (unsigned)M), dim3(256), stream,
+                  box, out, row_frags, l.ctas, copy ? 1 : 0, spin, poll_all);
+  return launch(arn::gather_poll_kernel<kPolPoll, kPolRearm, ARNORM_POLL_U>, dim3(l.ctas * (unsigned)M), dim3(256),
+                stream, box, out, row_frags, l.ctas, copy ? 1 : 0, spin, poll_all);
 }
 
 }  // namespace
@@ -393,10 +393,11 @@ int gather_push(const int32_t *shard, int32_t *mailbox, int tp, int cap, int S, 
   if (rank < 0 || nslots < 1 || rank + nslots > tp) return ARNORM_BAD_ARG;
   if (!aligned16(shard) || !aligned16(mailbox)) return ARNORM_BAD_ARG;
   const uint32_t frags = (uint32_t)S / 4;
-  const dim3 grid((frags + 255) / 256, (unsigned)M, (unsigned)nslots);
-  return launch(arn::gather_push_kernel<kPolPush>, grid, dim3(256), stream, reinterpret_cast<const u32x4 *>(shard),
-                reinterpret_cast<uint8_t *>(mailbox), frags, (uint32_t)M, (uint32_t)tp * S * 4u,
-                (uint32_t)rank * S * 4u);
+  const uint32_t chunks = (frags + 255) / 256;
+  if ((uint64_t)chunks * M * nslots >= (uint64_t(1) << 31)) return ARNORM_NOT_SERVED;
+  return launch(arn::gather_push_kernel<kPolPush>, dim3(chunks * (unsigned)M * (unsigned)nslots), dim3(256), stream,
+                reinterpret_cast<const u32x4 *>(shard), reinterpret_cast<uint8_t *>(mailbox), frags, (uint32_t)M,
+                (uint32_t)tp * S * 4u, (uint32_t)rank * S * 4u, chunks);
 }
 
 int gather_poll(int32_t *mailbox, int32_t *out, int tp, int cap, int S, int M, int copy, hipStream_t stream) {
