@@ -125,6 +125,21 @@ def test_push_reduce_norm_checks(L):
     b = list(a)
     b[6] = FAKE + 0x300000  # norm box aliases out
     assert L.arnorm_push_reduce_norm(*b, 2, 8, 64, 0, 4, 1e-6, None) == 2
+    # the two-launch form (M=64, or no norm box) rejects a bad consumer argument before it
+    # launches the push (which would fail here, with no GPU, as HIP_ERROR = 3)
+    for m, box in ((64, FAKE + 0x600000), (4, None)):
+        c = list(a)
+        c[6] = box
+        c[4] = c[3]  # residual_out aliases out
+        assert L.arnorm_push_reduce_norm(*c, 2, 8, 64, 0, m, 1e-6, None) == 2
+        c = list(a)
+        c[6] = box
+        c[2] = MIS  # misaligned gamma
+        assert L.arnorm_push_reduce_norm(*c, 2, 8, 64, 0, m, 1e-6, None) == 2
+        c = list(a)
+        c[6] = box
+        c[3] = c[5]  # out aliases the mailbox
+        assert L.arnorm_push_reduce_norm(*c, 2, 8, 64, 0, m, 1e-6, None) == 2
 
 
 def test_gather_checks(L):

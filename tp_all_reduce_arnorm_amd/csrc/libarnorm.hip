@@ -318,7 +318,18 @@ int arnorm_push_reduce_norm(const uint16_t *partials, const uint16_t *residual, 
                             int tp, int cap, int parity, int M, float eps, hipStream_t stream) {
   int rc = check_box(parities, tp, cap, parity, M);
   if (rc != ARNORM_OK) return rc;
+  // every check of both halves first, so that a call launches all of its work or none
   if (!aligned16(partials) || (residual && !aligned16(residual))) return ARNORM_BAD_ARG;
+  if (!aligned16(gamma) || !aligned16(out) || !aligned16(residual_out) || !aligned16(mailbox)) return ARNORM_BAD_ARG;
+  if (norm_box && !aligned16(norm_box)) return ARNORM_BAD_ARG;
+  const void *outs[3] = {out, residual_out, norm_box};
+  const void *ins[4] = {partials, residual, gamma, mailbox};
+  for (const void *o : outs)
+    for (const void *i : ins)
+      if (o && o == i && !(o == residual_out && i == residual)) return ARNORM_BAD_ARG;
+  if (out == residual_out) return ARNORM_BAD_ARG;
+  if (norm_box && (static_cast<void *>(norm_box) == out || static_cast<void *>(norm_box) == residual_out))
+    return ARNORM_BAD_ARG;
   // One launch only where its consumer may re-read every slot on each poll pass (a small
   // grid): measured at TP=8 it is then faster than the pair (M=4: 4.8 against 5.3 us),
   // while with witness polling (larger M) the pair of launches is faster.  Rows split 7
@@ -332,16 +343,6 @@ int arnorm_push_reduce_norm(const uint16_t *partials, const uint16_t *residual, 
     return arnorm_reduce_norm(nullptr, residual, gamma, out, residual_out, mailbox, norm_box, parities, tp, cap,
                               parity, 0, M, eps, stream);
   }
-  if (!aligned16(gamma) || !aligned16(out) || !aligned16(residual_out) || !aligned16(mailbox) ||
-      !aligned16(norm_box))
-    return ARNORM_BAD_ARG;
-  const void *outs[3] = {out, residual_out, norm_box};
-  const void *ins[4] = {partials, residual, gamma, mailbox};
-  for (const void *o : outs)
-    for (const void *i : ins)
-      if (o == i && !(o == residual_out && i == residual)) return ARNORM_BAD_ARG;
-  if (out == residual_out || static_cast<void *>(norm_box) == out || static_cast<void *>(norm_box) == residual_out)
-    return ARNORM_BAD_ARG;
 
   arn::StepArgs a;
   a.r.partial = nullptr;
