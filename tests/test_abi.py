@@ -120,6 +120,7 @@ def test_push_reduce_norm_checks(L):
          FAKE + 0x600000)
     assert L.arnorm_push_reduce_norm(*a, 2, 1, 64, 0, 4, 1e-6, None) == 1      # tp 1
     assert L.arnorm_push_reduce_norm(*a, 2, 8, 64, 0, 65, 1e-6, None) == 1     # M > cap
+    assert L.arnorm_push_reduce_norm(*a, 2, 8, 64, 0, 0, 1e-6, None) == 1      # M = 0
     assert L.arnorm_push_reduce_norm(*a, 2, 8, 64, 2, 4, 1e-6, None) == 2      # parity
     assert L.arnorm_push_reduce_norm(MIS, *a[1:], 2, 8, 64, 0, 4, 1e-6, None) == 2
     b = list(a)
@@ -158,6 +159,7 @@ def test_gather_push_poll_checks(L):
     assert L.gather_push_poll(FAKE, FAKE + 0x100000, FAKE + 0x200000, 1, 64, 896, 32, 1, None) == 1
     assert L.gather_push_poll(FAKE, FAKE + 0x100000, FAKE + 0x200000, 8, 64, 6, 32, 1, None) == 1
     assert L.gather_push_poll(FAKE, FAKE + 0x100000, FAKE + 0x200000, 8, 64, 896, 65, 1, None) == 1
+    assert L.gather_push_poll(FAKE, FAKE + 0x100000, FAKE + 0x200000, 8, 64, 896, 0, 1, None) == 1
     for m in (4, 32):  # one launch, and the pair
         assert L.gather_push_poll(MIS, FAKE + 0x100000, FAKE + 0x200000, 8, 64, 896, m, 1, None) == 2
         assert L.gather_push_poll(FAKE, FAKE + 0x100000, FAKE + 0x100000, 8, 64, 896, m, 1, None) == 2
@@ -187,6 +189,7 @@ def test_twoshot_push_reduce_read_checks(L):
     assert f(P, R, G, O, 2, 9, 64, 7168, 0, 4, None) == 1    # tp 9
     assert f(P, R, G, O, 2, 8, 64, 7164, 0, 4, None) == 1    # width % 8
     assert f(P, R, G, O, 2, 8, 64, 7168, 0, 65, None) == 1   # M > cap
+    assert f(P, R, G, O, 2, 8, 64, 7168, 0, 0, None) == 1    # M = 0
     assert f(P, R, G, O, 2, 8, 64, 7168, 2, 4, None) == 2    # parity
     for m in (4, 64):  # one launch, and the three launches
         assert f(MIS, R, G, O, 2, 8, 64, 7168, 0, m, None) == 2
