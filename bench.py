@@ -341,6 +341,18 @@ def pmc_workload(lib, torch, launches=3):
     return {"reduce_us": red_us, "push_us": push_us, "copy_bytes": n * 4}
 
 
+def cpu_model():
+    """The host CPU's model name, from /proc/cpuinfo."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown CPU"
+
+
 def cpu_baseline(budget_s=10.0):
     """The oracle (numpy, one thread) on the TP=8, M=4 stand-in call: push of 8 slots +
     poll / re-arm / reduce / norm, fresh partials each call."""
@@ -574,9 +586,11 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         cpu_us, n = cpu_baseline(args.cpu_seconds)
+        call_bytes = push_bytes(8, 4) + reduce_bytes(8, 4, False)
         cpu = {"value": round(cpu_us, 1), "unit": "µs/call", "cores": 1, "kind": "oracle",
                "sample": f"{n} oracle calls (push of 8 slots + reduce_norm) at TP=8, M=4, no residual; "
-                         f"median; {os.cpu_count()} host CPUs visible, numpy on one thread"}
+                         f"median; {os.cpu_count()} host CPUs visible ({cpu_model()}), numpy on one thread",
+               "algorithmic_gbps": round(call_bytes / (cpu_us * 1e-6) / 1e9, 3)}
     us_per_call = elapsed / args.steps * 1e6
     rec = {
         "metric": METRIC,
