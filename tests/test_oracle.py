@@ -157,6 +157,30 @@ def check_allreduce_golden(push_fn, reduce_fn):
         assert np.all(box == S0), f"{name}: mailbox not re-armed"
 
 
+def golden_residual_cases():
+    cases = []
+    for ln in read_golden("residual_words.txt"):
+        name, slots, res, want = [p.strip() for p in ln.split("|")]
+        cases.append((name, [int(x, 16) for x in slots.split(",")], int(res, 16), int(want, 16)))
+    return cases
+
+
+def check_residual_golden(push_fn, reduce_fn):
+    """The all-reduced word rounded, then the residual added and rounded again."""
+    for name, words, res_word, want in golden_residual_cases():
+        tp = len(words)
+        box = np.full((1, tp, 1, W // 2), S0, dtype=np.uint32)
+        partial = np.zeros((tp, 1, W), dtype=np.uint16)
+        for k, w in enumerate(words):
+            partial[k, 0, 0], partial[k, 0, 1] = w & 0xFFFF, w >> 16
+        residual = np.zeros((1, W), dtype=np.uint16)
+        residual[0, 0], residual[0, 1] = res_word & 0xFFFF, res_word >> 16
+        push_fn(box, partial, 0, 0)
+        _, res_out = reduce_fn(box, 0, 1, residual, np.full(W, 0x3F80, dtype=np.uint16), 1e-6)
+        got = int(res_out[0, 0]) | (int(res_out[0, 1]) << 16)
+        assert got == want, f"{name}: got {got:08X}, want {want:08X}"
+
+
 def check_tp2_theorem(allreduce_fn):
     """TP=2: the FP32 sum of two BF16 values rounded to BF16 equals the correctly
     rounded BF16 of the exact sum (double rounding is innocuous: 24 >= 2*8 + 2)."""
@@ -447,6 +471,11 @@ def test_gather():
     check_gather(oga.gather_push, oga.gather_poll)
 
 
+def test_residual_golden():
+    """All-reduce rounded once, residual added and rounded again (hand cases)."""
+    check_residual_golden(oar.arnorm_push, oar.arnorm_reduce_norm)
+
+
 def test_twoshot_golden():
     check_twoshot_golden(ots.twoshot_push, ots.twoshot_reduce)
 
@@ -577,6 +606,21 @@ def _mut_residual_double_round(r, c):
     return _mut_truncate(s.astype(np.float32))
 
 
+def _reduce_residual_one_rounding(box, parity, m, residual, gamma, eps):
+    # the residual added to the unrounded FP32 all-reduce: one rounding instead of two
+    slots = box[parity, :, :m, :]
+    olp.check_published(slots, "mutant")
+    lanes = obf.widen(obf.unpack_pairs(slots.copy()))
+    box[parity, :, :m, :] = S0
+    total = lanes[0].copy()
+    for k in range(1, lanes.shape[0]):
+        total = (total + lanes[k]).astype(np.float32)
+    if residual is not None:
+        total = (total + obf.widen(residual)).astype(np.float32)
+    new_res = obf.round_to_bf16(total)
+    return oar.rms_norm(new_res, gamma, eps), new_res
+
+
 def _with_allreduce(fn):
     def reduce_fn(box, parity, m, residual, gamma, eps):
         slots = box[parity, :, :m, :]
@@ -669,6 +713,8 @@ MUTANTS = {
     "norm over 7167": lambda: check_norm_random_rows(_mut_norm_wrong_width),
     "norm sum in float64 range": lambda: check_norm_fp32_range(_mut_norm_f64_range),
     "residual truncated": lambda: check_residual_add(_mut_residual_double_round),
+    "residual before the all-reduce rounding": lambda: check_residual_golden(oar.arnorm_push,
+                                                                             _reduce_residual_one_rounding),
     "gather keeps rows": lambda: check_gather(oga.gather_push, _gather_poll_no_rearm),
     "gather no clean": lambda: check_gather(_gather_push_no_clean, oga.gather_poll),
 }

@@ -523,3 +523,70 @@ def test_not_served_shapes(lib):
     assert lib.gather_push(torch.zeros((1, 2, 6), dtype=torch.int32, device="cuda"), g, 8, 0) is None
     with pytest.raises(lib.ArnormError):
         lib.arnorm_push(torch.zeros((2, 2, W), dtype=torch.int16, device="cuda"), box, 0, 7)
+
+
+def _golden_rows(fname, with_residual):
+    """The hand cases of a golden file as (name, slot words, residual word or None,
+    expected word)."""
+    from tests.conftest import read_golden
+
+    cases = []
+    for ln in read_golden(fname):
+        parts = [p.strip() for p in ln.split("|")]
+        words = [int(x, 16) for x in parts[1].split(",")]
+        res = int(parts[2], 16) if with_residual else None
+        cases.append((parts[0], words, res, int(parts[-1], 16)))
+    return cases
+
+
+@pytest.mark.parametrize("one_launch", [False, True])
+def test_golden_words_on_gpu(lib, one_launch):
+    """The hand cases under tests/golden, whose expected words are derived from the pages
+    and not from the oracle, through the HIP path: each slot word (and residual word) in
+    the first two columns of an otherwise zero row; the new residual's first word, or the
+    two-shot output's, must be the expected word, with every mailbox re-armed.  As the
+    push + consumer pair, or as one launch per call."""
+    say(f"[parity] golden words on the GPU one_launch={one_launch}")
+    cases = [(n, w, None, e) for n, w, _, e in _golden_rows("allreduce_words.txt", False)]
+    cases += _golden_rows("residual_words.txt", True)
+    for name, words, res_word, want in cases:
+        tp = len(words)
+        partial = np.zeros((tp, 1, W), dtype=np.uint16)
+        for k, w in enumerate(words):
+            partial[k, 0, 0], partial[k, 0, 1] = w & 0xFFFF, w >> 16
+        res_d = None
+        if res_word is not None:
+            residual = np.zeros((1, W), dtype=np.uint16)
+            residual[0, 0], residual[0, 1] = res_word & 0xFFFF, res_word >> 16
+            res_d = dev16(residual)
+        box = armed_box((1, tp, 1, W // 2))
+        nbox = armed_box((1, 1, 256))
+        g_d = dev16(np.full(W, 0x3F80, dtype=np.uint16))
+        out_d, rout_d = empty16((1, W)), empty16((1, W))
+        if one_launch:
+            assert lib.arnorm_push_reduce_norm(dev16(partial), res_d, g_d, box, 0, EPS, out_d, rout_d,
+                                               norm_box=nbox) is True
+        else:
+            assert lib.arnorm_push(dev16(partial), box, 0, 0) is True
+            assert lib.arnorm_reduce_norm(res_d, g_d, box, 0, EPS, out_d, rout_d) is True
+        assert lib.status() == lib.OK
+        got = host32(rout_d)[0, 0]
+        assert got == want, f"{name}: new residual word {got:08X}, want {want:08X}"
+        assert np.all(host32(box) == S0) and np.all(host32(nbox) == S0), f"{name}: not re-armed"
+    for name, words, _, want in _golden_rows("twoshot_words.txt", False):
+        tp, width = len(words), 8
+        partial = np.zeros((tp, 1, width), dtype=np.uint16)
+        for k, w in enumerate(words):
+            partial[k, 0, 0], partial[k, 0, 1] = w & 0xFFFF, w >> 16
+        recv, gath = armed_box((1, tp, 1, width // 2)), armed_box((1, 1, 1, width // 2))
+        out_d = empty16((1, width))
+        if one_launch:
+            assert lib.twoshot_push_reduce_read(dev16(partial), recv, gath, 0, out_d) is True
+        else:
+            assert lib.twoshot_push(dev16(partial), recv, 0, 0) is True
+            assert lib.twoshot_reduce(recv, gath, 0, 1) is True
+            assert lib.twoshot_read(gath, 0, out_d) is True
+        assert lib.status() == lib.OK
+        got = host32(out_d)[0, 0]
+        assert got == want, f"two-shot {name}: word {got:08X}, want {want:08X}"
+        assert np.all(host32(recv) == S0) and np.all(host32(gath) == S0), f"two-shot {name}: not re-armed"
