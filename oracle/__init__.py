@@ -21,15 +21,17 @@ Pins (what the oracle is checked against, in ``tests/test_oracle.py``):
   * round_to_bf16    -- torch's CPU float->bfloat16 cast and exact Fraction rounding
   * rank-order sum   -- TP=2 double-rounding theorem (exact Fraction sum), exact-prefix
                         TP=8 cases, the rank-vs-tree hand case, signed-zero hand cases
-  * residual add     -- exact Fraction sum rounded once
+  * residual add     -- exact Fraction sum rounded once; hand cases of the all-reduce
+                        rounded before the residual is added (tests/golden/residual_words.txt)
   * RMSNorm          -- closed forms (zero row, one-hot row, constant row, eps-dominated
-                        row) and a 50-digit decimal reference on random rows
+                        row, a row past the FP32 range) and a 60-digit decimal reference
+                        on random rows
   * mailbox protocol -- arm / push / poll / re-arm invariants, parity reuse
   * gather           -- hand case, byte movement, state after copy / no-copy
   * two-shot         -- the no-negative-zero hand cases (tests/golden/twoshot_words.txt),
                         the TP=2 theorem with -0 mapped to +0, and its protocol
-Parity unpinned: the reference kernel's exact sum-of-squares bit pattern (its tree
-order is not something the oracle reproduces); ``out`` is pinned to 1 BF16 ulp.
+Parity unpinned: the pages' kernel's exact sum-of-squares bit pattern (its tree order
+is not something the oracle reproduces); ``out`` is pinned to 1 BF16 ulp.
 """
 
 from .bf16 import (  # noqa: F401
