@@ -91,7 +91,7 @@ constexpr int reduce_occupancy(int nt) {
 // workgroup writes its part into slot k of every peer's inbox, polls its own inbox,
 // adds the K parts in workgroup order and re-arms its inbox.  A part is a sum of FMA
 // products started from +0, so it is never -0, the sentinel word.
-template <int TP, bool RES, bool FUSED, int NT, int K, int POL_LD, int POL_ST, int POL_IO>
+template <int TP, bool RES, bool FUSED, int NT, int K, int POL_LD, int POL_ST, int POL_IN, int POL_IO>
 __device__ __forceinline__ void reduce_row(const ReduceArgs &a, const uint32_t row, const uint32_t k) {
   constexpr int NF = K > 1 ? 1 : (kRowFrags + NT - 1) / NT;  // fragments per thread
   constexpr int NW = NT / 64;
@@ -125,11 +125,11 @@ __device__ __forceinline__ void reduce_row(const ReduceArgs &a, const uint32_t r
   for (int f = 0; f < NF; ++f) g[f] = buf_load<kPolPlain>(gam, off[f]);
   if constexpr (RES) {
 #pragma unroll
-    for (int f = 0; f < NF; ++f) res[f] = buf_load<POL_IO>(resr, off[f]);
+    for (int f = 0; f < NF; ++f) res[f] = buf_load<POL_IN>(resr, off[f]);
   }
   if constexpr (FUSED) {
 #pragma unroll
-    for (int f = 0; f < NF; ++f) mine[f] = buf_load<POL_IO>(part, off[f]);
+    for (int f = 0; f < NF; ++f) mine[f] = buf_load<POL_IN>(part, off[f]);
   }
 #pragma unroll
   for (int s = 0; s < TP; ++s)
@@ -285,9 +285,9 @@ __device__ __forceinline__ void reduce_row(const ReduceArgs &a, const uint32_t r
 // The grid lists a row's K workgroups next to each other (id = row * K + k): with
 // workgroups dispatched in id order, the lowest unfinished row always has all of its
 // workgroups dispatched (every lower id has finished), so the exchange cannot deadlock.
-template <int TP, bool RES, bool FUSED, int NT, int K, int POL_LD, int POL_ST, int POL_IO>
+template <int TP, bool RES, bool FUSED, int NT, int K, int POL_LD, int POL_ST, int POL_IN, int POL_IO>
 __global__ void __launch_bounds__(NT, reduce_occupancy(NT)) reduce_norm_kernel(ReduceArgs a) {
-  reduce_row<TP, RES, FUSED, NT, K, POL_LD, POL_ST, POL_IO>(a, blockIdx.x / K, blockIdx.x % K);
+  reduce_row<TP, RES, FUSED, NT, K, POL_LD, POL_ST, POL_IN, POL_IO>(a, blockIdx.x / K, blockIdx.x % K);
 }
 
 // ---------------------------------------------------------------------------------
@@ -305,7 +305,7 @@ struct StepArgs {
   uint32_t per_slot;      // producer workgroups per slot
 };
 
-template <int TP, bool RES, int K, int U, int POL_PUSH, int POL_LD, int POL_ST, int POL_IO>
+template <int TP, bool RES, int K, int U, int POL_PUSH, int POL_LD, int POL_ST, int POL_IN, int POL_IO>
 __global__ void __launch_bounds__(kRowFrags / K) push_reduce_kernel(StepArgs a) {
   constexpr int NT = kRowFrags / K;
   const uint32_t producers = TP * a.per_slot;
@@ -329,7 +329,7 @@ __global__ void __launch_bounds__(kRowFrags / K) push_reduce_kernel(StepArgs a) 
     return;
   }
   const uint32_t c = blockIdx.x - producers;
-  reduce_row<TP, RES, false, NT, K, POL_LD, POL_ST, POL_IO>(a.r, c / K, c % K);
+  reduce_row<TP, RES, false, NT, K, POL_LD, POL_ST, POL_IN, POL_IO>(a.r, c / K, c % K);
 }
 
 }  // namespace arn

@@ -25,7 +25,9 @@ std::atomic<int> g_poll_mode{0};   // Gather polls: 0 = automatic, 1 = re-read a
 // Cache policies (gfx950 cache bits, see device.hpp).  Slot reads, re-arm writes and
 // pushes are device-scope coherent (sc1); the re-arm writes are also non-temporal
 // (nothing reads the sentinel back until the next push of that parity overwrites it);
-// the caller's rows use the default policy.  Measured on MI355X at TP=8, M=4096: the
+// the residual (and the own partial of the fused form), read once, is non-temporal
+// (TP=8, M=4096: 84 against 83.4 % of 8 TB/s right after the push, 75.2 against 74.3 %
+// from HBM); the output rows use the default policy.  Measured on MI355X at TP=8, M=4096: the
 // non-temporal re-arm took the consumer from 201 to 169 us, while a non-temporal slot
 // read slowed it (183 us) and a non-temporal push slowed the small-M calls.  The
 // macros let a build measure other choices.
@@ -37,6 +39,9 @@ std::atomic<int> g_poll_mode{0};   // Gather polls: 0 = automatic, 1 = re-read a
 #endif
 #ifndef ARNORM_POL_PUSH
 #define ARNORM_POL_PUSH 16
+#endif
+#ifndef ARNORM_POL_IN
+#define ARNORM_POL_IN 2
 #endif
 #ifndef ARNORM_POL_IO
 #define ARNORM_POL_IO 0
@@ -86,7 +91,8 @@ std::atomic<int> g_poll_mode{0};   // Gather polls: 0 = automatic, 1 = re-read a
 constexpr int kPolPoll = ARNORM_POL_POLL;
 constexpr int kPolRearm = ARNORM_POL_REARM;
 constexpr int kPolPush = ARNORM_POL_PUSH;
-constexpr int kPolIO = ARNORM_POL_IO;  // the caller's rows (partial, residual, outputs)
+constexpr int kPolIn = ARNORM_POL_IN;  // the caller's rows read once (residual, own partial)
+constexpr int kPolIO = ARNORM_POL_IO;  // the caller's output rows
 
 bool aligned16(const void *p) { return p != nullptr && (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -143,14 +149,14 @@ uint8_t *parity_base(int32_t *mailbox, int parity, int tp, int cap) {
 
 template <int TP, bool RES, bool FUSED, int NT>
 int launch_reduce(const arn::ReduceArgs &a, int M, hipStream_t stream) {
-  return launch(arn::reduce_norm_kernel<TP, RES, FUSED, NT, 1, kPolPoll, kPolRearm, kPolIO>, dim3(M), dim3(NT), stream,
+  return launch(arn::reduce_norm_kernel<TP, RES, FUSED, NT, 1, kPolPoll, kPolRearm, kPolIn, kPolIO>, dim3(M), dim3(NT), stream,
                 a);
 }
 
 template <int TP, bool RES, bool FUSED, int K>
 int launch_reduce_split(const arn::ReduceArgs &a, int M, hipStream_t stream) {
   constexpr int NT = arn::kRowFrags / K;
-  return launch(arn::reduce_norm_kernel<TP, RES, FUSED, NT, K, kPolPoll, kPolRearm, kPolIO>, dim3(M * K), dim3(NT),
+  return launch(arn::reduce_norm_kernel<TP, RES, FUSED, NT, K, kPolPoll, kPolRearm, kPolIn, kPolIO>, dim3(M * K), dim3(NT),
                 stream, a);
 }
 
@@ -365,9 +371,9 @@ int arnorm_push_reduce_norm(const uint16_t *partials, const uint16_t *residual, 
   const dim3 grid(tp * a.per_slot + M * K);
   const bool res = residual != nullptr;
 #define ARNORM_STEP_LAUNCH_K(TPV, KV)                                                                              \
-  return res ? launch(arn::push_reduce_kernel<TPV, true, KV, U, kPolPush, kPolPoll, kPolRearm, kPolIO>, grid,     \
+  return res ? launch(arn::push_reduce_kernel<TPV, true, KV, U, kPolPush, kPolPoll, kPolRearm, kPolIn, kPolIO>, grid,     \
                       dim3(nt), stream, a)                                                                         \
-             : launch(arn::push_reduce_kernel<TPV, false, KV, U, kPolPush, kPolPoll, kPolRearm, kPolIO>, grid,    \
+             : launch(arn::push_reduce_kernel<TPV, false, KV, U, kPolPush, kPolPoll, kPolRearm, kPolIn, kPolIO>, grid,    \
                       dim3(nt), stream, a);
 #define ARNORM_STEP_LAUNCH(TPV)                                                                                   \
   case TPV:                                                                                                      \
