@@ -380,18 +380,18 @@ def cpu_baseline(budget_s=10.0):
 # -- rocprofv3 summaries (run on the CSVs a profiled run wrote) ----------------------
 
 PROFILE_COMMANDS = {
-    "lat": "rocprofv3 --kernel-trace --stats -f csv -d gpurun_out/prof_lat -o lat -- "
-           "python bench.py --mode latency --steps 2000 > gpurun_out/prof_lat.log 2>&1",
-    "roof": "rocprofv3 --kernel-trace --stats -f csv -d gpurun_out/prof_roof -o roof -- "
-            "python bench.py --mode roofline > gpurun_out/prof_roof.log 2>&1",
-    "gather": "rocprofv3 --kernel-trace --stats -f csv -d gpurun_out/prof_gather -o gather -- "
-              "python bench.py --mode gather > gpurun_out/prof_gather.log 2>&1",
-    "twoshot": "rocprofv3 --kernel-trace --stats -f csv -d gpurun_out/prof_twoshot -o twoshot -- "
-               "python bench.py --mode twoshot > gpurun_out/prof_twoshot.log 2>&1",
-    "fetch": "rocprofv3 --pmc FETCH_SIZE -f csv -d gpurun_out/pmc_fetch -o fetch -- "
-             "python bench.py --mode pmc > gpurun_out/pmc_fetch.log 2>&1",
-    "write": "rocprofv3 --pmc WRITE_SIZE -f csv -d gpurun_out/pmc_write -o write -- "
-             "python bench.py --mode pmc > gpurun_out/pmc_write.log 2>&1",
+    "lat": "rocprofv3 --kernel-trace --stats -f csv -d prof_out/prof_lat -o lat -- "
+           "python bench.py --mode latency --steps 2000 > prof_out/prof_lat.log 2>&1",
+    "roof": "rocprofv3 --kernel-trace --stats -f csv -d prof_out/prof_roof -o roof -- "
+            "python bench.py --mode roofline > prof_out/prof_roof.log 2>&1",
+    "gather": "rocprofv3 --kernel-trace --stats -f csv -d prof_out/prof_gather -o gather -- "
+              "python bench.py --mode gather > prof_out/prof_gather.log 2>&1",
+    "twoshot": "rocprofv3 --kernel-trace --stats -f csv -d prof_out/prof_twoshot -o twoshot -- "
+               "python bench.py --mode twoshot > prof_out/prof_twoshot.log 2>&1",
+    "fetch": "rocprofv3 --pmc FETCH_SIZE -f csv -d prof_out/pmc_fetch -o fetch -- "
+             "python bench.py --mode pmc > prof_out/pmc_fetch.log 2>&1",
+    "write": "rocprofv3 --pmc WRITE_SIZE -f csv -d prof_out/pmc_write -o write -- "
+             "python bench.py --mode pmc > prof_out/pmc_write.log 2>&1",
 }
 
 
