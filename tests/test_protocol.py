@@ -74,12 +74,15 @@ def test_gather_missing_push_times_out(lib, small_spin):
     assert_bits_equal(host32(gbox_d), gbox_h, "gather mailbox")
 
 
-def test_graph_replay_alternating_parities(lib):
-    """push + reduce_norm for parity 0, then parity 1, captured once and replayed; every
-    replay (with eager work and synchronizations in between) matches the oracle."""
+@pytest.mark.parametrize("form", ["pair", "one_call", "one_call_split14"])
+def test_graph_replay_alternating_parities(lib, form):
+    """push + reduce_norm (or the one-launch call, rows split 7 or 14 ways through a norm
+    box) for parity 0, then parity 1, captured once and replayed; every replay (with eager
+    work and synchronizations in between) matches the oracle."""
     import torch
 
-    say("[protocol] HIP graph replay, c2 shape")
+    say(f"[protocol] HIP graph replay, c2 shape, {form}")
+    lib.set_reduce_split(14 if form == "one_call_split14" else 0)
     cfg = wl.CONFIGS["c2"]
     src = wl.ArNormInputs(cfg)
     shape = (2, 8, 64, W // 2)
@@ -90,10 +93,17 @@ def test_graph_replay_alternating_parities(lib):
     outs = [(empty16((4, W)), empty16((4, W))) for _ in range(2)]
     torch.cuda.synchronize()
     graph = torch.cuda.CUDAGraph()
+    nbox = armed_box((2, 64, 256))
     with torch.cuda.graph(graph):
         for parity, p_d in ((0, p0_d), (1, p1_d)):
-            assert lib.arnorm_push(p_d, box_d, parity, 0) is True
-            assert lib.arnorm_reduce_norm(None, g_d, box_d, parity, EPS, outs[parity][0], outs[parity][1]) is True
+            if form == "pair":
+                assert lib.arnorm_push(p_d, box_d, parity, 0) is True
+                assert lib.arnorm_reduce_norm(None, g_d, box_d, parity, EPS, outs[parity][0],
+                                              outs[parity][1]) is True
+            else:
+                assert lib.arnorm_push_reduce_norm(p_d, None, g_d, box_d, parity, EPS, outs[parity][0],
+                                                   outs[parity][1], norm_box=nbox) is True
+    lib.set_reduce_split(0)
     box_h = oracle.arm(np.empty(shape, dtype=np.uint32))
     wants = []
     for parity, p in ((0, p0), (1, p1)):
@@ -110,6 +120,7 @@ def test_graph_replay_alternating_parities(lib):
             assert_bits_equal(host16(outs[parity][1]), wants[parity][1], f"replay {replay} residual_out")
             assert_out_close(host16(outs[parity][0]), wants[parity][0], f"replay {replay} out")
         assert_bits_equal(host32(box_d), box_h, f"replay {replay} mailbox")
+        assert np.all(host32(nbox) == 0x80000000), f"replay {replay} norm box"
         _ = torch.ones(1024, device="cuda").sum().item()  # eager work between replays
     assert lib.status() == lib.OK
 
