@@ -4,9 +4,11 @@
 // kernel), in the one-GPU stand-in of the two-shot page (owners = 1: TP local slots
 // of one mailbox play the ranks).  The pages' design (one 8-CTA cluster per row,
 // 112 threads of 8 columns, sums of squares exchanged through distributed shared
-// memory, a multicast push) is NVIDIA prior art; here one workgroup owns a whole row,
-// so the row's sum of squares never leaves the CU: per-thread FMA chains, a wave64
-// butterfly, and the wave sums added through LDS in wave order.
+// memory, a multicast push) is NVIDIA prior art.  Here one workgroup owns a whole row,
+// so the row's sum of squares never leaves the CU (per-thread FMA chains, a wave64
+// butterfly, the wave sums added through LDS in wave order); at small M a row may
+// instead be split over 7 or 14 workgroups, which exchange their parts through a
+// sentinel-armed norm box, itself a small Lamport mailbox (reduce_row, K > 1).
 #pragma once
 
 #include "device.hpp"
