@@ -84,6 +84,14 @@ def _stream(stream):
     return ctypes.c_void_p(stream.cuda_stream)
 
 
+def _shape(t, shape, what):
+    """Raise ValueError unless tensor t has this shape: the kernels index the caller's
+    buffers by the sizes passed, so a short buffer would be read or written past its
+    end."""
+    if t is None or tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{what} must have shape {tuple(shape)}, got {None if t is None else tuple(t.shape)}")
+
+
 def _ptr(t, nbytes_per_elem=None, what="tensor"):
     if t is None:
         return None
@@ -106,7 +114,8 @@ def arnorm_push(partial, mailbox, parity, rank, stream=None):
     if width != HIDDEN:
         return None
     p, tp, cap, words = mailbox.shape
-    assert words == ROW_WORDS
+    if words != ROW_WORDS:
+        raise ValueError(f"mailbox rows must be {ROW_WORDS} words, got {words}")
     return _check("arnorm_push", LIB.arnorm_push(
         _ptr(partial, 2, "partial"), _ptr(mailbox, 4, "mailbox"), p, tp, cap, parity, rank, nslots, m,
         _stream(stream)))
@@ -122,9 +131,16 @@ def arnorm_reduce_norm(residual, gamma, mailbox, parity, eps, out, residual_out,
     if width != HIDDEN:
         return None
     p, tp, cap, words = mailbox.shape
-    assert words == ROW_WORDS
+    if words != ROW_WORDS:
+        raise ValueError(f"mailbox rows must be {ROW_WORDS} words, got {words}")
+    _shape(residual_out, (m, HIDDEN), "residual_out")
+    _shape(gamma, (HIDDEN,), "gamma")
+    if residual is not None:
+        _shape(residual, (m, HIDDEN), "residual")
+    if partial is not None:
+        _shape(partial, (m, HIDDEN), "partial")
     if norm_box is not None:
-        assert tuple(norm_box.shape) == (p, cap, NORM_BOX_ROW_WORDS)
+        _shape(norm_box, (p, cap, NORM_BOX_ROW_WORDS), "norm_box")
     return _check("arnorm_reduce_norm", LIB.arnorm_reduce_norm(
         _ptr(partial, 2, "partial"), _ptr(residual, 2, "residual"), _ptr(gamma, 2, "gamma"),
         _ptr(out, 2, "out"), _ptr(residual_out, 2, "residual_out"), _ptr(mailbox, 4, "mailbox"),
@@ -139,9 +155,17 @@ def arnorm_push_reduce_norm(partials, residual, gamma, mailbox, parity, eps, out
     if width != HIDDEN:
         return None
     p, tp, cap, words = mailbox.shape
-    assert words == ROW_WORDS and tp_ == tp and tuple(out.shape) == (m, HIDDEN)
+    if words != ROW_WORDS:
+        raise ValueError(f"mailbox rows must be {ROW_WORDS} words, got {words}")
+    if tp_ != tp:
+        raise ValueError(f"partials hold {tp_} ranks, the mailbox {tp} slots")
+    _shape(out, (m, HIDDEN), "out")
+    _shape(residual_out, (m, HIDDEN), "residual_out")
+    _shape(gamma, (HIDDEN,), "gamma")
+    if residual is not None:
+        _shape(residual, (m, HIDDEN), "residual")
     if norm_box is not None:
-        assert tuple(norm_box.shape) == (p, cap, NORM_BOX_ROW_WORDS)
+        _shape(norm_box, (p, cap, NORM_BOX_ROW_WORDS), "norm_box")
     return _check("arnorm_push_reduce_norm", LIB.arnorm_push_reduce_norm(
         _ptr(partials, 2, "partials"), _ptr(residual, 2, "residual"), _ptr(gamma, 2, "gamma"),
         _ptr(out, 2, "out"), _ptr(residual_out, 2, "residual_out"), _ptr(mailbox, 4, "mailbox"),
@@ -152,7 +176,8 @@ def gather_push(shard, mailbox, tp, rank, stream=None):
     """shard: int32 [nslots, M, S]; mailbox: int32 [cap, tp*S]."""
     nslots, m, s = shard.shape
     cap, width = mailbox.shape
-    assert width == tp * s
+    if width != tp * s:
+        raise ValueError(f"mailbox rows must be tp*S = {tp * s} words, got {width}")
     return _check("gather_push", LIB.gather_push(
         _ptr(shard, 4, "shard"), _ptr(mailbox, 4, "mailbox"), tp, cap, s, rank, nslots, m, _stream(stream)))
 
@@ -161,7 +186,11 @@ def gather_poll(mailbox, tp, m, out=None, copy=True, stream=None):
     """Poll rows < m of mailbox (int32 [cap, tp*S]); copy: into out (int32 [m, tp*S])
     and re-arm; no copy: leave the published rows in place."""
     cap, width = mailbox.shape
+    if tp < 1 or width % tp:
+        raise ValueError(f"mailbox rows of {width} words do not split over tp = {tp}")
     s = width // tp
+    if copy:
+        _shape(out, (m, width), "out")
     return _check("gather_poll", LIB.gather_poll(
         _ptr(mailbox, 4, "mailbox"), _ptr(out, 4, "out") if copy else None, tp, cap, s, m, 1 if copy else 0,
         _stream(stream)))
@@ -173,7 +202,10 @@ def gather_push_poll(shard, mailbox, out=None, copy=True, stream=None):
     small calls."""
     tp, m, s = shard.shape
     cap, width = mailbox.shape
-    assert width == tp * s
+    if width != tp * s:
+        raise ValueError(f"mailbox rows must be tp*S = {tp * s} words, got {width}")
+    if copy:
+        _shape(out, (m, width), "out")
     return _check("gather_push_poll", LIB.gather_push_poll(
         _ptr(shard, 4, "shard"), _ptr(mailbox, 4, "mailbox"), _ptr(out, 4, "out") if copy else None, tp, cap, s, m,
         1 if copy else 0, _stream(stream)))
@@ -183,7 +215,8 @@ def twoshot_push(partial, recv, parity, rank, stream=None):
     """partial: BF16 [nslots, M, width]; recv: int32 [parities, tp, cap, width/2]."""
     nslots, m, width = partial.shape
     p, tp, cap, words = recv.shape
-    assert words * 2 == width
+    if words * 2 != width:
+        raise ValueError(f"recv rows of {words} words do not hold {width} BF16 columns")
     return _check("twoshot_push", LIB.twoshot_push(
         _ptr(partial, 2, "partial"), _ptr(recv, 4, "recv"), p, tp, cap, width, parity, rank, nslots, m,
         _stream(stream)))
@@ -193,16 +226,17 @@ def twoshot_reduce(recv, gather, parity, m, stream=None):
     """The owner's reduce of rows < m: recv int32 [parities, tp, cap, width/2] into the
     gather row int32 [parities, 1, cap, width/2]."""
     p, tp, cap, words = recv.shape
-    assert tuple(gather.shape) == (p, 1, cap, words)
+    _shape(gather, (p, 1, cap, words), "gather")
     return _check("twoshot_reduce", LIB.twoshot_reduce(
         _ptr(recv, 4, "recv"), _ptr(gather, 4, "gather"), p, tp, cap, 2 * words, parity, m, _stream(stream)))
 
 
 def twoshot_read(gather, parity, out, stream=None):
     """A reader of the gather row: rows < M (M = out.shape[0]) into out (BF16 [M, width])."""
-    p, _, cap, words = gather.shape
+    p, one, cap, words = gather.shape
     m, width = out.shape
-    assert width == 2 * words
+    if one != 1 or width != 2 * words:
+        raise ValueError(f"gather must be [parities, 1, cap, width/2] for out [M, {width}]")
     return _check("twoshot_read", LIB.twoshot_read(
         _ptr(gather, 4, "gather"), _ptr(out, 2, "out"), p, cap, width, parity, m, _stream(stream)))
 
@@ -213,8 +247,10 @@ def twoshot_push_reduce_read(partial, recv, gather, parity, out, stream=None):
     launch for small calls."""
     tp, m, width = partial.shape
     p, tp2, cap, words = recv.shape
-    assert tp2 == tp and words * 2 == width and tuple(gather.shape) == (p, 1, cap, words)
-    assert tuple(out.shape) == (m, width)
+    if tp2 != tp or words * 2 != width:
+        raise ValueError(f"recv must be [parities, {tp}, cap, {width // 2}], got {tuple(recv.shape)}")
+    _shape(gather, (p, 1, cap, words), "gather")
+    _shape(out, (m, width), "out")
     return _check("twoshot_push_reduce_read", LIB.twoshot_push_reduce_read(
         _ptr(partial, 2, "partial"), _ptr(recv, 4, "recv"), _ptr(gather, 4, "gather"), _ptr(out, 2, "out"), p, tp,
         cap, width, parity, m, _stream(stream)))
