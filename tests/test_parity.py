@@ -366,6 +366,45 @@ def test_c5_full_size_sampled_rows(lib):
     assert np.array_equal(r2, want_res) and np.array_equal(o2, want_out)
 
 
+def test_max_rows_2gib_slot_block(lib):
+    """The largest M served at TP=8: 149,796 rows, a slot block of 2,147,475,456 bytes, just
+    under the 2 GiB a buffer resource spans (17 GB of mailbox).  Inputs are drawn on the
+    device (seeded); the whole mailbox must be re-armed, and sampled rows, the first and
+    last included, must match the oracle."""
+    import torch
+
+    tp, m = 8, (2**31 - 1) // (W * 2)
+    assert m * W * 2 < 2**31 <= (m + 1) * W * 2
+    free, _ = torch.cuda.mem_get_info()
+    if free < 64 * 2**30:
+        pytest.skip("needs about 45 GB of free device memory")
+    say(f"[parity] max rows M={m}")
+    gen = torch.Generator(device="cuda").manual_seed(2024)
+    parts = torch.empty((tp, m, W), dtype=torch.bfloat16, device="cuda")
+    for s in range(tp):
+        parts[s] = torch.randn((m, W), generator=gen, device="cuda").to(torch.bfloat16)
+    resid = torch.randn((m, W), generator=gen, device="cuda").to(torch.bfloat16)
+    gamma = (1 + 0.1 * torch.randn(W, generator=gen, device="cuda")).to(torch.bfloat16)
+    box_d = armed_box((1, tp, m, W // 2))
+    out_d, rout_d = empty16((m, W)), empty16((m, W))
+    assert lib.arnorm_push(parts, box_d, 0, 0) is True
+    assert lib.arnorm_reduce_norm(resid, gamma, box_d, 0, EPS, out_d, rout_d) is True
+    assert lib.status() == lib.OK
+    assert bool((box_d == torch.tensor(-(1 << 31), dtype=torch.int32, device="cuda")).all())
+    rng = np.random.default_rng(123)
+    rows = np.unique(np.concatenate([[0, 1, m // 2, m - 2, m - 1], rng.choice(m, 59, replace=False)]))
+    idx = torch.from_numpy(rows).cuda()
+    p = host16(parts.view(torch.int16).index_select(1, idx))
+    r = host16(resid.view(torch.int16).index_select(0, idx))
+    g = host16(gamma.view(torch.int16))
+    del parts, resid
+    box_h = oracle.arm(np.empty((1, tp, len(rows), W // 2), dtype=np.uint32))
+    oracle.arnorm_push(box_h, p, 0, 0)
+    want_out, want_res = oracle.arnorm_reduce_norm(box_h, 0, len(rows), r, g, EPS)
+    assert_bits_equal(host16(rout_d.index_select(0, idx)), want_res, "residual_out (sampled rows)")
+    assert_out_close(host16(out_d.index_select(0, idx)), want_out, "out (sampled rows)")
+
+
 # -- edge cases ------------------------------------------------------------------
 
 
