@@ -107,4 +107,29 @@ __device__ inline float wave_sum(float v) {
   return v;
 }
 
+// A lane's value read by every lane (v_readlane_b32), bit for bit.
+__device__ inline float lane_f32(float v, int lane) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
+}
+
+// DPP move of v within rows of 16 lanes; CTRL is the gfx9 DPP control word.
+template <int CTRL>
+__device__ inline float dpp_f32(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+// The same sum with DPP moves instead of LDS-pipe shuffles: the 16 lanes of a row
+// exchange across quads (quad_perm [1,0,3,2] and [2,3,0,1]), half rows (row_half_mirror)
+// and rows (row_mirror), each step adding a commutative pair, so every lane of a row
+// holds that row's sum; the four row sums are then read out and added in row order.
+// Fewer cycles than the butterfly (its LDS-pipe shuffles, each a round trip, become
+// VALU moves), which matters where a row's sum sits on a chain of dependent steps.
+__device__ inline float wave_sum_dpp(float v) {
+  v = v + dpp_f32<0xB1>(v);   // quad_perm [1,0,3,2]
+  v = v + dpp_f32<0x4E>(v);   // quad_perm [2,3,0,1]
+  v = v + dpp_f32<0x141>(v);  // row_half_mirror
+  v = v + dpp_f32<0x140>(v);  // row_mirror
+  return (lane_f32(v, 0) + lane_f32(v, 16)) + (lane_f32(v, 32) + lane_f32(v, 48));
+}
+
 }  // namespace arn
