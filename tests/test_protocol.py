@@ -221,3 +221,93 @@ def test_concurrent_gather_consumer_first(lib, side_streams, frags_per_thread):
     finally:
         lib.set_spin_limit(old)
         lib.set_poll(0, 0)
+
+
+def test_three_host_threads_three_mailboxes(lib, side_streams):
+    """Host threads calling the library at once, each on its own stream and mailbox: 24
+    one-launch ArNorm calls (TP=8, M=4, rows split through a norm box), 24 one-launch
+    Gathers (TP=8, M=4, S=896) and 24 one-launch two-shot calls (TP=8, M=4), all in flight
+    together.  Every call's output and the final mailboxes must match the oracle."""
+    import threading
+
+    import torch
+
+    say("[protocol] three host threads, three streams, three mailboxes")
+    calls, tp, m, cap, s = 24, 8, 4, 64, 896
+    rng = np.random.default_rng(404)
+
+    def bf16(shape, scale):
+        x = (np.float32(scale) * rng.standard_normal(shape, dtype=np.float32)).view(np.uint32)
+        return (x >> 16).astype(np.uint16)
+
+    ar_p = [bf16((tp, m, W), 0.02) for _ in range(calls)]
+    gamma = ((np.float32(1) + np.float32(0.1) * rng.standard_normal(W, dtype=np.float32)).view(np.uint32) >> 16)
+    gamma = gamma.astype(np.uint16)
+    g_sh = []
+    for _ in range(calls):
+        w = rng.integers(0, 1 << 32, size=(tp, m, s), dtype=np.uint64).astype(np.uint32)
+        w[rng.random(w.shape) < 0.03] = 0x80000000
+        g_sh.append(w)
+    ts_p = []
+    for _ in range(calls):
+        p = bf16((tp, m, W), 0.5)
+        p[:, :, 3::7] = 0x8000
+        ts_p.append(p)
+
+    ar_box, nbox = armed_box((2, tp, cap, W // 2)), armed_box((2, cap, 256))
+    g_box = armed_box((cap, tp * s))
+    ts_recv, ts_gath = armed_box((2, tp, cap, W // 2)), armed_box((2, 1, cap, W // 2))
+    ar_in, g_d = [dev16(p) for p in ar_p], dev16(gamma)
+    g_in = [dev32(w) for w in g_sh]
+    ts_in = [dev16(p) for p in ts_p]
+    ar_out = [(empty16((m, W)), empty16((m, W))) for _ in range(calls)]
+    g_out = [torch.empty((m, tp * s), dtype=torch.int32, device="cuda") for _ in range(calls)]
+    ts_out = [empty16((m, W)) for _ in range(calls)]
+    torch.cuda.synchronize()
+
+    errors = []
+
+    def run(stream, body):
+        try:
+            with torch.cuda.stream(stream):
+                for i in range(calls):
+                    assert body(i) is True
+        except Exception as e:  # noqa: BLE001 -- reported after the join
+            errors.append(e)
+
+    jobs = [
+        (side_streams[0], lambda i: lib.arnorm_push_reduce_norm(ar_in[i], None, g_d, ar_box, i % 2, EPS, ar_out[i][0],
+                                                                ar_out[i][1], norm_box=nbox)),
+        (side_streams[1], lambda i: lib.gather_push_poll(g_in[i], g_box, out=g_out[i], copy=True)),
+        (side_streams[2], lambda i: lib.twoshot_push_reduce_read(ts_in[i], ts_recv, ts_gath, i % 2, ts_out[i])),
+    ]
+    threads = [threading.Thread(target=run, args=job) for job in jobs]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    torch.cuda.synchronize()
+    assert not errors, errors
+    assert lib.status() == lib.OK
+
+    ar_h = oracle.arm(np.empty((2, tp, cap, W // 2), dtype=np.uint32))
+    g_h = oracle.arm(np.empty((cap, tp * s), dtype=np.uint32))
+    recv_h = oracle.arm(np.empty((2, tp, cap, W // 2), dtype=np.uint32))
+    gath_h = oracle.arm(np.empty((2, 1, cap, W // 2), dtype=np.uint32))
+    for i in range(calls):
+        oracle.arnorm_push(ar_h, ar_p[i], i % 2, 0)
+        want_out, want_res = oracle.arnorm_reduce_norm(ar_h, i % 2, m, None, gamma, EPS)
+        assert_bits_equal(host16(ar_out[i][1]), want_res, f"ArNorm call {i} residual_out")
+        exact_zero = (oracle.widen(want_res) == 0) | (oracle.widen(gamma) == 0)[None, :]
+        assert_out_close(host16(ar_out[i][0]), want_out, f"ArNorm call {i} out", exact_zero=exact_zero)
+        oracle.gather_push(g_h, g_sh[i], 0)
+        assert_bits_equal(host32(g_out[i]), oracle.gather_poll(g_h, m, True), f"Gather call {i}")
+        oracle.twoshot_push(recv_h, ts_p[i], i % 2, 0)
+        want = oracle.twoshot_reduce(recv_h, gath_h, i % 2, m)
+        assert_bits_equal(oracle.twoshot_read(gath_h, i % 2, m), want, "oracle two-shot read")
+        assert_bits_equal(host16(ts_out[i]), want, f"two-shot call {i}")
+    assert_bits_equal(host32(ar_box), ar_h, "ArNorm mailbox")
+    assert np.all(host32(nbox) == 0x80000000), "norm box left re-armed"
+    assert_bits_equal(host32(g_box), g_h, "Gather mailbox")
+    assert_bits_equal(host32(ts_recv), recv_h, "two-shot slots")
+    assert_bits_equal(host32(ts_gath), gath_h, "two-shot gather row")
