@@ -4,16 +4,21 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W]
 
 One step = one ArNorm call of the one-GPU stand-in at TP=8, M=4 (the embedding
-call: residual = AR(x)): arnorm_push of the 8 ranks' partial rows, then
-arnorm_reduce_norm (poll, re-arm, rank-order sum, RMSNorm), alternating the two
-layer parities.  The calls are captured in HIP graphs and replayed; K steps are timed
-between two device synchronizations, inputs already resident in HBM.
+call: residual = AR(x)): one arnorm_push_reduce_norm, the 8 ranks' pushes of their
+partial rows and the consumer (poll, re-arm, rank-order sum, RMSNorm; rows split over
+7 workgroups through a norm box) in one launch, alternating the two layer parities.
+The calls are captured in HIP graphs and replayed; K steps are timed between two
+device synchronizations, inputs already resident in HBM.
 
 The same JSON line carries:
   roofline      the consumer kernel at TP=8, M=4096 with residual (the HBM-bound
                 workload): algorithmic bytes per launch / its average duration, HIP
-                events around each launch on the stream it runs on, against 8 TB/s
+                events around each launch on the stream it runs on, against 8 TB/s;
+                and (roofline.call) the whole call at that size, push + consumer, as
+                it repeats back to back
   push          the producer kernel at the same size, same method
+  gather        Gather calls (TP=8, M=32, S=896, and the drafter's shapes)
+  twoshot       the two-shot stand-in call at M=4 and its kernels at M=4096
   cpu_baseline  the CPU oracle timed on the same TP=8, M=4 call on this host
 Prints exactly one JSON line (rank 0, one GPU).
 """
@@ -263,14 +268,16 @@ def time_twoshot(lib, torch, calls=1000, chunk=50, launches=20, modes=("cold", "
     return res
 
 
-def time_roofline(lib, torch, launches=20, modes=("cold", "warm")):
+def time_roofline(lib, torch, launches=20, modes=("cold", "warm"), steady_calls=0):
     """Consumer and producer kernels at TP=8, M=4096 with residual, each launch timed
     with HIP events on the launch stream.  "cold": before every timed launch a 1 GiB
     read-only pass over an unrelated buffer leaves MI355X's 256 MB last-level cache
     holding clean lines of that buffer, so the kernel's bytes come from HBM.  "warm": the
     push and the consumer back to back, as the call runs, where the consumer finds part of
     what the push just wrote still in that cache.  Returns cfg and {mode: (reduce_us,
-    push_us)}."""
+    push_us)}; with steady_calls, also "steady": µs per call of that many push + consumer
+    pairs back to back, timed as a whole (the stand-in call at this size as it repeats,
+    each kernel paying for the lines the previous one left dirty in the cache)."""
     from tp_all_reduce_arnorm_amd import workloads as wl
 
     cfg = wl.CONFIGS["c5"]
@@ -308,6 +315,16 @@ def time_roofline(lib, torch, launches=20, modes=("cold", "warm")):
         assert lib.status() == lib.OK
         res[mode] = (float(np.mean([a.elapsed_time(b) for a, b in red])) * 1e3,
                      float(np.mean([a.elapsed_time(b) for a, b in push])) * 1e3)
+    if steady_calls:
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steady_calls):
+            assert lib.arnorm_push(p_d, box, 0, 0) is True
+            assert lib.arnorm_reduce_norm(r_d, g_d, box, 0, EPS, out, rout) is True
+        e1.record()
+        torch.cuda.synchronize()
+        assert lib.status() == lib.OK
+        res["steady"] = e0.elapsed_time(e1) * 1e3 / steady_calls
     return cfg, res
 
 
@@ -558,7 +575,7 @@ def main():
     elapsed = time_latency(lib, torch, args.steps, args.warmup)
     pair_us = time_latency(lib, torch, args.steps, args.warmup, one_launch=False) / args.steps * 1e6
     m_us = {m: time_latency(lib, torch, args.steps, args.warmup, m=m) / args.steps * 1e6 for m in (1, 64)}
-    cfg5, troof = time_roofline(lib, torch)
+    cfg5, troof = time_roofline(lib, torch, steady_calls=20)
     red_us, push_us = troof["cold"]
     warm_red_us, warm_push_us = troof["warm"]
     cfg4, gather_us = time_gather(lib, torch)
@@ -629,6 +646,11 @@ def main():
             "warm": {"kernel_us": round(warm_red_us, 2), "frac": round(rb / (warm_red_us * 1e-6) / 1e9 / PEAK_HBM_GBPS, 4),
                      "note": "right after the push, as the call runs: part of the slots the push just wrote "
                              "are still in the last-level cache"},
+            "call": {"us_per_call": round(troof["steady"], 2), "algorithmic_bytes": rb + pb,
+                     "frac": round((rb + pb) / (troof["steady"] * 1e-6) / 1e9 / PEAK_HBM_GBPS, 4),
+                     "note": "the whole stand-in call at this size, push of 8 slots + consumer, 20 calls back "
+                             "to back timed as one span: each kernel also writes back what the previous one "
+                             "left dirty in the last-level cache"},
         },
         "push": {
             "kernel": "arnorm_push", "workload": "8 slots, M=4096, cold as the roofline", "algorithmic_bytes": pb,
