@@ -63,6 +63,14 @@ std::atomic<int> g_poll_mode{0};   // Gather polls: 0 = automatic, 1 = re-read a
 #ifndef ARNORM_STEP_PUSH_U
 #define ARNORM_STEP_PUSH_U 2
 #endif
+// arnorm_push_reduce_norm, one-launch form: up to this M a row's consumer workgroups are
+// placed on one XCD (push_reduce_kernel, xcd_rows).  Measured on MI355X at TP=8 (us per
+// call, HIP-graph replay, spread against one XCD per row): M=1 4.44 / 4.21, M=2 4.52 /
+// 4.44, M=3 4.58 / 4.56, M=4 4.64 / 4.59, M=5 4.67 / 4.69, M=6 4.74 / 4.91, M=8 5.14 /
+// 5.21: the exchange stays in one L2 while the rows are few, and crowds the XCDs after.
+#ifndef ARNORM_XCD_ROWS_MAX_M
+#define ARNORM_XCD_ROWS_MAX_M 4
+#endif
 // Fragments per thread in flight in a Gather poll whose grid is capped below a thread
 // per fragment.
 #ifndef ARNORM_POLL_U
@@ -368,7 +376,8 @@ int arnorm_push_reduce_norm(const uint16_t *partials, const uint16_t *residual, 
   constexpr int U = ARNORM_STEP_PUSH_U;
   const uint32_t nt = arn::kRowFrags / K;
   a.per_slot = (a.frags + nt * U - 1) / (nt * U);
-  const dim3 grid(tp * a.per_slot + M * K);
+  a.xcd_rows = M <= ARNORM_XCD_ROWS_MAX_M;
+  const dim3 grid(tp * a.per_slot + (a.xcd_rows ? (M + 7) / 8 * 8 * K : M * K));
   const bool res = residual != nullptr;
 #define ARNORM_STEP_LAUNCH_K(TPV, KV)                                                                              \
   return res ? launch(arn::push_reduce_kernel<TPV, true, KV, U, kPolPush, kPolPoll, kPolRearm, kPolIn, kPolIO>, grid,     \
