@@ -86,7 +86,7 @@ def time_latency(lib, torch, steps, warmup, chunk=50, one_launch=True, m=None):
 
     from tp_all_reduce_arnorm_amd import workloads as wl
 
-    cfg = wl.CONFIGS["c2"] if m is None else dataclasses.replace(wl.CONFIGS["c2"], m=m)
+    cfg = wl.CONFIGS["tp8_m4"] if m is None else dataclasses.replace(wl.CONFIGS["tp8_m4"], m=m)
     src = wl.ArNormInputs(cfg)
     box = torch.empty((2, cfg.tp, cfg.cap, HIDDEN // 2), dtype=torch.int32, device="cuda")
     nbox = torch.empty((2, cfg.cap, 256), dtype=torch.int32, device="cuda")
@@ -145,17 +145,17 @@ def gather_bytes(tp, m, s, copy=True):
     return 2 * words * 4, (3 if copy else 1) * words * 4
 
 
-def time_gather(lib, torch, calls=1000, chunk=50, name="c4", one_launch=True, m=None):
+def time_gather(lib, torch, calls=1000, chunk=50, name="gather_tp8_m32", one_launch=True, m=None):
     """µs per Gather call, graph-replayed: gather_push_poll (every rank's push and the
     copying poll, one launch for calls within 1 MiB), or with one_launch False the pair
-    gather_push + gather_poll.  c4 is TP=8, M=32, S=896; ctx and logits are the
+    gather_push + gather_poll.  gather_tp8_m32 is TP=8, M=32, S=896; ctx and logits are the
     drafter's context-projection and lm_head shapes; m overrides the row count."""
     import dataclasses
 
     from tp_all_reduce_arnorm_amd import workloads as wl
 
     cfg = wl.CONFIGS[name] if m is None else dataclasses.replace(wl.CONFIGS[name], m=m)
-    words = wl.gather_shards(cfg) if name == "c4" else wl.bf16_shards(cfg)
+    words = wl.gather_shards(cfg) if name == "gather_tp8_m32" else wl.bf16_shards(cfg)
     shards = torch.from_numpy(words.view(np.int32)).cuda()
     box = torch.empty((cfg.cap, cfg.tp * cfg.s), dtype=torch.int32, device="cuda")
     assert lib.lamport_arm(box) is True
@@ -201,7 +201,7 @@ def time_twoshot(lib, torch, calls=1000, chunk=50, launches=20, modes=("cold", "
     from tp_all_reduce_arnorm_amd import workloads as wl
 
     res = {}
-    cfg = wl.CONFIGS["c2"]
+    cfg = wl.CONFIGS["tp8_m4"]
     src = wl.ArNormInputs(cfg)
     recv = torch.empty((2, 8, cfg.cap, HIDDEN // 2), dtype=torch.int32, device="cuda")
     gath = torch.empty((2, 1, cfg.cap, HIDDEN // 2), dtype=torch.int32, device="cuda")
@@ -235,7 +235,7 @@ def time_twoshot(lib, torch, calls=1000, chunk=50, launches=20, modes=("cold", "
         res[key] = (time.perf_counter() - t0) / (calls // chunk * chunk) * 1e6
         del g
 
-    cfg = wl.CONFIGS["c5"]
+    cfg = wl.CONFIGS["tp8_m4096"]
     p5 = torch.from_numpy(wl.ArNormInputs(cfg).partials().view(np.int16)).cuda()
     recv = torch.empty((1, 8, cfg.cap, HIDDEN // 2), dtype=torch.int32, device="cuda")
     gath = torch.empty((1, 1, cfg.cap, HIDDEN // 2), dtype=torch.int32, device="cuda")
@@ -280,7 +280,7 @@ def time_roofline(lib, torch, launches=20, modes=("cold", "warm"), steady_calls=
     each kernel paying for the lines the previous one left dirty in the cache)."""
     from tp_all_reduce_arnorm_amd import workloads as wl
 
-    cfg = wl.CONFIGS["c5"]
+    cfg = wl.CONFIGS["tp8_m4096"]
     src = wl.ArNormInputs(cfg)
     p, r = src.call()
     box = torch.empty((1, cfg.tp, cfg.cap, HIDDEN // 2), dtype=torch.int32, device="cuda")
@@ -376,7 +376,7 @@ def cpu_baseline(budget_s=10.0):
     import oracle
     from tp_all_reduce_arnorm_amd import workloads as wl
 
-    cfg = wl.CONFIGS["c2"]
+    cfg = wl.CONFIGS["tp8_m4"]
     src = wl.ArNormInputs(cfg)
     box = oracle.arm(np.empty((2, cfg.tp, cfg.cap, HIDDEN // 2), dtype=np.uint32))
     inputs = [src.partials() for _ in range(8)]
@@ -589,10 +589,10 @@ def main():
                         "two_launch_us_per_call": round(pus, 3),
                         "push_algorithmic_bytes": gather_bytes(c.tp, c.m, c.s)[0],
                         "poll_algorithmic_bytes": gather_bytes(c.tp, c.m, c.s)[1]}
-    for name, m in (("c4", 4), ("logits", 1)):  # decode-sized calls, one launch
+    for key, name, m in (("gather_tp8_m4", "gather_tp8_m32", 4), ("logits_m1", "logits", 1)):  # one launch
         c, us = time_gather(lib, torch, name=name, m=m)
         _, pus = time_gather(lib, torch, name=name, m=m, one_launch=False)
-        shapes[f"{name}_m{m}"] = {"tp": c.tp, "m": c.m, "s_words": c.s, "us_per_call": round(us, 3),
+        shapes[key] = {"tp": c.tp, "m": c.m, "s_words": c.s, "us_per_call": round(us, 3),
                                   "two_launch_us_per_call": round(pus, 3)}
     tsr, tsq = twoshot_bytes(8, 4096)
     gpb, gqb = gather_bytes(cfg4.tp, cfg4.m, cfg4.s)
@@ -663,7 +663,7 @@ def main():
         "gather": {
             "workload": "Gather TP=8 M=32 S=896 words cap=64: gather_push_poll with copy, HIP-graph replay "
                         "(917504 B of gathered rows, above the 512 KiB one-launch limit, so it runs as "
-                        "the pair gather_push + gather_poll; the c4_m4 and logits_m1 drafter_shapes "
+                        "the pair gather_push + gather_poll; the gather_tp8_m4 and logits_m1 drafter_shapes "
                         "entries are one-launch calls); two_launch_us_per_call is the pair itself",
             "us_per_call": round(gather_us, 3), "two_launch_us_per_call": round(gather_pair_us, 3),
             "push_algorithmic_bytes": gpb, "poll_algorithmic_bytes": gqb,

@@ -131,7 +131,7 @@ def test_c_client_on_gpu(tmp_path):
     if not os.path.exists(lib):
         pytest.skip("libarnorm.so not built")
     say("[c client] one-launch ArNorm from C on the GPU")
-    cfg = wl.CONFIGS["c2"]
+    cfg = wl.CONFIGS["tp8_m4"]
     src = wl.ArNormInputs(cfg)
     calls = 4
     parts = [src.call()[0] for _ in range(calls)]

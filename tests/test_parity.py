@@ -2,7 +2,7 @@
 same seeded inputs.  Bit-exact: residual_out (the all-reduced row when there is no
 residual), every gathered word, and the mailbox after every call.  out: within one
 BF16 ulp, with at most 1 % of its values off the oracle's bits.  Sizes: the five
-workloads (c1..c5, c5 on sampled rows), plus edge cases."""
+workloads (tp2_m1..tp8_m4096, tp8_m4096 on sampled rows), plus edge cases."""
 
 import numpy as np
 import pytest
@@ -81,33 +81,33 @@ def run_config(lib, name, calls=None, threads=0, split=None):
         run_call(lib, box_d, box_h, p, r, gamma_d, src.gamma, call % cfg.parities, norm_box=nbox)
 
 
-def test_c1(lib):
-    run_config(lib, "c1")
+def test_tp2_m1(lib):
+    run_config(lib, "tp2_m1")
 
 
-def test_c2(lib):
-    run_config(lib, "c2")
+def test_tp8_m4(lib):
+    run_config(lib, "tp8_m4")
 
 
-def test_c3(lib):
-    run_config(lib, "c3")
+def test_tp8_m64(lib):
+    run_config(lib, "tp8_m64")
 
 
 @pytest.mark.parametrize("threads", [448, 256])
-def test_c3_other_workgroup_sizes(lib, threads):
-    run_config(lib, "c3", calls=4, threads=threads)
+def test_tp8_m64_other_workgroup_sizes(lib, threads):
+    run_config(lib, "tp8_m64", calls=4, threads=threads)
 
 
 @pytest.mark.parametrize("split", [0, 7, 14])
-@pytest.mark.parametrize("name", ["c1", "c2", "c3"])
+@pytest.mark.parametrize("name", ["tp2_m1", "tp8_m4", "tp8_m64"])
 def test_split_rows(lib, name, split):
     """Rows split over 7 or 14 workgroups (and the automatic choice), the row's sum of
     squares exchanged through the norm box, which every call leaves re-armed."""
     run_config(lib, name, calls=min(wl.CONFIGS[name].calls, 12), split=split)
 
 
-@pytest.mark.parametrize("name,with_box,split", [("c1", True, 0), ("c2", True, 0), ("c3", True, 0), ("c2", False, 0),
-                                                ("c1", True, 14), ("c2", True, 14)])
+@pytest.mark.parametrize("name,with_box,split", [("tp2_m1", True, 0), ("tp8_m4", True, 0), ("tp8_m64", True, 0), ("tp8_m4", False, 0),
+                                                ("tp2_m1", True, 14), ("tp8_m4", True, 14)])
 def test_push_reduce_norm_one_call(lib, name, with_box, split):
     """arnorm_push_reduce_norm (one launch with a norm box where the TP slots of rows < M
     fit 1 MiB, rows split 7 or 14 ways; else the pair of launches) against the oracle's
@@ -162,11 +162,11 @@ def test_push_reduce_norm_torture(lib, tp, split):
         assert lib.status() == lib.OK
 
 
-def test_c3_per_rank_pushes_and_chained_residual(lib):
+def test_tp8_m64_per_rank_pushes_and_chained_residual(lib):
     """Ranks push one by one (and in groups), and each call's residual is the previous
     call's residual_out, as consecutive layers use it."""
-    cfg = wl.CONFIGS["c3"]
-    say("[parity] c3 per-rank pushes, chained residual")
+    cfg = wl.CONFIGS["tp8_m64"]
+    say("[parity] tp8_m64 per-rank pushes, chained residual")
     src = wl.ArNormInputs(cfg)
     shape = (2, 8, 64, W // 2)
     box_d, box_h = armed_box(shape), oracle.arm(np.empty(shape, dtype=np.uint32))
@@ -179,9 +179,9 @@ def test_c3_per_rank_pushes_and_chained_residual(lib):
                             pushes=groupings[call % len(groupings)])
 
 
-def test_c4_gather(lib):
-    cfg = wl.CONFIGS["c4"]
-    say("[parity] c4 gather copy / no-copy")
+def test_gather_tp8_m32(lib):
+    cfg = wl.CONFIGS["gather_tp8_m32"]
+    say("[parity] gather_tp8_m32 copy / no-copy")
     shards = wl.gather_shards(cfg)
     gshape = (cfg.cap, cfg.tp * cfg.s)
     gbox_d = armed_box(gshape)
@@ -247,7 +247,7 @@ def test_drafter_gather_shapes(lib, name, m, tp):
         assert np.array_equal(blk[:, 1::2][~sent], src[:, 1::2][~sent]) and np.all(blk[:, 1::2][sent] == 0)
 
 
-@pytest.mark.parametrize("name,m", [("c4", 32), ("c4", 16), ("c4", 1), ("ctx", 64), ("logits", 4),
+@pytest.mark.parametrize("name,m", [("gather_tp8_m32", 32), ("gather_tp8_m32", 16), ("gather_tp8_m32", 1), ("ctx", 64), ("logits", 4),
                                     ("logits", 2), ("logits", 1)])
 def test_gather_push_poll_one_call(lib, name, m):
     """gather_push_poll (one launch for calls within 512 KiB, else the pair) against the
@@ -259,7 +259,7 @@ def test_gather_push_poll_one_call(lib, name, m):
 
     say(f"[parity] gather_push_poll {name} M={m}")
     cfg = dataclasses.replace(wl.CONFIGS[name], m=m)
-    shards = wl.gather_shards(cfg) if name == "c4" else wl.bf16_shards(cfg)
+    shards = wl.gather_shards(cfg) if name == "gather_tp8_m32" else wl.bf16_shards(cfg)
     gshape = (cfg.cap, cfg.tp * cfg.s)
     gbox_d, gbox_h = armed_box(gshape), oracle.arm(np.empty(gshape, dtype=np.uint32))
     sh_d = dev32(shards)
@@ -279,7 +279,7 @@ def test_gather_push_poll_one_call(lib, name, m):
 
 
 @pytest.mark.parametrize("u,mode", [(1, 2), (4, 1), (4, 2)])
-@pytest.mark.parametrize("name,m", [("c4", 16), ("c4", 1), ("logits", 1)])
+@pytest.mark.parametrize("name,m", [("gather_tp8_m32", 16), ("gather_tp8_m32", 1), ("logits", 1)])
 def test_gather_poll_layouts_one_launch(lib, name, m, u, mode):
     """gather_push_poll in one launch, its pollers forced to 1 or 4 fragments per thread and
     to re-read or witness waits: the producers in the same grid are still writing when
@@ -291,7 +291,7 @@ def test_gather_poll_layouts_one_launch(lib, name, m, u, mode):
     say(f"[parity] gather one launch {name} M={m} frags/thread={u} mode={mode}")
     lib.set_poll(u, mode)
     cfg = dataclasses.replace(wl.CONFIGS[name], m=m)
-    shards = wl.gather_shards(cfg) if name == "c4" else wl.bf16_shards(cfg)
+    shards = wl.gather_shards(cfg) if name == "gather_tp8_m32" else wl.bf16_shards(cfg)
     gshape = (cfg.cap, cfg.tp * cfg.s)
     gbox_d, gbox_h = armed_box(gshape), oracle.arm(np.empty(gshape, dtype=np.uint32))
     sh_d = dev32(shards)
@@ -315,7 +315,7 @@ def test_gather_large(lib, tp, m, s):
     import torch
 
     say(f"[parity] gather large tp={tp} M={m} S={s}")
-    cfg = dataclasses.replace(wl.CONFIGS["c4"], tp=tp, m=m, s=s, cap=m, seed=40 + tp)
+    cfg = dataclasses.replace(wl.CONFIGS["gather_tp8_m32"], tp=tp, m=m, s=s, cap=m, seed=40 + tp)
     shards = wl.gather_shards(cfg)
     gshape = (cfg.cap, tp * s)
     gbox_d, gbox_h = armed_box(gshape), oracle.arm(np.empty(gshape, dtype=np.uint32))
@@ -336,14 +336,14 @@ def test_gather_large(lib, tp, m, s):
     assert lib.status() == lib.OK
 
 
-def test_c5_full_size_sampled_rows(lib):
+def test_tp8_m4096_full_size_sampled_rows(lib):
     """M = 4096, TP = 8, in the launch configuration the benchmark times; the oracle
     checks a sample of rows one by one (rows are independent), and the whole mailbox
     must be re-armed."""
     import torch
 
-    cfg = wl.CONFIGS["c5"]
-    say("[parity] c5 full size")
+    cfg = wl.CONFIGS["tp8_m4096"]
+    say("[parity] tp8_m4096 full size")
     src = wl.ArNormInputs(cfg)
     p, r = src.call()
     shape = (1, 8, cfg.cap, W // 2)
@@ -546,7 +546,7 @@ def test_norm_closed_form_rows(lib, threads):
 def test_fused_own_push(lib, rank, split):
     """The one-kernel form: the consumer brings rank `rank`'s row itself."""
     say(f"[parity] fused own push rank={rank} split={split}")
-    cfg = wl.CONFIGS["c3"]
+    cfg = wl.CONFIGS["tp8_m64"]
     src = wl.ArNormInputs(cfg)
     shape = (2, 8, 64, W // 2)
     box_d, box_h = armed_box(shape), oracle.arm(np.empty(shape, dtype=np.uint32))
@@ -577,7 +577,7 @@ def test_max_rows_and_single_row(lib):
 
 def test_in_place_residual(lib):
     say("[parity] residual_out == residual")
-    cfg = wl.CONFIGS["c3"]
+    cfg = wl.CONFIGS["tp8_m64"]
     src = wl.ArNormInputs(cfg)
     p, r = src.call()
     box_d = armed_box((2, 8, 64, W // 2))

@@ -24,7 +24,7 @@ def small_spin(lib):
 
 def test_missing_push_times_out_and_recovers(lib, small_spin):
     say("[protocol] arnorm missing push -> timeout -> lamport_arm -> exact")
-    cfg = wl.CONFIGS["c2"]
+    cfg = wl.CONFIGS["tp8_m4"]
     src = wl.ArNormInputs(cfg)
     shape = (2, 8, 64, W // 2)
     box_d = armed_box(shape)
@@ -56,7 +56,7 @@ def test_gather_missing_push_times_out(lib, small_spin):
     import torch
 
     say("[protocol] gather missing push -> timeout -> lamport_arm -> exact")
-    cfg = wl.CONFIGS["c4"]
+    cfg = wl.CONFIGS["gather_tp8_m32"]
     shards = wl.gather_shards(cfg)
     gshape = (cfg.cap, cfg.tp * cfg.s)
     gbox_d = armed_box(gshape)
@@ -81,9 +81,9 @@ def test_graph_replay_alternating_parities(lib, form):
     work and synchronizations in between) matches the oracle."""
     import torch
 
-    say(f"[protocol] HIP graph replay, c2 shape, {form}")
+    say(f"[protocol] HIP graph replay, tp8_m4 shape, {form}")
     lib.set_reduce_split(14 if form == "one_call_split14" else 0)
-    cfg = wl.CONFIGS["c2"]
+    cfg = wl.CONFIGS["tp8_m4"]
     src = wl.ArNormInputs(cfg)
     shape = (2, 8, 64, W // 2)
     box_d = armed_box(shape)
@@ -183,7 +183,7 @@ def test_concurrent_consumer_polls_while_producer_pushes(lib, side_streams, m, r
 
 @pytest.mark.parametrize("frags_per_thread", [0, 4])
 def test_concurrent_gather_consumer_first(lib, side_streams, frags_per_thread):
-    """The poll launched first on its own stream, the push later and delayed, at c4, with
+    """The poll launched first on its own stream, the push later and delayed, at gather_tp8_m32, with
     the witness wait forced: one fragment per thread (automatic) or 4 in flight per
     thread (forced)."""
     import torch
@@ -193,7 +193,7 @@ def test_concurrent_gather_consumer_first(lib, side_streams, frags_per_thread):
     lib.set_spin_limit(1 << 16)
     lib.set_poll(frags_per_thread, 2)
     try:
-        cfg = wl.CONFIGS["c4"]
+        cfg = wl.CONFIGS["gather_tp8_m32"]
         shards = wl.gather_shards(cfg)
         gshape = (cfg.cap, cfg.tp * cfg.s)
         gbox_d = armed_box(gshape)

@@ -37,7 +37,7 @@ def boxes(parities, tp, cap, width):
             oracle.arm(np.empty(gshape, dtype=np.uint32)))
 
 
-@pytest.mark.parametrize("name", ["c2", "c3"])
+@pytest.mark.parametrize("name", ["tp8_m4", "tp8_m64"])
 def test_workload_shapes(lib, name):
     cfg = wl.CONFIGS[name]
     say(f"[twoshot] {name}")
@@ -92,7 +92,7 @@ def test_m4096_sampled_rows(lib):
     import torch
 
     say("[twoshot] M=4096 sampled rows")
-    cfg = wl.CONFIGS["c5"]
+    cfg = wl.CONFIGS["tp8_m4096"]
     src = wl.ArNormInputs(cfg)
     p = src.partials()
     recv_d = armed_box((1, 8, cfg.cap, W // 2))
@@ -170,9 +170,9 @@ def tsr_call(lib, recv_d, gath_d, recv_h, gath_h, partials, parity):
     return got
 
 
-@pytest.mark.parametrize("name,calls", [("c2", 8), ("c3", 4)])
+@pytest.mark.parametrize("name,calls", [("tp8_m4", 8), ("tp8_m64", 4)])
 def test_one_call_workloads(lib, name, calls):
-    """c2 (TP=8, M=4: one launch) and c3 (M=64: the three launches)."""
+    """tp8_m4 (TP=8, M=4: one launch) and tp8_m64 (M=64: the three launches)."""
     cfg = wl.CONFIGS[name]
     say(f"[twoshot] one call {name}")
     src = wl.ArNormInputs(cfg)

@@ -15,8 +15,8 @@ def _tree_sum(slot_words):
     return obf.round_to_bf16(lanes[0])
 
 
-def test_c1_shapes_and_distribution():
-    cfg = wl.CONFIGS["c1"]
+def test_tp2_m1_shapes_and_distribution():
+    cfg = wl.CONFIGS["tp2_m1"]
     src = wl.ArNormInputs(cfg)
     p, r = src.call()
     assert p.shape == (2, 1, 7168) and p.dtype == np.uint16
@@ -28,19 +28,19 @@ def test_c1_shapes_and_distribution():
 
 
 def test_seeded_reproducible():
-    a = wl.ArNormInputs(wl.CONFIGS["c2"]).call()[0]
-    b = wl.ArNormInputs(wl.CONFIGS["c2"]).call()[0]
+    a = wl.ArNormInputs(wl.CONFIGS["tp8_m4"]).call()[0]
+    b = wl.ArNormInputs(wl.CONFIGS["tp8_m4"]).call()[0]
     assert np.array_equal(a, b)
 
 
-def test_c2_no_residual():
-    p, r = wl.ArNormInputs(wl.CONFIGS["c2"]).call()
+def test_tp8_m4_no_residual():
+    p, r = wl.ArNormInputs(wl.CONFIGS["tp8_m4"]).call()
     assert r is None and p.shape == (8, 4, 7168)
     assert abs(obf.widen(p).astype(np.float64).std() - 0.02) < 0.002
 
 
-def test_c3_sentinel_and_tree_rows():
-    cfg = wl.CONFIGS["c3"]
+def test_tp8_m64_sentinel_and_tree_rows():
+    cfg = wl.CONFIGS["tp8_m64"]
     src = wl.ArNormInputs(cfg)
     p, r = src.call()
     words = obf.pack_pairs(p)
@@ -56,13 +56,13 @@ def test_c3_sentinel_and_tree_rows():
     assert abs(obf.widen(p[:, :48]).astype(np.float64).std() - 0.5) < 0.05
 
 
-def test_c4_shards():
-    cfg = wl.CONFIGS["c4"]
+def test_gather_tp8_m32_shards():
+    cfg = wl.CONFIGS["gather_tp8_m32"]
     w = wl.gather_shards(cfg)
     assert w.shape == (8, 32, 896) and w.dtype == np.uint32
     assert 0.02 < np.mean(w == np.uint32(0x80000000)) < 0.04
 
 
-def test_c5_shape_metadata():
-    cfg = wl.CONFIGS["c5"]
+def test_tp8_m4096_shape_metadata():
+    cfg = wl.CONFIGS["tp8_m4096"]
     assert (cfg.tp, cfg.m, cfg.cap, cfg.parities) == (8, 4096, 4096, 1)

@@ -14,17 +14,19 @@ kernels and the CPU oracle both expect them:
 Workloads (the TP8 drafter shapes of the vLLM DSpark drafter pages: hidden 7168,
 rows M = tokens in flight, TP slots playing the ranks of the one-GPU stand-in):
 
-  c1  ArNorm TP=2, M=1, residual, one parity, seed 0
-  c2  ArNorm TP=8, M=4, no residual (residual = AR(x)), 2 parities over 8 calls, seed 1
-  c3  ArNorm TP=8, M=64 = cap, residual, 5 % of partial words set to the sentinel
-      pair, rows 48..63 built so that rank-order and pairwise-tree sums differ,
-      61 calls over 2 parities, seed 2
-  c4  Gather TP=8, M=32, S=896 words, cap=64, uniform words with 3 % sentinel, seed 3
-  c5  ArNorm TP=8, M=4096, residual, partials and residual N(0, 1), seed 4
-  ctx     Gather of the context projection: TP=8, [M=64, 896] BF16 shards (448 words),
-          N(0, 1) with 1 % of values -0, seed 5
-  logits  Gather of the lm_head logits: TP=8, [M=4, 20480] BF16 shards (10240 words) of
-          a synthetic V = 163840, N(0, 1) with 1 % of values -0, seed 6
+  tp2_m1          ArNorm TP=2, M=1, residual, one parity, seed 0
+  tp8_m4          ArNorm TP=8, M=4, no residual (residual = AR(x)), 2 parities over 8
+                  calls, seed 1
+  tp8_m64         ArNorm TP=8, M=64 = cap, residual, 5 % of partial words set to the
+                  sentinel pair, rows 48..63 built so that rank-order and pairwise-tree
+                  sums differ, 61 calls over 2 parities, seed 2
+  gather_tp8_m32  Gather TP=8, M=32, S=896 words, cap=64, uniform words with 3 %
+                  sentinel, seed 3
+  tp8_m4096       ArNorm TP=8, M=4096, residual, partials and residual N(0, 1), seed 4
+  ctx             Gather of the context projection: TP=8, [M=64, 896] BF16 shards (448
+                  words), N(0, 1) with 1 % of values -0, seed 5
+  logits          Gather of the lm_head logits: TP=8, [M=4, 20480] BF16 shards (10240
+                  words) of a synthetic V = 163840, N(0, 1) with 1 % of values -0, seed 6
 """
 
 from dataclasses import dataclass, field
@@ -66,22 +68,22 @@ class GatherConfig:
 
 
 CONFIGS = {
-    "c1": ArNormConfig(
-        "c1", tp=2, m=1, cap=64, parities=1, residual=True, sigma_partial=0.5,
+    "tp2_m1": ArNormConfig(
+        "tp2_m1", tp=2, m=1, cap=64, parities=1, residual=True, sigma_partial=0.5,
         sigma_residual=1.0, seed=0,
         description="ArNorm TP=2 slots, M=1 row, width 7168, residual, one parity"),
-    "c2": ArNormConfig(
-        "c2", tp=8, m=4, cap=64, parities=2, residual=False, sigma_partial=0.02,
+    "tp8_m4": ArNormConfig(
+        "tp8_m4", tp=8, m=4, cap=64, parities=2, residual=False, sigma_partial=0.02,
         sigma_residual=0.0, seed=1, calls=8,
         description="ArNorm TP=8, M=4 rows, width 7168, residual=False, 2 parities x 8 calls"),
-    "c3": ArNormConfig(
-        "c3", tp=8, m=64, cap=64, parities=2, residual=True, sigma_partial=0.5,
+    "tp8_m64": ArNormConfig(
+        "tp8_m64", tp=8, m=64, cap=64, parities=2, residual=True, sigma_partial=0.5,
         sigma_residual=1.0, seed=2, calls=61, sentinel_frac=0.05,
         tree_rows=tuple(range(48, 64)),
         description="ArNorm TP=8, M=64 (cap), residual, 5% sentinel words, "
                     "rank-vs-tree rows, 61 calls over 2 parities"),
-    "c4": GatherConfig(
-        "c4", tp=8, m=32, s=896, cap=64, sentinel_frac=0.03, seed=3,
+    "gather_tp8_m32": GatherConfig(
+        "gather_tp8_m32", tp=8, m=32, s=896, cap=64, sentinel_frac=0.03, seed=3,
         description="Gather TP=8, [M=32, S=896] word shards into [cap=64, 8*896]"),
     # the drafter's own gather shapes: the context projection's [M, 7168/TP] BF16 rows
     # and the lm_head's [M, V/TP] BF16 logits (V = 163840, a synthetic vocabulary: the
@@ -92,8 +94,8 @@ CONFIGS = {
     "logits": GatherConfig(
         "logits", tp=8, m=4, s=10240, cap=64, sentinel_frac=0.0, seed=6,
         description="lm_head logits gather: TP=8, [M=4, 20480] BF16 shards -> [M, 163840]"),
-    "c5": ArNormConfig(
-        "c5", tp=8, m=4096, cap=4096, parities=1, residual=True, sigma_partial=1.0,
+    "tp8_m4096": ArNormConfig(
+        "tp8_m4096", tp=8, m=4096, cap=4096, parities=1, residual=True, sigma_partial=1.0,
         sigma_residual=1.0, seed=4,
         description="ArNorm TP=8, M=4096 rows, width 7168, residual (HBM roofline run)"),
 }
