@@ -19,6 +19,7 @@ The same JSON line carries:
   push          the producer kernel at the same size, same method
   gather        Gather calls (TP=8, M=32, S=896, and the drafter's shapes)
   twoshot       the two-shot stand-in call at M=4 and its kernels at M=4096
+  drafter_step  a drafter decode step's collectives: 11 ArNorm calls and 2 Gathers
   cpu_baseline  the CPU oracle timed on the same TP=8, M=4 call on this host
 Prints exactly one JSON line (rank 0, one GPU).
 """
@@ -135,6 +136,59 @@ def time_latency(lib, torch, steps, warmup, chunk=50, one_launch=True, m=None):
     assert lib.status() == lib.OK
 
     return elapsed
+
+
+def time_drafter_step(lib, torch, steps=400, layers=11):
+    """µs per drafter decode step's collectives, graph-replayed: `layers` one-launch
+    ArNorm calls at TP=8, M=4 (the first without a residual, the embedding case; the
+    others with the new residual chained in place, as consecutive layers use it; parities
+    alternating) and the two Gathers of a step, the context projection (M=64, S=448
+    words) and the lm_head logits (M=4, S=10240 words)."""
+    import dataclasses
+
+    from tp_all_reduce_arnorm_amd import workloads as wl
+
+    cfg = wl.CONFIGS["tp8_m4"]
+    src = wl.ArNormInputs(dataclasses.replace(cfg, residual=True, sigma_residual=1.0))
+    box = torch.empty((2, cfg.tp, cfg.cap, HIDDEN // 2), dtype=torch.int32, device="cuda")
+    nbox = torch.empty((2, cfg.cap, 256), dtype=torch.int32, device="cuda")
+    assert lib.lamport_arm(box) is True and lib.lamport_arm(nbox) is True
+    parts = [torch.from_numpy(src.partials().view(np.int16)).cuda() for _ in range(layers)]
+    gamma = torch.from_numpy(src.gamma.view(np.int16)).cuda()
+    resid = torch.empty((cfg.m, HIDDEN), dtype=torch.int16, device="cuda")
+    out = torch.empty((cfg.m, HIDDEN), dtype=torch.int16, device="cuda")
+    gathers = []
+    for name in ("ctx", "logits"):
+        g = wl.CONFIGS[name]
+        gbox = torch.empty((g.cap, g.tp * g.s), dtype=torch.int32, device="cuda")
+        assert lib.lamport_arm(gbox) is True
+        gathers.append((torch.from_numpy(wl.bf16_shards(g).view(np.int32)).cuda(), gbox,
+                        torch.empty((g.m, g.tp * g.s), dtype=torch.int32, device="cuda")))
+
+    def step(k):
+        for layer in range(layers):
+            parity = (k * layers + layer) % 2
+            assert lib.arnorm_push_reduce_norm(parts[layer], resid if layer else None, gamma, box, parity, EPS,
+                                               out, resid, norm_box=nbox) is True
+        for shards, gbox, gout in gathers:
+            assert lib.gather_push_poll(shards, gbox, out=gout, copy=True) is True
+
+    for k in range(2):
+        step(k)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for k in range(2):  # two steps: the parities line up again after an even number of calls
+            step(k)
+    graph.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps // 2):
+        graph.replay()
+    torch.cuda.synchronize()
+    us = (time.perf_counter() - t0) / (steps // 2 * 2) * 1e6
+    assert lib.status() == lib.OK
+    return us
 
 
 def gather_bytes(tp, m, s, copy=True):
@@ -581,6 +635,7 @@ def main():
     cfg4, gather_us = time_gather(lib, torch)
     _, gather_pair_us = time_gather(lib, torch, one_launch=False)
     ts = time_twoshot(lib, torch)
+    step_us = time_drafter_step(lib, torch)
     shapes = {}
     for name in ("ctx", "logits"):
         c, us = time_gather(lib, torch, name=name)
@@ -683,6 +738,15 @@ def main():
             "warm_reduce_frac": round(tsr / (ts["reduce_us_m4096_warm"] * 1e-6) / 1e9 / PEAK_HBM_GBPS, 4),
             "warm_read_frac": round(tsq / (ts["read_us_m4096_warm"] * 1e-6) / 1e9 / PEAK_HBM_GBPS, 4),
             "reduce_algorithmic_bytes": tsr, "read_algorithmic_bytes": tsq,
+        },
+        "drafter_step": {
+            "workload": "the collectives of one drafter decode step at TP=8, HIP-graph replay: 11 one-launch "
+                        "ArNorm calls at M=4 (the first without a residual, the others chaining the new "
+                        "residual in place), the context-projection Gather (M=64, S=448 words) and the "
+                        "lm_head logits Gather (M=4, S=10240 words)",
+            "us_per_step": round(step_us, 2),
+            "context": "the pages quote 6-9 us per stock one-shot all-reduce (11 per step) and 16-20 us per "
+                       "stock all-gather (2 per step) on their NVLink hardware: another machine's figures",
         },
         "cpu_baseline": cpu,
     }
