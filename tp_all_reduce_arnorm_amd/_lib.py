@@ -150,7 +150,8 @@ def arnorm_reduce_norm(residual, gamma, mailbox, parity, eps, out, residual_out,
 def arnorm_push_reduce_norm(partials, residual, gamma, mailbox, parity, eps, out, residual_out, norm_box=None,
                             stream=None):
     """One stand-in call: every rank's push (partials BF16 [tp, M, 7168]) and the
-    consumer, in one launch when norm_box is given and M <= 64."""
+    consumer.  One launch when norm_box is given and the TP slots of rows < M total at
+    most 1 MiB (M <= 9 at TP=8); otherwise the pair arnorm_push + arnorm_reduce_norm."""
     tp_, m, width = partials.shape
     if width != HIDDEN:
         return None
