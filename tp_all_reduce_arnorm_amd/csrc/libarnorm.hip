@@ -63,13 +63,20 @@ std::atomic<int> g_poll_mode{0};   // Gather polls: 0 = automatic, 1 = re-read a
 #ifndef ARNORM_STEP_PUSH_U
 #define ARNORM_STEP_PUSH_U 2
 #endif
-// arnorm_push_reduce_norm, one-launch form: up to this M a row's consumer workgroups are
-// placed on one XCD (push_reduce_kernel, xcd_rows).  Measured on MI355X at TP=8 (us per
-// call, HIP-graph replay, spread against one XCD per row): M=1 4.44 / 4.21, M=2 4.52 /
-// 4.44, M=3 4.58 / 4.56, M=4 4.64 / 4.59, M=5 4.67 / 4.69, M=6 4.74 / 4.91, M=8 5.14 /
-// 5.21: the exchange stays in one L2 while the rows are few, and crowds the XCDs after.
+// arnorm_push_reduce_norm, one-launch form, few rows: up to this M a row's consumer
+// workgroups are placed on one XCD (push_reduce_kernel, xcd_rows) and the producers take
+// ARNORM_STEP_PUSH_U_FEW fragments per thread (half as many producer workgroups).
+// Measured on MI355X at TP=8 (us per call, HIP-graph replay):
+//   one XCD per row (spread / one XCD): M=1 4.44 / 4.21, M=2 4.52 / 4.44, M=3 4.58 /
+//   4.56, M=4 4.64 / 4.59, M=5 4.67 / 4.69, M=6 4.74 / 4.91, M=8 5.14 / 5.21;
+//   then 4 fragments per producer thread (2 / 4): M=2 4.49 / 4.41, M=3 4.52 / 4.46,
+//   M=4 4.61 / 4.50, M=5 4.70 / 4.82, M=6 4.80 / 4.91;
+// the exchange stays in one L2 while the rows are few, and crowds the XCDs after.
 #ifndef ARNORM_XCD_ROWS_MAX_M
 #define ARNORM_XCD_ROWS_MAX_M 4
+#endif
+#ifndef ARNORM_STEP_PUSH_U_FEW
+#define ARNORM_STEP_PUSH_U_FEW 4
 #endif
 // Fragments per thread in flight in a Gather poll whose grid is capped below a thread
 // per fragment.
@@ -373,20 +380,26 @@ int arnorm_push_reduce_norm(const uint16_t *partials, const uint16_t *residual, 
   a.r.poll_all = (uint64_t)tp * M * arn::kRowBytes <= ARNORM_POLL_ALL_MAX_BYTES;
   a.partials = reinterpret_cast<const u32x4 *>(partials);
   a.frags = (uint32_t)M * arn::kRowFrags;
-  constexpr int U = ARNORM_STEP_PUSH_U;
+  const bool few = M <= ARNORM_XCD_ROWS_MAX_M;
+  const int U = few ? ARNORM_STEP_PUSH_U_FEW : ARNORM_STEP_PUSH_U;
   const uint32_t nt = arn::kRowFrags / K;
   a.per_slot = (a.frags + nt * U - 1) / (nt * U);
-  a.xcd_rows = M <= ARNORM_XCD_ROWS_MAX_M;
-  const dim3 grid(tp * a.per_slot + (a.xcd_rows ? (M + 7) / 8 * 8 * K : M * K));
+  a.xcd_rows = few;
+  const dim3 grid(tp * a.per_slot + (few ? (M + 7) / 8 * 8 * K : M * K));
   const bool res = residual != nullptr;
+#define ARNORM_STEP_LAUNCH_U(TPV, KV, UV)                                                                          \
+  return res ? launch(arn::push_reduce_kernel<TPV, true, KV, UV, kPolPush, kPolPoll, kPolRearm, kPolIn, kPolIO>,    \
+                      grid, dim3(nt), stream, a)                                                                   \
+             : launch(arn::push_reduce_kernel<TPV, false, KV, UV, kPolPush, kPolPoll, kPolRearm, kPolIn, kPolIO>,   \
+                      grid, dim3(nt), stream, a);
 #define ARNORM_STEP_LAUNCH_K(TPV, KV)                                                                              \
-  return res ? launch(arn::push_reduce_kernel<TPV, true, KV, U, kPolPush, kPolPoll, kPolRearm, kPolIn, kPolIO>, grid,     \
-                      dim3(nt), stream, a)                                                                         \
-             : launch(arn::push_reduce_kernel<TPV, false, KV, U, kPolPush, kPolPoll, kPolRearm, kPolIn, kPolIO>, grid,    \
-                      dim3(nt), stream, a);
+  if (few) ARNORM_STEP_LAUNCH_U(TPV, KV, ARNORM_STEP_PUSH_U_FEW)                                                   \
+  ARNORM_STEP_LAUNCH_U(TPV, KV, ARNORM_STEP_PUSH_U)
 #define ARNORM_STEP_LAUNCH(TPV)                                                                                   \
   case TPV:                                                                                                      \
-    if (K == 7) ARNORM_STEP_LAUNCH_K(TPV, 7)                                                                     \
+    if (K == 7) {                                                                                                \
+      ARNORM_STEP_LAUNCH_K(TPV, 7)                                                                               \
+    }                                                                                                            \
     ARNORM_STEP_LAUNCH_K(TPV, 14)
   switch (tp) {
     ARNORM_STEP_LAUNCH(2)
@@ -399,6 +412,7 @@ int arnorm_push_reduce_norm(const uint16_t *partials, const uint16_t *residual, 
   }
 #undef ARNORM_STEP_LAUNCH
 #undef ARNORM_STEP_LAUNCH_K
+#undef ARNORM_STEP_LAUNCH_U
   return ARNORM_NOT_SERVED;
 }
 
