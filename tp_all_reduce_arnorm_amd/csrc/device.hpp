@@ -59,9 +59,8 @@ __device__ inline void buf_store(u32x4 v, __amdgpu_buffer_rsrc_t r, uint32_t byt
   __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)byte_off, 0, POL);
 }
 
-// Streaming (non-temporal) 16 B load/store of ordinary inputs and outputs.
+// Streaming (non-temporal) 16 B load of an input read once.
 __device__ inline u32x4 nt_load(const u32x4 *p) { return __builtin_nontemporal_load(p); }
-__device__ inline void nt_store(u32x4 v, u32x4 *p) { __builtin_nontemporal_store(v, p); }
 
 // One re-read of a fragment for a poll loop: four relaxed device-scope atomic
 // loads, which the compiler may neither hoist out of the loop nor merge, and which

@@ -37,7 +37,10 @@ gather_push_kernel(const u32x4 *__restrict__ shard, uint8_t *__restrict__ box, u
 }
 
 // The poll of one row's fragments by workgroup `cta` of `ctas` (cta*256 + t, strided by
-// ctas*256), with copy and re-arm.  Waiting must not steal the producers' bandwidth: a
+// ctas*256), with copy and re-arm.  The copy is stored with the default cache policy, as
+// the ArNorm consumer stores its rows: the last-level cache keeps it for the next reader
+// (a non-temporal store made the one-slot read at M=4096, width 7168, 35.0 against
+// 32.0 us from HBM, and changed nothing at small M).  Waiting must not steal the producers' bandwidth: a
 // wave with unpublished fragments watches one witness (the fragment of its lowest
 // waiting lane; every lane loads the same 16 B) and its lanes re-read their own
 // fragments only once that is published; a small grid (poll_all) re-reads every
@@ -77,7 +80,7 @@ __device__ __forceinline__ void poll_row(uint8_t *row, u32x4 *out_row, uint32_t 
       }
     }
     if (copy && mine && ok) {
-      nt_store(w, out_row + i);
+      out_row[i] = w;
       buf_store<POL_ST>(sentinel4(), r, i * 16u);
     }
   }
@@ -137,7 +140,7 @@ __device__ __forceinline__ void poll_row_batch(uint8_t *row, u32x4 *out_row, uin
 #pragma unroll
       for (int u = 0; u < U; ++u)
         if (idx[u] < row_frags && !((pend >> u) & 1u)) {
-          nt_store(w[u], out_row + idx[u]);
+          out_row[idx[u]] = w[u];
           buf_store<POL_ST>(sentinel4(), r, idx[u] * 16u);
         }
     }
