@@ -125,6 +125,48 @@ def test_graph_replay_alternating_parities(lib, form):
     assert lib.status() == lib.OK
 
 
+@pytest.mark.parametrize("name,m", [("gather_tp8_m32", 4), ("gather_tp8_m32", 32), ("logits", 1)])
+def test_graph_replay_gather(lib, name, m):
+    """gather_push_poll with copy captured twice in one graph (two shard sets into one
+    mailbox: each call leaves it re-armed for the next) and replayed; every replay, with
+    eager work and synchronizations in between, matches the oracle.  M=4 and the logits
+    row are one launch each, M=32 the pair gather_push + gather_poll."""
+    import dataclasses
+
+    import torch
+
+    say(f"[protocol] HIP graph replay, gather_push_poll {name} M={m}")
+    cfg = dataclasses.replace(wl.CONFIGS[name], m=m)
+    gen = wl.gather_shards if name == "gather_tp8_m32" else wl.bf16_shards
+    shards = [gen(cfg), gen(dataclasses.replace(cfg, seed=cfg.seed + 1))]
+    assert not np.array_equal(shards[0], shards[1])
+    gshape = (cfg.cap, cfg.tp * cfg.s)
+    gbox_d = armed_box(gshape)
+    sh_d = [dev32(x) for x in shards]
+    outs = [torch.empty((m, cfg.tp * cfg.s), dtype=torch.int32, device="cuda") for _ in range(2)]
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for x_d, o_d in zip(sh_d, outs):
+            assert lib.gather_push_poll(x_d, gbox_d, out=o_d, copy=True) is True
+    gbox_h = oracle.arm(np.empty(gshape, dtype=np.uint32))
+    wants = []
+    for x in shards:
+        oracle.gather_push(gbox_h, x, 0)
+        wants.append(oracle.gather_poll(gbox_h, m, True))
+    for replay in range(5):
+        for o_d in outs:
+            o_d.fill_(0)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for k in range(2):
+            assert_bits_equal(host32(outs[k]), wants[k], f"replay {replay} call {k} gathered words")
+        assert_bits_equal(host32(gbox_d), gbox_h, f"replay {replay} gather mailbox")
+        _ = torch.ones(1024, device="cuda").sum().item()  # eager work between replays
+    assert lib.status() == lib.OK
+
+
 @pytest.mark.parametrize("m,residual,split", [(4, False, None), (64, True, None), (1, True, None),
                                               (4, False, 14), (64, True, 7)])
 def test_concurrent_consumer_polls_while_producer_pushes(lib, side_streams, m, residual, split):
