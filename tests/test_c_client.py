@@ -156,3 +156,134 @@ def test_c_client_on_gpu(tmp_path):
         want_out, want_res = oracle.arnorm_reduce_norm(box_h, c % 2, cfg.m, None, src.gamma, cfg.eps)
         assert_bits_equal(got[c, 1], want_res, f"call {c} residual_out")
         assert_out_close(got[c, 0], want_out, f"call {c} out")
+
+
+C_GPU_GATHER_TWOSHOT = r"""
+#include <stdio.h>
+#include <stdlib.h>
+#include <stdint.h>
+#include "arnorm.h"
+
+#define CHECK(x) do { if ((x) != hipSuccess) { fprintf(stderr, "HIP error at line %d\n", __LINE__); return 3; } } while (0)
+
+/* Gather and two-shot calls from plain C (hipMalloc, no PyTorch).
+   in.bin: int32 tp, m, cap, s (words per rank), width, calls; then per call the shards
+   uint32 [tp, m, s]; then per call the two-shot partials bf16 [tp, m, width].
+   out.bin: per call the gathered rows uint32 [m, tp*s]; then per call the two-shot
+   rows bf16 [m, width]. */
+int main(int argc, char **argv) {
+  if (argc != 3) return 2;
+  FILE *f = fopen(argv[1], "rb");
+  if (!f) return 2;
+  int32_t h[6];
+  if (fread(h, 4, 6, f) != 6) return 2;
+  const int tp = h[0], m = h[1], cap = h[2], s = h[3], width = h[4], calls = h[5];
+  const size_t sh_n = (size_t)tp * m * s, g_n = (size_t)m * tp * s, p_n = (size_t)tp * m * width, o_n = (size_t)m * width;
+  uint32_t *sh = malloc(sh_n * 4 * calls), *gout = malloc(g_n * 4);
+  uint16_t *parts = malloc(p_n * 2 * calls), *tout = malloc(o_n * 2);
+  if (fread(sh, 4, sh_n * calls, f) != sh_n * calls || fread(parts, 2, p_n * calls, f) != p_n * calls) return 2;
+  fclose(f);
+  const size_t gbox_words = (size_t)cap * tp * s;
+  const size_t recv_words = (size_t)2 * tp * cap * (width / 2), gath_words = (size_t)2 * cap * (width / 2);
+  int32_t *d_sh, *gbox, *d_gout, *recv, *gath;
+  uint16_t *d_parts, *d_tout;
+  CHECK(hipMalloc((void **)&d_sh, sh_n * 4 * calls));
+  CHECK(hipMalloc((void **)&gbox, gbox_words * 4));
+  CHECK(hipMalloc((void **)&d_gout, g_n * 4 * calls));
+  CHECK(hipMalloc((void **)&recv, recv_words * 4));
+  CHECK(hipMalloc((void **)&gath, gath_words * 4));
+  CHECK(hipMalloc((void **)&d_parts, p_n * 2 * calls));
+  CHECK(hipMalloc((void **)&d_tout, o_n * 2 * calls));
+  CHECK(hipMemcpy(d_sh, sh, sh_n * 4 * calls, hipMemcpyHostToDevice));
+  CHECK(hipMemcpy(d_parts, parts, p_n * 2 * calls, hipMemcpyHostToDevice));
+  hipStream_t st;
+  CHECK(hipStreamCreate(&st));
+  if (lamport_arm(gbox, gbox_words, ARNORM_SENTINEL, st) != ARNORM_OK) return 4;
+  if (lamport_arm(recv, recv_words, ARNORM_SENTINEL, st) != ARNORM_OK) return 4;
+  if (lamport_arm(gath, gath_words, ARNORM_SENTINEL, st) != ARNORM_OK) return 4;
+  for (int c = 0; c < calls; ++c) {
+    int rc = gather_push_poll(d_sh + sh_n * c, gbox, d_gout + g_n * c, tp, cap, s, m, 1, st);
+    if (rc != ARNORM_OK) { fprintf(stderr, "gather call %d: %s\n", c, arnorm_strerror(rc)); return 5; }
+    rc = twoshot_push_reduce_read(d_parts + p_n * c, recv, gath, d_tout + o_n * c, 2, tp, cap, width, c % 2, m, st);
+    if (rc != ARNORM_OK) { fprintf(stderr, "two-shot call %d: %s\n", c, arnorm_strerror(rc)); return 5; }
+  }
+  int status = -1;
+  if (arnorm_status(&status, st) != ARNORM_OK || status != ARNORM_OK) return 6;
+  int32_t *chk[3] = {gbox, recv, gath};
+  const size_t chk_n[3] = {gbox_words, recv_words, gath_words};
+  for (int b = 0; b < 3; ++b) {
+    int32_t *hb = malloc(chk_n[b] * 4);
+    CHECK(hipMemcpy(hb, chk[b], chk_n[b] * 4, hipMemcpyDeviceToHost));
+    for (size_t i = 0; i < chk_n[b]; ++i)
+      if ((uint32_t)hb[i] != ARNORM_SENTINEL) { fprintf(stderr, "buffer %d word %zu not re-armed\n", b, i); return 7; }
+    free(hb);
+  }
+  FILE *o = fopen(argv[2], "wb");
+  if (!o) return 2;
+  for (int c = 0; c < calls; ++c) {
+    CHECK(hipMemcpy(gout, d_gout + g_n * c, g_n * 4, hipMemcpyDeviceToHost));
+    fwrite(gout, 4, g_n, o);
+  }
+  for (int c = 0; c < calls; ++c) {
+    CHECK(hipMemcpy(tout, d_tout + o_n * c, o_n * 2, hipMemcpyDeviceToHost));
+    fwrite(tout, 2, o_n, o);
+  }
+  fclose(o);
+  printf("c gpu client: %d gather and %d two-shot calls ok\n", calls, calls);
+  return 0;
+}
+"""
+
+
+@pytest.mark.gpu
+def test_c_client_gather_and_twoshot_on_gpu(tmp_path):
+    """A plain C program (hipMalloc, no PyTorch) runs one-launch Gather calls (TP=8, M=4,
+    S=896 words) and one-launch two-shot calls (TP=8, M=4, width 7168) over two parities;
+    its outputs match the oracle and it finds every mailbox re-armed."""
+    import dataclasses
+
+    import numpy as np
+
+    import oracle
+    from tests.gpu_util import assert_bits_equal, say
+    from tp_all_reduce_arnorm_amd import workloads as wl
+
+    lib = os.path.join(LIB_DIR, "libarnorm.so")
+    if not os.path.exists(lib):
+        pytest.skip("libarnorm.so not built")
+    say("[c client] one-launch Gather and two-shot calls from C on the GPU")
+    gcfg = dataclasses.replace(wl.CONFIGS["gather_tp8_m32"], m=4)
+    tcfg = wl.CONFIGS["tp8_m4"]
+    width, calls = 7168, 4
+    shards = [wl.gather_shards(dataclasses.replace(gcfg, seed=gcfg.seed + c)) for c in range(calls)]
+    src = wl.ArNormInputs(tcfg)
+    parts = [src.partials() for _ in range(calls)]
+    with open(tmp_path / "in.bin", "wb") as f:
+        f.write(np.array([gcfg.tp, gcfg.m, gcfg.cap, gcfg.s, width, calls], dtype=np.int32).tobytes())
+        for x in shards:
+            f.write(np.ascontiguousarray(x, dtype=np.uint32).tobytes())
+        for p in parts:
+            f.write(np.ascontiguousarray(p, dtype=np.uint16).tobytes())
+    (tmp_path / "client.c").write_text(C_GPU_GATHER_TWOSHOT)
+    exe = tmp_path / "client"
+    subprocess.run(["gcc", "-std=c11", "-O1", "-Wall", "-Werror", "-D__HIP_PLATFORM_AMD__", f"-I{ROOT}/include",
+                    "-I/opt/rocm/include", str(tmp_path / "client.c"), "-o", str(exe), f"-L{LIB_DIR}", "-larnorm",
+                    "-L/opt/rocm/lib", "-lamdhip64", f"-Wl,-rpath,{LIB_DIR}", "-Wl,-rpath,/opt/rocm/lib"],
+                   check=True, capture_output=True, text=True, timeout=120)
+    r = subprocess.run([str(exe), str(tmp_path / "in.bin"), str(tmp_path / "out.bin")], capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode == 0, r.stdout + r.stderr
+    raw = np.fromfile(tmp_path / "out.bin", dtype=np.uint8)
+    g_bytes = calls * gcfg.m * gcfg.tp * gcfg.s * 4
+    assert raw.size == g_bytes + calls * tcfg.m * width * 2
+    got_g = raw[:g_bytes].view(np.uint32).reshape(calls, gcfg.m, gcfg.tp * gcfg.s)
+    got_t = raw[g_bytes:].view(np.uint16).reshape(calls, tcfg.m, width)
+    gbox_h = oracle.arm(np.empty((gcfg.cap, gcfg.tp * gcfg.s), dtype=np.uint32))
+    recv_h = oracle.arm(np.empty((2, tcfg.tp, tcfg.cap, width // 2), dtype=np.uint32))
+    gath_h = oracle.arm(np.empty((2, 1, tcfg.cap, width // 2), dtype=np.uint32))
+    for c in range(calls):
+        oracle.gather_push(gbox_h, shards[c], 0)
+        assert_bits_equal(got_g[c], oracle.gather_poll(gbox_h, gcfg.m, True), f"call {c} gathered words")
+        oracle.twoshot_push(recv_h, parts[c], c % 2, 0)
+        oracle.twoshot_reduce(recv_h, gath_h, c % 2, tcfg.m)
+        assert_bits_equal(got_t[c], oracle.twoshot_read(gath_h, c % 2, tcfg.m), f"call {c} two-shot rows")
