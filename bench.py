@@ -78,7 +78,7 @@ def committed_traffic(kernel_key):
     return entry.get("bytes_per_launch")
 
 
-def time_latency(lib, torch, steps, warmup, chunk=50, one_launch=True, m=None):
+def time_latency(lib, torch, steps, warmup, chunk=200, one_launch=True, m=None):
     """Seconds for `steps` stand-in calls at TP=8, M=4 (or M=m), no residual,
     graph-replayed.  one_launch: arnorm_push_reduce_norm (every rank's push and the
     consumer in one launch where the slots fit 1 MiB, else the pair); else the pair
@@ -199,7 +199,7 @@ def gather_bytes(tp, m, s, copy=True):
     return 2 * words * 4, (3 if copy else 1) * words * 4
 
 
-def time_gather(lib, torch, calls=1000, chunk=50, name="gather_tp8_m32", one_launch=True, m=None):
+def time_gather(lib, torch, calls=2000, chunk=200, name="gather_tp8_m32", one_launch=True, m=None):
     """µs per Gather call, graph-replayed: gather_push_poll (every rank's push and the
     copying poll, one launch for calls within 1 MiB), or with one_launch False the pair
     gather_push + gather_poll.  gather_tp8_m32 is TP=8, M=32, S=896; ctx and logits are the
@@ -247,7 +247,7 @@ def twoshot_bytes(tp, m, width=HIDDEN):
     return 2 * tp * m * row + m * row, 3 * m * row
 
 
-def time_twoshot(lib, torch, calls=1000, chunk=50, launches=20, modes=("cold", "warm")):
+def time_twoshot(lib, torch, calls=2000, chunk=200, launches=20, modes=("cold", "warm")):
     """Two-shot stand-in: µs per graph-replayed call at TP=8, M=4 (push of 8 slots,
     owner's reduce, read of the gather row) as one twoshot_push_reduce_read launch and
     as the three launches, and the reduce / read kernels at M=4096 (cold and warm, as
@@ -507,12 +507,12 @@ def summarize_profiles(outdir):
             ("roof", "ArNorm kernels at TP=8, M=4096, residual: one push of 8 slots + one consumer launch, "
                      "23 times, each launch after a 1 GiB read-only pass (torch's float32 sum) that evicts the "
                      "last-level cache", "arnorm_tp8_m4096_kernel_stats.md"),
-            ("gather", "Gather at TP=8, S=896 words, cap=64, HIP-graph replay: 1000 gather_push_poll calls "
+            ("gather", "Gather at TP=8, S=896 words, cap=64, HIP-graph replay: 2000 gather_push_poll calls "
                        "at M=32 (917504 B, so run as the pair gather_push of 8 slots + gather_poll with "
-                       "copy), 1000 calls of that pair, then 1000 one-launch gather_push_poll calls at M=4",
+                       "copy), 2000 calls of that pair, then 2000 one-launch gather_push_poll calls at M=4",
              "gather_tp8_m32_s896_kernel_stats.md"),
-            ("twoshot", "Two-shot all-reduce stand-in (owners = 1): TP=8, M=4 graph-replayed calls, 1000 as "
-                        "one twoshot_push_reduce_read launch each, then 1000 as the three launches (push, "
+            ("twoshot", "Two-shot all-reduce stand-in (owners = 1): TP=8, M=4 graph-replayed calls, 2000 as "
+                        "one twoshot_push_reduce_read launch each, then 2000 as the three launches (push, "
                         "owner's reduce, read), then 23 calls at TP=8, M=4096 whose reduce and read each follow "
                         "a 1 GiB read-only pass (torch's float32 sum) that evicts the last-level cache",
              "twoshot_tp8_kernel_stats.md")):
