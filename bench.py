@@ -481,13 +481,33 @@ def _short(name):
     return name.split("(")[0].replace("void ", "")
 
 
-def _stats_table(path):
+def _trace_medians(path):
+    """Median duration in ns per kernel name from a rocprofv3 kernel-trace CSV (None if
+    the file is absent)."""
+    import csv
+
+    if not os.path.exists(path):
+        return None
+    durs = {}
+    with open(path) as f:
+        rd = csv.DictReader(f)
+        if not {"Kernel_Name", "Start_Timestamp", "End_Timestamp"} <= set(rd.fieldnames or ()):
+            return None
+        for r in rd:
+            durs.setdefault(r["Kernel_Name"], []).append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+    return {k: float(np.median(v)) for k, v in durs.items()}
+
+
+def _stats_table(path, trace_path=None):
     import csv
 
     rows = list(csv.DictReader(open(path)))
-    out = ["| kernel | calls | average µs | min µs | max µs | share of GPU time |", "|---|---|---|---|---|---|"]
+    med = _trace_medians(trace_path) if trace_path else None
+    head = "| kernel | calls | average µs | " + ("median µs | " if med else "") + "min µs | max µs | share of GPU time |"
+    out = [head, "|---" * (head.count("|") - 1) + "|"]
     for r in rows:
-        out.append(f"| `{_short(r['Name'])}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+        m = f"{med[r['Name']] / 1e3:.2f} | " if med and r["Name"] in med else ("– | " if med else "")
+        out.append(f"| `{_short(r['Name'])}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | {m}"
                    f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | {float(r['Percentage']):.1f} % |")
     return rows, "\n".join(out)
 
@@ -518,7 +538,8 @@ def summarize_profiles(outdir):
              "twoshot_tp8_kernel_stats.md")):
         if not os.path.exists(os.path.join(outdir, f"prof_{key}", f"{key}_kernel_stats.csv")):
             continue
-        rows, table = _stats_table(os.path.join(outdir, f"prof_{key}", f"{key}_kernel_stats.csv"))
+        rows, table = _stats_table(os.path.join(outdir, f"prof_{key}", f"{key}_kernel_stats.csv"),
+                                   os.path.join(outdir, f"prof_{key}", f"{key}_kernel_trace.csv"))
         sha = _profiled_sha(os.path.join(outdir, f"prof_{key}.log"))
         with open(os.path.join(prof, fname), "w") as f:
             f.write(f"# rocprofv3 kernel statistics: {title}\n\n"

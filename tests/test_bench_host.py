@@ -68,3 +68,19 @@ def test_committed_profiles_name_their_command():
         with open(os.path.join(ROOT, "profiles", n)) as f:
             text = f.read()
         assert "rocprofv3" in text and "python bench.py" in text and "sha256" in text, n
+
+
+def test_profile_table_median_from_trace(tmp_path):
+    """The profile summary's median column comes from the per-dispatch kernel trace."""
+    stats = tmp_path / "k_kernel_stats.csv"
+    stats.write_text('"Name","Calls","TotalDurationNs","AverageNs","Percentage","MinNs","MaxNs","StdDev"\n'
+                     '"void arn::k(int)","3","9000","3000","100.0","1000","5000","0"\n')
+    trace = tmp_path / "k_kernel_trace.csv"
+    trace.write_text('"Kernel_Name","Start_Timestamp","End_Timestamp"\n'
+                     '"void arn::k(int)","100","1100"\n"void arn::k(int)","2000","7000"\n'
+                     '"void arn::k(int)","9000","12000"\n')
+    _, table = bench._stats_table(str(stats), str(trace))
+    assert "median µs" in table
+    assert "| `arn::k` | 3 | 3.00 | 3.00 | 1.00 | 5.00 | 100.0 % |" in table
+    _, plain = bench._stats_table(str(stats), str(tmp_path / "absent.csv"))
+    assert "median" not in plain and "| `arn::k` | 3 | 3.00 | 1.00 | 5.00 | 100.0 % |" in plain
