@@ -81,6 +81,8 @@ def _check(fn, code):
 def _stream(stream):
     if stream is None:
         stream = torch.cuda.current_stream()
+    elif stream.device.index != torch.cuda.current_device():
+        raise ValueError(f"stream is on {stream.device}, the current device is cuda:{torch.cuda.current_device()}")
     return ctypes.c_void_p(stream.cuda_stream)
 
 
@@ -97,6 +99,9 @@ def _ptr(t, nbytes_per_elem=None, what="tensor"):
         return None
     if not t.is_cuda or not t.is_contiguous():
         raise ValueError(f"{what} must be a contiguous device tensor")
+    if t.device.index != torch.cuda.current_device():
+        # the kernels run on the current device, which must own every buffer they touch
+        raise ValueError(f"{what} is on {t.device}, the current device is cuda:{torch.cuda.current_device()}")
     if nbytes_per_elem is not None and t.element_size() != nbytes_per_elem:
         raise ValueError(f"{what} must have {nbytes_per_elem}-byte elements, got {t.dtype}")
     return ctypes.c_void_p(t.data_ptr())
