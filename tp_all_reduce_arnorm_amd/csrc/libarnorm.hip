@@ -46,8 +46,20 @@ std::atomic<int> g_poll_mode{0};   // Gather polls: 0 = automatic, 1 = re-read a
 #ifndef ARNORM_POL_IO
 #define ARNORM_POL_IO 0
 #endif
+// Fragments per thread of the producer kernel (arnorm_push, twoshot_push): 2 while a
+// slot's rows total at most ARNORM_PUSH_SMALL_BYTES, else 4.  Measured on MI355X at
+// TP=8 (us per call of the pair push + consumer, graph-replayed, U = 1 / 2 / 4 / 8):
+// M=16 5.12 / 5.12-5.13 / 5.21-5.22 / 5.47, M=32 5.74 / 5.53-5.54 / 5.63 / 5.80,
+// M=64 7.36 / 7.29-7.30 / 7.53 / 7.50; the push of 8 slots at M=4096 from HBM:
+// 138-140 / 138-139 / 134 / 137-138 us.
 #ifndef ARNORM_PUSH_U
 #define ARNORM_PUSH_U 4
+#endif
+#ifndef ARNORM_PUSH_U_SMALL
+#define ARNORM_PUSH_U_SMALL 2
+#endif
+#ifndef ARNORM_PUSH_SMALL_BYTES
+#define ARNORM_PUSH_SMALL_BYTES (1u << 20)
 #endif
 // Largest M for which a row is split over 14 (or 7) workgroups when a norm box is given.
 // Measured on MI355X, TP=8, stand-in call (push + consumer): 7 workgroups per row beat
@@ -256,6 +268,19 @@ int launch_poll(uint8_t *box, u32x4 *out, uint32_t row_frags, int M, int copy, h
                 stream, box, out, row_frags, l.ctas, copy ? 1 : 0, spin, poll_all);
 }
 
+// The producer kernel over `frags` fragments per slot of nslots slots.
+int launch_push(const void *partial, uint8_t *first, size_t slot_stride, uint32_t frags, int nslots,
+                hipStream_t stream) {
+  const bool small = (uint64_t)frags * 16u <= ARNORM_PUSH_SMALL_BYTES;
+  const uint32_t per_wg = 256u * (small ? ARNORM_PUSH_U_SMALL : ARNORM_PUSH_U);
+  const dim3 grid(std::max(1u, std::min((frags + per_wg - 1) / per_wg, 1024u)), (unsigned)nslots);
+  const u32x4 *src = reinterpret_cast<const u32x4 *>(partial);
+  if (small)
+    return launch(arn::push_kernel<ARNORM_PUSH_U_SMALL, kPolPush>, grid, dim3(256), stream, src, first, slot_stride,
+                  frags);
+  return launch(arn::push_kernel<ARNORM_PUSH_U, kPolPush>, grid, dim3(256), stream, src, first, slot_stride, frags);
+}
+
 }  // namespace
 
 extern "C" {
@@ -277,13 +302,8 @@ int arnorm_push(const uint16_t *partial, int32_t *mailbox, int parities, int tp,
   if (rc != ARNORM_OK) return rc;
   if (rank < 0 || nslots < 1 || rank + nslots > tp) return ARNORM_BAD_ARG;
   if (!aligned16(partial) || !aligned16(mailbox)) return ARNORM_BAD_ARG;
-  constexpr int U = ARNORM_PUSH_U;
-  const uint32_t frags = (uint32_t)M * arn::kRowFrags;
-  const uint32_t want = (frags + 256 * U - 1) / (256 * U);
-  const dim3 grid(std::max(1u, std::min(want, 1024u)), (unsigned)nslots);
   uint8_t *first = parity_base(mailbox, parity, tp, cap) + (size_t)rank * cap * arn::kRowBytes;
-  return launch(arn::push_kernel<U, kPolPush>, grid, dim3(256), stream, reinterpret_cast<const u32x4 *>(partial),
-                first, (size_t)cap * arn::kRowBytes, frags);
+  return launch_push(partial, first, (size_t)cap * arn::kRowBytes, (uint32_t)M * arn::kRowFrags, nslots, stream);
 }
 
 int arnorm_reduce_norm(const uint16_t *partial, const uint16_t *residual, const uint16_t *gamma, uint16_t *out,
@@ -493,14 +513,10 @@ int twoshot_push(const uint16_t *partial, int32_t *recv, int parities, int tp, i
   if (rc != ARNORM_OK) return rc;
   if (rank < 0 || nslots < 1 || rank + nslots > tp) return ARNORM_BAD_ARG;
   if (!aligned16(partial) || !aligned16(recv)) return ARNORM_BAD_ARG;
-  constexpr int U = ARNORM_PUSH_U;
   const size_t row_bytes = (size_t)width * 2;
-  const uint32_t frags = (uint32_t)((size_t)M * row_bytes / 16);
-  const uint32_t want = (frags + 256 * U - 1) / (256 * U);
-  const dim3 grid(std::max(1u, std::min(want, 1024u)), (unsigned)nslots);
   uint8_t *first = reinterpret_cast<uint8_t *>(recv) + ((size_t)parity * tp + rank) * cap * row_bytes;
-  return launch(arn::push_kernel<U, kPolPush>, grid, dim3(256), stream, reinterpret_cast<const u32x4 *>(partial),
-                first, (size_t)cap * row_bytes, frags);
+  return launch_push(partial, first, (size_t)cap * row_bytes, (uint32_t)((size_t)M * row_bytes / 16), nslots,
+                     stream);
 }
 
 int twoshot_reduce(int32_t *recv, int32_t *gather, int parities, int tp, int cap, int width, int parity, int M,
