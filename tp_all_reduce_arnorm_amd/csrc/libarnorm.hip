@@ -46,20 +46,29 @@ std::atomic<int> g_poll_mode{0};   // Gather polls: 0 = automatic, 1 = re-read a
 #ifndef ARNORM_POL_IO
 #define ARNORM_POL_IO 0
 #endif
-// Fragments per thread of the producer kernel (arnorm_push, twoshot_push): 2 while a
-// slot's rows total at most ARNORM_PUSH_SMALL_BYTES, else 4.  Measured on MI355X at
-// TP=8 (us per call of the pair push + consumer, graph-replayed, U = 1 / 2 / 4 / 8):
-// M=16 5.12 / 5.12-5.13 / 5.21-5.22 / 5.47, M=32 5.74 / 5.53-5.54 / 5.63 / 5.80,
-// M=64 7.36 / 7.29-7.30 / 7.53 / 7.50; the push of 8 slots at M=4096 from HBM:
-// 138-140 / 138-139 / 134 / 137-138 us.
+// Producer kernel (arnorm_push, twoshot_push) layout: 2 fragments per thread while a
+// slot's rows total at most ARNORM_PUSH_SMALL_BYTES, else one fragment per thread with
+// up to ARNORM_PUSH_MAX_GRID workgroups per slot (larger pushes loop).  Measured on
+// MI355X at TP=8.  Small: us per call of the pair push + consumer, graph-replayed,
+// fragments per thread 1 / 2 / 4 / 8: M=16 5.12 / 5.12-5.13 / 5.21-5.22 / 5.47, M=32
+// 5.74 / 5.53-5.54 / 5.63 / 5.80, M=64 7.36 / 7.29-7.30 / 7.53 / 7.50.  Large: the push of
+// 8 slots at M=4096, us from HBM / right after the consumer / push + consumer as the
+// call repeats: 4 per thread, at most 1024 workgroups 134.4-134.7 / 155.2-157.4 /
+// 320.0-323.8; 2 per thread, 7168 workgroups 128.5-128.8 / 150.9-151.5 / 316.0-316.9;
+// 1 per thread, 14336 workgroups 134.1-134.2 / 144.7-145.4 / 309.8-310.2; 1 per thread,
+// at most 8192 131.3-131.7 / 147.4-148.1 / 312.2-312.6, at most 4096 134.1-134.6 /
+// 157.9-158.6 / 322.7-323.0.
 #ifndef ARNORM_PUSH_U
-#define ARNORM_PUSH_U 4
+#define ARNORM_PUSH_U 1
 #endif
 #ifndef ARNORM_PUSH_U_SMALL
 #define ARNORM_PUSH_U_SMALL 2
 #endif
 #ifndef ARNORM_PUSH_SMALL_BYTES
 #define ARNORM_PUSH_SMALL_BYTES (1u << 20)
+#endif
+#ifndef ARNORM_PUSH_MAX_GRID
+#define ARNORM_PUSH_MAX_GRID 16384
 #endif
 // Largest M for which a row is split over 14 (or 7) workgroups when a norm box is given.
 // Measured on MI355X, TP=8, stand-in call (push + consumer): 7 workgroups per row beat
@@ -273,7 +282,8 @@ int launch_push(const void *partial, uint8_t *first, size_t slot_stride, uint32_
                 hipStream_t stream) {
   const bool small = (uint64_t)frags * 16u <= ARNORM_PUSH_SMALL_BYTES;
   const uint32_t per_wg = 256u * (small ? ARNORM_PUSH_U_SMALL : ARNORM_PUSH_U);
-  const dim3 grid(std::max(1u, std::min((frags + per_wg - 1) / per_wg, 1024u)), (unsigned)nslots);
+  const dim3 grid(std::max(1u, std::min((frags + per_wg - 1) / per_wg, (uint32_t)ARNORM_PUSH_MAX_GRID)),
+                  (unsigned)nslots);
   const u32x4 *src = reinterpret_cast<const u32x4 *>(partial);
   if (small)
     return launch(arn::push_kernel<ARNORM_PUSH_U_SMALL, kPolPush>, grid, dim3(256), stream, src, first, slot_stride,
