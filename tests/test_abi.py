@@ -232,3 +232,19 @@ def test_binding_mirrors_the_abi():
               "gather_poll", "gather_push_poll", "twoshot_push", "twoshot_reduce", "twoshot_read",
               "twoshot_push_reduce_read"):
         assert callable(getattr(_lib, n))
+
+
+def test_binding_fails_loudly_without_the_library(tmp_path):
+    """The binding has no fallback: imported from a package directory where libarnorm.so
+    was never built, it raises ImportError naming the build command."""
+    import shutil
+    import sys
+
+    pkg = tmp_path / "unbuilt_pkg"
+    pkg.mkdir()
+    (pkg / "__init__.py").write_text("")
+    shutil.copy(os.path.join(ROOT, "tp_all_reduce_arnorm_amd", "_lib.py"), pkg / "_lib.py")
+    r = subprocess.run([sys.executable, "-c", "import unbuilt_pkg._lib"], cwd=str(tmp_path), capture_output=True,
+                       text=True, timeout=300)
+    assert r.returncode != 0
+    assert "ImportError" in r.stderr and "is not built" in r.stderr
