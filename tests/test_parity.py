@@ -575,6 +575,33 @@ def test_max_rows_and_single_row(lib):
         run_call(lib, box_d, box_h, p, res, dev16(gamma), gamma, 0)
 
 
+@pytest.mark.parametrize("m", [73, 74])
+def test_push_layout_threshold(lib, m):
+    """M=73 and M=74 at TP=8: a slot's rows just under and just over 1 MiB, where the
+    producer switches from 2 fragments per thread to one (and the two-slot pushes of
+    ranks 0-1 and the six of ranks 2-7 with it), with the one call beside the pair."""
+    import dataclasses
+
+    say(f"[parity] push layout threshold M={m}")
+    cfg = dataclasses.replace(wl.CONFIGS["tp8_m64"], m=m, cap=80, sentinel_frac=0.05)
+    src = wl.ArNormInputs(cfg)
+    shape = (2, 8, cfg.cap, W // 2)
+    box_d, box_h = armed_box(shape), oracle.arm(np.empty(shape, dtype=np.uint32))
+    g_d = dev16(src.gamma)
+    p, r = src.call()
+    run_call(lib, box_d, box_h, p, r, g_d, src.gamma, 0, pushes=[(0, 2), (2, 6)])
+    p, r = src.call()
+    out_d, rout_d = empty16((m, W)), empty16((m, W))
+    nbox = norm_box_for(shape)
+    assert lib.arnorm_push_reduce_norm(dev16(p), dev16(r), g_d, box_d, 1, EPS, out_d, rout_d, norm_box=nbox) is True
+    oracle.arnorm_push(box_h, p, 1, 0)
+    want_out, want_res = oracle.arnorm_reduce_norm(box_h, 1, m, r, src.gamma, EPS)
+    assert_bits_equal(host16(rout_d), want_res, "one-call residual_out")
+    assert_out_close(host16(out_d), want_out)
+    assert_bits_equal(host32(box_d), box_h, "mailbox")
+    assert lib.status() == lib.OK
+
+
 def test_in_place_residual(lib):
     say("[parity] residual_out == residual")
     cfg = wl.CONFIGS["tp8_m64"]
