@@ -498,6 +498,30 @@ def _trace_medians(path):
     return {k: float(np.median(v)) for k, v in durs.items()}
 
 
+def _shape_table(trace_path):
+    """Per launch shape (kernel, grid, workgroup) of this library's kernels: calls, median
+    and average duration, from a rocprofv3 kernel-trace CSV; None without one."""
+    import csv
+
+    if not trace_path or not os.path.exists(trace_path):
+        return None
+    durs = {}
+    with open(trace_path) as f:
+        rd = csv.DictReader(f)
+        need = {"Kernel_Name", "Start_Timestamp", "End_Timestamp", "Grid_Size_X", "Workgroup_Size_X"}
+        if not need <= set(rd.fieldnames or ()):
+            return None
+        for r in rd:
+            if "arn::" not in r["Kernel_Name"]:
+                continue
+            key = (_short(r["Kernel_Name"]), int(r["Grid_Size_X"]), int(r["Workgroup_Size_X"]))
+            durs.setdefault(key, []).append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+    out = ["| kernel | grid (threads) | workgroup | calls | median µs | average µs |", "|---|---|---|---|---|---|"]
+    for (name, grid, wg), v in sorted(durs.items(), key=lambda kv: (kv[0][0], kv[0][1])):
+        out.append(f"| `{name}` | {grid} | {wg} | {len(v)} | {np.median(v) / 1e3:.2f} | {np.mean(v) / 1e3:.2f} |")
+    return "\n".join(out)
+
+
 def _stats_table(path, trace_path=None):
     import csv
 
@@ -523,7 +547,8 @@ def summarize_profiles(outdir):
             ("lat", "Stand-in ArNorm call at TP=8, M=4, no residual, HIP-graph replay: 2000 calls of one "
                     "arnorm_push_reduce_norm launch each (the 8 ranks' pushes and the consumer, rows split "
                     "7 ways through the norm box), then 2000 calls as the pair arnorm_push of 8 slots + "
-                    "arnorm_reduce_norm", "arnorm_tp8_m4_kernel_stats.md"),
+                    "arnorm_reduce_norm, then 2000 arnorm_push_reduce_norm calls at M=1 (one launch) and "
+                    "2000 at M=64 (the pair)", "arnorm_tp8_m4_kernel_stats.md"),
             ("roof", "ArNorm kernels at TP=8, M=4096, residual: one push of 8 slots + one consumer launch, "
                      "23 times, each launch after a 1 GiB read-only pass (torch's float32 sum) that evicts the "
                      "last-level cache", "arnorm_tp8_m4096_kernel_stats.md"),
@@ -541,10 +566,14 @@ def summarize_profiles(outdir):
         rows, table = _stats_table(os.path.join(outdir, f"prof_{key}", f"{key}_kernel_stats.csv"),
                                    os.path.join(outdir, f"prof_{key}", f"{key}_kernel_trace.csv"))
         sha = _profiled_sha(os.path.join(outdir, f"prof_{key}.log"))
+        shapes = _shape_table(os.path.join(outdir, f"prof_{key}", f"{key}_kernel_trace.csv")) if key == "lat" else None
         with open(os.path.join(prof, fname), "w") as f:
             f.write(f"# rocprofv3 kernel statistics: {title}\n\n"
                     f"Command, from the repository root on one MI355X:\n\n    {PROFILE_COMMANDS[key]}\n\n"
                     f"Kernel sources sha256[:16] = `{sha}`.\n\n{table}\n")
+            if shapes:
+                f.write(f"\nThe library's kernels by launch shape (grid size in threads; M=1, 4 and 64 launch "
+                        f"different grids):\n\n{shapes}\n")
 
     def counters(key):
         path = os.path.join(outdir, f"pmc_{key}", f"{key}_counter_collection.csv")
@@ -625,8 +654,11 @@ def main():
     if args.mode == "latency":
         elapsed = time_latency(lib, torch, args.steps, args.warmup)
         pair = time_latency(lib, torch, args.steps, args.warmup, one_launch=False)
+        m_us = {f"m{m}_us_per_call": time_latency(lib, torch, args.steps, args.warmup, m=m) / args.steps * 1e6
+                for m in (1, 64)}
         print(json.dumps({"mode": "latency", "us_per_call": elapsed / args.steps * 1e6,
-                          "two_launch_us_per_call": pair / args.steps * 1e6, "sources_sha": sha}), flush=True)
+                          "two_launch_us_per_call": pair / args.steps * 1e6, **m_us, "sources_sha": sha}),
+              flush=True)
         return
     if args.mode == "roofline":
         _, t = time_roofline(lib, torch, modes=("cold",))

@@ -84,3 +84,16 @@ def test_profile_table_median_from_trace(tmp_path):
     assert "| `arn::k` | 3 | 3.00 | 3.00 | 1.00 | 5.00 | 100.0 % |" in table
     _, plain = bench._stats_table(str(stats), str(tmp_path / "absent.csv"))
     assert "median" not in plain and "| `arn::k` | 3 | 3.00 | 1.00 | 5.00 | 100.0 % |" in plain
+
+
+def test_profile_shape_table(tmp_path):
+    """Launch shapes of the library's kernels are told apart by grid size."""
+    trace = tmp_path / "lat_kernel_trace.csv"
+    trace.write_text('"Kernel_Name","Start_Timestamp","End_Timestamp","Grid_Size_X","Workgroup_Size_X"\n'
+                     '"void arn::k(int)","0","1000","128","128"\n"void arn::k(int)","0","3000","128","128"\n'
+                     '"void arn::k(int)","0","5000","896","128"\n"void at::native::other()","0","9","1","1"\n')
+    table = bench._shape_table(str(trace))
+    assert "| `arn::k` | 128 | 128 | 2 | 2.00 | 2.00 |" in table
+    assert "| `arn::k` | 896 | 128 | 1 | 5.00 | 5.00 |" in table
+    assert "other" not in table
+    assert bench._shape_table(str(tmp_path / "absent.csv")) is None
