@@ -353,3 +353,164 @@ def test_three_host_threads_three_mailboxes(lib, side_streams):
     assert_bits_equal(host32(g_box), g_h, "Gather mailbox")
     assert_bits_equal(host32(ts_recv), recv_h, "two-shot slots")
     assert_bits_equal(host32(ts_gath), gath_h, "two-shot gather row")
+
+
+def test_concurrent_consumer_first_m4096(lib, side_streams):
+    """The whole-row consumer at M = 4096 (TP = 8, residual) launched first on its own
+    stream, the push of all 8 slots later and delayed on another: the consumer's grid is
+    capped at what the GPU holds at once with room left for the producer, so every poll
+    ends within a bounded spin and every row matches the oracle."""
+    import torch
+
+    say("[protocol] concurrent consumer-first M=4096")
+    old = lib.get_spin_limit()
+    lib.set_spin_limit(1 << 18)
+    try:
+        cfg = wl.CONFIGS["tp8_m4096"]
+        src = wl.ArNormInputs(cfg)
+        p, r = src.call()
+        box_d = armed_box((1, 8, cfg.cap, W // 2))
+        p_d, r_d, g_d = dev16(p), dev16(r), dev16(src.gamma)
+        out_d, rout_d = empty16((cfg.m, W)), empty16((cfg.m, W))
+        cur = torch.cuda.current_stream()
+        s_prod, s_cons = side_streams[0], side_streams[1]
+        torch.cuda.synchronize()
+        s_prod.wait_stream(cur)
+        s_cons.wait_stream(cur)
+        with torch.cuda.stream(s_cons):
+            assert lib.arnorm_reduce_norm(r_d, g_d, box_d, 0, EPS, out_d, rout_d) is True
+        with torch.cuda.stream(s_prod):
+            torch.cuda._sleep(200000)
+            assert lib.arnorm_push(p_d, box_d, 0, 0) is True
+        cur.wait_stream(s_prod)
+        cur.wait_stream(s_cons)
+        torch.cuda.synchronize()
+        assert lib.status() == lib.OK, "a poll timed out: the consumer's grid kept the producer out"
+        assert bool((box_d == torch.tensor(-(1 << 31), dtype=torch.int32, device="cuda")).all())
+        del box_d, p_d, r_d
+        got_out, got_res = host16(out_d), host16(rout_d)
+        blk = 1024
+        for r0 in range(0, cfg.m, blk):
+            box_h = oracle.arm(np.empty((1, 8, blk, W // 2), dtype=np.uint32))
+            oracle.arnorm_push(box_h, p[:, r0:r0 + blk], 0, 0)
+            want_out, want_res = oracle.arnorm_reduce_norm(box_h, 0, blk, r[r0:r0 + blk], src.gamma, EPS)
+            assert_bits_equal(got_res[r0:r0 + blk], want_res, f"residual_out rows {r0}..")
+            assert_out_close(got_out[r0:r0 + blk], want_out, f"out rows {r0}..")
+    finally:
+        lib.set_spin_limit(old)
+
+
+def test_concurrent_gather_consumer_first_m4096(lib, side_streams):
+    """gather_poll over 4096 rows of TP=8 x 896 words (7.3 M fragments, 4 per thread in
+    flight over at most 1024 workgroups) launched before its push: every word and the
+    mailbox must match the oracle and no poll may time out."""
+    import dataclasses
+
+    import torch
+
+    say("[protocol] concurrent gather consumer-first M=4096")
+    old = lib.get_spin_limit()
+    lib.set_spin_limit(1 << 18)
+    try:
+        cfg = dataclasses.replace(wl.CONFIGS["gather_tp8_m32"], m=4096, cap=4096, seed=77)
+        shards = wl.gather_shards(cfg)
+        gshape = (cfg.cap, cfg.tp * cfg.s)
+        gbox_d = armed_box(gshape)
+        sh_d = dev32(shards)
+        out_d = torch.empty((cfg.m, cfg.tp * cfg.s), dtype=torch.int32, device="cuda")
+        cur = torch.cuda.current_stream()
+        s_prod, s_cons = side_streams[0], side_streams[1]
+        torch.cuda.synchronize()
+        s_prod.wait_stream(cur)
+        s_cons.wait_stream(cur)
+        with torch.cuda.stream(s_cons):
+            assert lib.gather_poll(gbox_d, cfg.tp, cfg.m, out=out_d, copy=True) is True
+        with torch.cuda.stream(s_prod):
+            torch.cuda._sleep(200000)
+            assert lib.gather_push(sh_d, gbox_d, cfg.tp, 0) is True
+        cur.wait_stream(s_prod)
+        cur.wait_stream(s_cons)
+        torch.cuda.synchronize()
+        assert lib.status() == lib.OK
+        gbox_h = oracle.arm(np.empty(gshape, dtype=np.uint32))
+        oracle.gather_push(gbox_h, shards, 0)
+        assert_bits_equal(host32(out_d), oracle.gather_poll(gbox_h, cfg.m, True), "gathered words")
+        assert_bits_equal(host32(gbox_d), gbox_h, "gather mailbox")
+    finally:
+        lib.set_spin_limit(old)
+
+
+def test_concurrent_twoshot_owner_first_m448(lib, side_streams):
+    """The two-shot owner's reduce at M = 448 (1568 workgroups, at most 7 per CU: a grid
+    that leaves a producer room) launched before the push, on its own stream, with the read
+    of the gather row after it on that stream: no poll may time out, and every row, slot
+    and the gather row must match the oracle."""
+    import dataclasses
+
+    import torch
+
+    say("[protocol] concurrent two-shot owner-first M=448")
+    old = lib.get_spin_limit()
+    lib.set_spin_limit(1 << 18)
+    try:
+        cfg = dataclasses.replace(wl.CONFIGS["tp8_m4096"], m=448, cap=448, seed=44)
+        p = wl.ArNormInputs(cfg).partials()
+        recv_d = armed_box((1, 8, cfg.cap, W // 2))
+        gath_d = armed_box((1, 1, cfg.cap, W // 2))
+        p_d = dev16(p)
+        out_d = empty16((cfg.m, W))
+        cur = torch.cuda.current_stream()
+        s_prod, s_own = side_streams[0], side_streams[1]
+        torch.cuda.synchronize()
+        for s in side_streams:
+            s.wait_stream(cur)
+        with torch.cuda.stream(s_own):
+            assert lib.twoshot_reduce(recv_d, gath_d, 0, cfg.m) is True
+            assert lib.twoshot_read(gath_d, 0, out_d) is True
+        with torch.cuda.stream(s_prod):
+            torch.cuda._sleep(200000)
+            assert lib.twoshot_push(p_d, recv_d, 0, 0) is True
+        for s in side_streams:
+            cur.wait_stream(s)
+        torch.cuda.synchronize()
+        assert lib.status() == lib.OK
+        s0 = torch.tensor(-(1 << 31), dtype=torch.int32, device="cuda")
+        assert bool((recv_d == s0).all()) and bool((gath_d == s0).all())
+        got = host16(out_d)
+        assert_bits_equal(got, oracle.reduce_no_negative_zero(oracle.clean(oracle.pack_pairs(p))), "rows")
+    finally:
+        lib.set_spin_limit(old)
+
+
+def test_status_taken_while_another_stream_times_out(lib, side_streams):
+    """arnorm_status takes the status word with one device atomic: while a poll on one
+    stream spins towards its limit (its push withheld), status reads on another stream
+    report OK until the timeout lands, the timeout is reported exactly once, and the word
+    is clear after."""
+    import torch
+
+    say("[protocol] status taken on one stream while another times out")
+    old = lib.get_spin_limit()
+    lib.set_spin_limit(1 << 14)
+    try:
+        box = armed_box((1, 8))  # TP=2 ranks of S=4 words, one row; never pushed
+        cur = torch.cuda.current_stream()
+        s_wait, s_read = side_streams[0], side_streams[1]
+        assert lib.status() == lib.OK
+        torch.cuda.synchronize()
+        s_wait.wait_stream(cur)
+        with torch.cuda.stream(s_wait):
+            assert lib.gather_poll(box, 2, 1, copy=False) is True
+        seen = []
+        for _ in range(200):
+            seen.append(lib.status(stream=s_read))
+            if s_wait.query():
+                break
+        s_wait.synchronize()
+        seen.append(lib.status(stream=s_read))
+        seen.append(lib.status())
+        assert seen.count(lib.TIMEOUT) == 1, seen
+        assert seen[-1] == lib.OK and seen[-2] in (lib.OK, lib.TIMEOUT)
+        assert lib.lamport_arm(box) is True
+    finally:
+        lib.set_spin_limit(old)

@@ -94,27 +94,51 @@ def _shape(t, shape, what):
         raise ValueError(f"{what} must have shape {tuple(shape)}, got {None if t is None else tuple(t.shape)}")
 
 
+# BF16 arguments: bfloat16 tensors, or int16 / uint16 tensors holding BF16 bit patterns.
+BF16_DTYPES = (torch.bfloat16, torch.int16, torch.uint16)
+# Mailboxes, shards and gathered rows: 32-bit words.
+WORD_DTYPES = (torch.int32, torch.uint32)
+_DTYPES = {2: BF16_DTYPES, 4: WORD_DTYPES}
+
+
+def bf16_served(*tensors):
+    """Whether every given BF16 argument is BF16 (None entries are absent arguments).
+    drafter.comm, DrafterComm.ar_norm: the front-end serves BF16 rows only and returns None
+    otherwise; a float16 or float32 tensor would otherwise be read as BF16 bits."""
+    return all(t is None or t.dtype in BF16_DTYPES for t in tensors)
+
+
+def _words(t, what):
+    if t is not None and t.dtype not in WORD_DTYPES:
+        raise ValueError(f"{what} must hold 32-bit words (int32), got {t.dtype}")
+
+
 def _ptr(t, nbytes_per_elem=None, what="tensor"):
     if t is None:
         return None
+    if nbytes_per_elem is not None and t.dtype not in _DTYPES[nbytes_per_elem]:
+        raise ValueError(f"{what} must be one of {', '.join(str(d) for d in _DTYPES[nbytes_per_elem])}, got {t.dtype}")
     if not t.is_cuda or not t.is_contiguous():
         raise ValueError(f"{what} must be a contiguous device tensor")
     if t.device.index != torch.cuda.current_device():
         # the kernels run on the current device, which must own every buffer they touch
         raise ValueError(f"{what} is on {t.device}, the current device is cuda:{torch.cuda.current_device()}")
-    if nbytes_per_elem is not None and t.element_size() != nbytes_per_elem:
-        raise ValueError(f"{what} must have {nbytes_per_elem}-byte elements, got {t.dtype}")
     return ctypes.c_void_p(t.data_ptr())
 
 
 def lamport_arm(buf, sentinel=SENTINEL, stream=None):
-    """Fill a mailbox (any contiguous 32-bit tensor) with the sentinel."""
+    """Fill a mailbox (a contiguous int32 tensor) with the sentinel."""
+    _words(buf, "buf")
     return _check("lamport_arm", LIB.lamport_arm(_ptr(buf, 4, "buf"), buf.numel(), sentinel, _stream(stream)))
 
 
 def arnorm_push(partial, mailbox, parity, rank, stream=None):
     """partial: BF16 [nslots, M, 7168] (bfloat16/int16/uint16); mailbox: int32
-    [parities, tp, cap, 3584].  Pushes slots rank .. rank+nslots-1 of mailbox[parity]."""
+    [parities, tp, cap, 3584].  Pushes slots rank .. rank+nslots-1 of mailbox[parity].
+    None (not served) for a partial of another dtype or width."""
+    if not bf16_served(partial):
+        return None
+    _words(mailbox, "mailbox")
     nslots, m, width = partial.shape
     if width != HIDDEN:
         return None
@@ -131,7 +155,12 @@ def arnorm_reduce_norm(residual, gamma, mailbox, parity, eps, out, residual_out,
     """Poll, re-arm and reduce rows < M (M = out.shape[0]) of mailbox[parity]; writes
     out and residual_out (BF16 [M, 7168]).  residual None: residual = AR(x).
     partial (BF16 [M, 7168]) is the fused own-rank push of rank `rank`.  norm_box
-    (int32 [parities, cap, 256], sentinel-armed) lets small-M calls split rows."""
+    (int32 [parities, cap, 256], sentinel-armed) lets small-M calls split rows.
+    None (not served) when a BF16 argument has another dtype (as the pages' ar_norm)."""
+    if not bf16_served(residual, gamma, out, residual_out, partial):
+        return None
+    _words(mailbox, "mailbox")
+    _words(norm_box, "norm_box")
     m, width = out.shape
     if width != HIDDEN:
         return None
@@ -156,7 +185,12 @@ def arnorm_push_reduce_norm(partials, residual, gamma, mailbox, parity, eps, out
                             stream=None):
     """One stand-in call: every rank's push (partials BF16 [tp, M, 7168]) and the
     consumer.  One launch when norm_box is given and the TP slots of rows < M total at
-    most 1 MiB (M <= 9 at TP=8); otherwise the pair arnorm_push + arnorm_reduce_norm."""
+    most 1 MiB (M <= 9 at TP=8); otherwise the pair arnorm_push + arnorm_reduce_norm.
+    None (not served) when a BF16 argument has another dtype (as the pages' ar_norm)."""
+    if not bf16_served(partials, residual, gamma, out, residual_out):
+        return None
+    _words(mailbox, "mailbox")
+    _words(norm_box, "norm_box")
     tp_, m, width = partials.shape
     if width != HIDDEN:
         return None
@@ -180,6 +214,8 @@ def arnorm_push_reduce_norm(partials, residual, gamma, mailbox, parity, eps, out
 
 def gather_push(shard, mailbox, tp, rank, stream=None):
     """shard: int32 [nslots, M, S]; mailbox: int32 [cap, tp*S]."""
+    _words(shard, "shard")
+    _words(mailbox, "mailbox")
     nslots, m, s = shard.shape
     cap, width = mailbox.shape
     if width != tp * s:
@@ -191,6 +227,8 @@ def gather_push(shard, mailbox, tp, rank, stream=None):
 def gather_poll(mailbox, tp, m, out=None, copy=True, stream=None):
     """Poll rows < m of mailbox (int32 [cap, tp*S]); copy: into out (int32 [m, tp*S])
     and re-arm; no copy: leave the published rows in place."""
+    _words(mailbox, "mailbox")
+    _words(out, "out")
     cap, width = mailbox.shape
     if tp < 1 or width % tp:
         raise ValueError(f"mailbox rows of {width} words do not split over tp = {tp}")
@@ -206,6 +244,9 @@ def gather_push_poll(shard, mailbox, out=None, copy=True, stream=None):
     """One Gather call: every rank's shard (int32 [tp, M, S]) pushed and the M gathered
     rows polled (copied into out and re-armed, or left published), in one launch for
     small calls."""
+    _words(shard, "shard")
+    _words(mailbox, "mailbox")
+    _words(out, "out")
     tp, m, s = shard.shape
     cap, width = mailbox.shape
     if width != tp * s:
@@ -218,7 +259,11 @@ def gather_push_poll(shard, mailbox, out=None, copy=True, stream=None):
 
 
 def twoshot_push(partial, recv, parity, rank, stream=None):
-    """partial: BF16 [nslots, M, width]; recv: int32 [parities, tp, cap, width/2]."""
+    """partial: BF16 [nslots, M, width]; recv: int32 [parities, tp, cap, width/2].  None
+    (not served) for a partial of another dtype."""
+    if not bf16_served(partial):
+        return None
+    _words(recv, "recv")
     nslots, m, width = partial.shape
     p, tp, cap, words = recv.shape
     if words * 2 != width:
@@ -231,6 +276,8 @@ def twoshot_push(partial, recv, parity, rank, stream=None):
 def twoshot_reduce(recv, gather, parity, m, stream=None):
     """The owner's reduce of rows < m: recv int32 [parities, tp, cap, width/2] into the
     gather row int32 [parities, 1, cap, width/2]."""
+    _words(recv, "recv")
+    _words(gather, "gather")
     p, tp, cap, words = recv.shape
     _shape(gather, (p, 1, cap, words), "gather")
     return _check("twoshot_reduce", LIB.twoshot_reduce(
@@ -238,7 +285,11 @@ def twoshot_reduce(recv, gather, parity, m, stream=None):
 
 
 def twoshot_read(gather, parity, out, stream=None):
-    """A reader of the gather row: rows < M (M = out.shape[0]) into out (BF16 [M, width])."""
+    """A reader of the gather row: rows < M (M = out.shape[0]) into out (BF16 [M, width]).
+    None (not served) for an out of another dtype."""
+    if not bf16_served(out):
+        return None
+    _words(gather, "gather")
     p, one, cap, words = gather.shape
     m, width = out.shape
     if one != 1 or width != 2 * words:
@@ -250,7 +301,11 @@ def twoshot_read(gather, parity, out, stream=None):
 def twoshot_push_reduce_read(partial, recv, gather, parity, out, stream=None):
     """One two-shot call of every rank: partial BF16 [tp, M, width] pushed into recv,
     reduced by the owner into the gather row, read into out (BF16 [M, width]); one
-    launch for small calls."""
+    launch for small calls.  None (not served) when partial or out has another dtype."""
+    if not bf16_served(partial, out):
+        return None
+    _words(recv, "recv")
+    _words(gather, "gather")
     tp, m, width = partial.shape
     p, tp2, cap, words = recv.shape
     if tp2 != tp or words * 2 != width:

@@ -70,6 +70,7 @@ struct ReduceArgs {
   uint8_t *box;             // mailbox[parity]: [TP, cap, 14336 B]
   size_t slot_stride;       // cap * 14336 bytes
   uint32_t *nbox;           // norm_box[parity]: [cap, 256 words] (split rows only)
+  uint32_t rows;            // M
   int rank;                 // own slot (FUSED only)
   int poll_all;             // later poll passes re-read every slot (small grids) instead of a witness
   float eps;
@@ -93,14 +94,22 @@ constexpr int reduce_occupancy(int nt) {
 // workgroup writes its part into slot k of every peer's inbox, polls its own inbox,
 // adds the K parts in workgroup order and re-arms its inbox.  A part is a sum of FMA
 // products started from +0, so it is never -0, the sentinel word.
+//
+// `it` counts the rows a workgroup has done before this one (a whole-row workgroup may
+// loop over rows): the wave sums alternate between two LDS buffers by its parity, so a
+// wave that starts the next row cannot overwrite sums that a slower wave of the same
+// workgroup is still reading (between two uses of one buffer every wave has passed the
+// other row's barrier).
 template <int TP, bool RES, bool FUSED, int NT, int K, int POL_LD, int POL_ST, int POL_IN, int POL_IO>
-__device__ __forceinline__ void reduce_row(const ReduceArgs &a, const uint32_t row, const uint32_t k) {
+__device__ __forceinline__ void reduce_row(const ReduceArgs &a, const uint32_t row, const uint32_t k,
+                                           const uint32_t it = 0) {
   constexpr int NF = K > 1 ? 1 : (kRowFrags + NT - 1) / NT;  // fragments per thread
   constexpr int NW = NT / 64;
   static_assert(NT % 64 == 0 && NW <= 16, "wave64 workgroups of at most 16 waves");
   static_assert(K == 1 || (NT * K == kRowFrags && K * K <= kNormBoxRowWords), "a split row is K * NT fragments");
-  __shared__ float wave_sums[NW];
+  __shared__ float wave_sums_buf[2][NW];
   __shared__ float row_total;
+  float *wave_sums = wave_sums_buf[it & 1];
 
   const int t = threadIdx.x;
   const size_t row_off = (size_t)row * kRowBytes;
@@ -299,12 +308,22 @@ __device__ __forceinline__ void reduce_row(const ReduceArgs &a, const uint32_t r
   }
 }
 
-// The grid lists a row's K workgroups next to each other (id = row * K + k): with
-// workgroups dispatched in id order, the lowest unfinished row always has all of its
-// workgroups dispatched (every lower id has finished), so the exchange cannot deadlock.
+// K = 1: a grid of at most M workgroups, each taking rows blockIdx.x, blockIdx.x +
+// gridDim.x, ... in turn.  The host caps the grid at what the GPU holds at once with room
+// left beside it, so that a consumer launched before its producer (on another stream)
+// never waits on a row whose workgroup could not be dispatched.  K > 1: the grid lists a
+// row's K workgroups next to each other (id = row * K + k): with workgroups dispatched in
+// id order, the lowest unfinished row always has all of its workgroups dispatched (every
+// lower id has finished), so the exchange cannot deadlock.
 template <int TP, bool RES, bool FUSED, int NT, int K, int POL_LD, int POL_ST, int POL_IN, int POL_IO>
 __global__ void __launch_bounds__(NT, reduce_occupancy(NT)) reduce_norm_kernel(ReduceArgs a) {
-  reduce_row<TP, RES, FUSED, NT, K, POL_LD, POL_ST, POL_IN, POL_IO>(a, blockIdx.x / K, blockIdx.x % K);
+  if constexpr (K == 1) {
+    uint32_t it = 0;
+    for (uint32_t row = blockIdx.x; row < a.rows; row += gridDim.x, ++it)
+      reduce_row<TP, RES, FUSED, NT, 1, POL_LD, POL_ST, POL_IN, POL_IO>(a, row, 0, it);
+  } else {
+    reduce_row<TP, RES, FUSED, NT, K, POL_LD, POL_ST, POL_IN, POL_IO>(a, blockIdx.x / K, blockIdx.x % K);
+  }
 }
 
 // ---------------------------------------------------------------------------------

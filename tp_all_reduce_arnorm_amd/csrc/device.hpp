@@ -38,10 +38,16 @@ enum : int { kPolPlain = 0, kPolNT = 2, kPolDevice = 16, kPolDeviceNT = 18 };
 #define ARNORM_WPE_256 0
 #endif
 
-// Device status word: bit 0 set when a poll gave up (ARNORM_TIMEOUT).  Written with a
-// vector atomic, read and cleared by the host through its symbol.  The library is one
-// translation unit, so this is its only definition.
+// Device status word: bit 0 set when a poll gave up (ARNORM_TIMEOUT).  Set with a
+// vector atomic OR by any kernel; taken by status_take_kernel, which swaps it with 0 in
+// one device atomic and leaves the old value in g_status_taken for the host to copy.  The
+// library is one translation unit, so these are their only definitions.
 __device__ unsigned int g_status;
+__device__ unsigned int g_status_taken;
+
+__global__ void __launch_bounds__(64) status_take_kernel() {
+  if (threadIdx.x == 0) g_status_taken = atomicExch(&g_status, 0u);
+}
 
 // Buffer resource over `bytes` bytes at `base` (raw buffer: stride 0; the gfx9
 // data-format word).  Accesses past `bytes` read 0 and drop their stores.

@@ -36,78 +36,43 @@ gather_push_kernel(const u32x4 *__restrict__ shard, uint8_t *__restrict__ box, u
                   frags, c, chunks);
 }
 
-// The poll of one row's fragments by workgroup `cta` of `ctas` (cta*256 + t, strided by
-// ctas*256), with copy and re-arm.  The copy is stored with the default cache policy, as
-// the ArNorm consumer stores its rows: the last-level cache keeps it for the next reader
-// (a non-temporal store made the one-slot read at M=4096, width 7168, 35.0 against
-// 32.0 us from HBM, and changed nothing at small M).  Waiting must not steal the producers' bandwidth: a
-// wave with unpublished fragments watches one witness (the fragment of its lowest
-// waiting lane; every lane loads the same 16 B) and its lanes re-read their own
-// fragments only once that is published; a small grid (poll_all) re-reads every
-// pending fragment on each pass instead, so the data arrives with the news.  The loop
-// trip count is uniform per wave (the step is a multiple of 64).
-template <int POL_LD, int POL_ST>
-__device__ __forceinline__ void poll_row(uint8_t *row, u32x4 *out_row, uint32_t row_frags, uint32_t cta,
-                                         uint32_t ctas, int copy, uint64_t spin_limit, int poll_all) {
-  const __amdgpu_buffer_rsrc_t r = make_rsrc(row, row_frags * 16u);
-  const int lane = threadIdx.x & 63;
-  for (uint32_t base = cta * 256u + (threadIdx.x & ~63u); base < row_frags; base += ctas * 256u) {
-    const uint32_t i = base + lane;
-    const bool mine = i < row_frags;
-    u32x4 w = buf_load<POL_LD>(r, mine ? i * 16u : 0x80000000u);
-    bool ok = !mine || published(w);
-    for (uint64_t polls = 0;; ++polls) {
-      const uint64_t waiting = __ballot(!ok);
-      if (waiting == 0) break;
-      if (polls >= spin_limit) {
-        if (!ok) atomicOr(&g_status, 1u);
-        break;
-      }
-      if (poll_all) {
-        __builtin_amdgcn_s_sleep(1);
-      } else {
-        const int wl = __ffsll((unsigned long long)waiting) - 1;
-        const uint32_t *wp = reinterpret_cast<const uint32_t *>(row + (size_t)(base + wl) * 16u);
-        if (!published(load_fragment_coherent(wp))) {
-          __builtin_amdgcn_s_sleep(8);
-          continue;
-        }
-      }
-      asm volatile("" ::: "memory");
-      if (!ok) {
-        w = buf_load<POL_LD>(r, i * 16u);
-        ok = published(w);
-      }
-    }
-    if (copy && mine && ok) {
-      out_row[i] = w;
-      buf_store<POL_ST>(sentinel4(), r, i * 16u);
-    }
-  }
-}
-
-// poll_row with U fragments per thread in flight, for a grid too large to give every
-// fragment a thread of its own: workgroup `cta` of `ctas` takes blocks of 256*U
-// fragments (blk + u*256 + t), strided by ctas*256*U, issues the U loads of a thread
-// together, and waits on the thread's pending ones as poll_row does (the witness of a
-// wave is the first pending fragment of its lowest waiting lane).  The block loop is
-// uniform per workgroup; lanes past the row end load out of range (0) and store nothing.
+// The poll of a flat range of n fragments (the rows < M of a mailbox are one contiguous
+// block, and so are those of `out`), with copy and re-arm.  Workgroup w of W takes blocks
+// w, w + W, ... of 256*U fragments; in block b thread t owns fragments b*256*U + u*256 + t
+// (u < U), issues their U loads together, then waits on its pending ones.  Each block gets
+// a buffer resource of its own, so the range may span more than a resource's 4 GiB; lanes
+// past the range end load out of range (0) and store nothing.  The block loop is uniform
+// per workgroup.
+//
+// Waiting must not steal the producers' bandwidth: a wave with unpublished fragments
+// watches one witness (the first pending fragment of its lowest waiting lane; every lane
+// loads the same 16 B) and its lanes re-read their own pending fragments only once that is
+// published; a small range (poll_all) re-reads every pending fragment on each pass
+// instead, so the data arrives with the news.  The copy is stored with the default cache
+// policy, as the ArNorm consumer stores its rows: the last-level cache keeps it for the
+// next reader (a non-temporal store made the one-slot read at M=4096, width 7168, 35.0
+// against 32.0 us from HBM, and changed nothing at small M).
 template <int POL_LD, int POL_ST, int U>
-__device__ __forceinline__ void poll_row_batch(uint8_t *row, u32x4 *out_row, uint32_t row_frags, uint32_t cta,
-                                               uint32_t ctas, int copy, uint64_t spin_limit, int poll_all) {
-  const __amdgpu_buffer_rsrc_t r = make_rsrc(row, row_frags * 16u);
-  for (uint32_t blk = cta * 256u * U; blk < row_frags; blk += ctas * 256u * U) {
+__device__ __forceinline__ void poll_range(uint8_t *box, u32x4 *out, uint64_t n, uint32_t w, uint32_t W, int copy,
+                                           uint64_t spin_limit, int poll_all) {
+  constexpr uint32_t kBlk = 256u * U;
+  const uint64_t nblk = (n + kBlk - 1) / kBlk;
+  for (uint64_t b = w; b < nblk; b += W) {
+    const uint64_t first = b * kBlk;
+    const uint32_t cnt = (uint32_t)(n - first < kBlk ? n - first : kBlk);
+    uint8_t *blk = box + first * 16u;
+    const __amdgpu_buffer_rsrc_t r = make_rsrc(blk, cnt * 16u);
     uint32_t idx[U];
-    u32x4 w[U];
+    u32x4 v[U];
     uint32_t pend = 0;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      idx[u] = blk + u * 256u + threadIdx.x;
-      w[u] = buf_load<POL_LD>(r, idx[u] < row_frags ? idx[u] * 16u : 0x80000000u);
+      idx[u] = u * 256u + threadIdx.x;
+      v[u] = buf_load<POL_LD>(r, idx[u] < cnt ? idx[u] * 16u : 0x80000000u);
     }
 #pragma unroll
     for (int u = 0; u < U; ++u)
-      if (idx[u] < row_frags && !published(w[u])) pend |= 1u << u;
+      if (idx[u] < cnt && !published(v[u])) pend |= 1u << u;
     for (uint64_t polls = 0;; ++polls) {
       const uint64_t waiting = __ballot(pend != 0);
       if (waiting == 0) break;
@@ -118,12 +83,12 @@ __device__ __forceinline__ void poll_row_batch(uint8_t *row, u32x4 *out_row, uin
       if (poll_all) {
         __builtin_amdgcn_s_sleep(1);
       } else {
-        uint32_t first = 0;
+        uint32_t first_pending = 0;
 #pragma unroll
         for (int u = U - 1; u >= 0; --u)
-          if ((pend >> u) & 1u) first = idx[u];
-        const uint32_t wi = __shfl(first, __ffsll((unsigned long long)waiting) - 1, 64);
-        if (!published(load_fragment_coherent(reinterpret_cast<const uint32_t *>(row + (size_t)wi * 16u)))) {
+          if ((pend >> u) & 1u) first_pending = idx[u];
+        const uint32_t wi = __shfl(first_pending, __ffsll((unsigned long long)waiting) - 1, 64);
+        if (!published(load_fragment_coherent(reinterpret_cast<const uint32_t *>(blk + (size_t)wi * 16u)))) {
           __builtin_amdgcn_s_sleep(8);
           continue;
         }
@@ -132,34 +97,29 @@ __device__ __forceinline__ void poll_row_batch(uint8_t *row, u32x4 *out_row, uin
 #pragma unroll
       for (int u = 0; u < U; ++u)
         if ((pend >> u) & 1u) {
-          w[u] = buf_load<POL_LD>(r, idx[u] * 16u);
-          if (published(w[u])) pend &= ~(1u << u);
+          v[u] = buf_load<POL_LD>(r, idx[u] * 16u);
+          if (published(v[u])) pend &= ~(1u << u);
         }
     }
     if (copy) {
+      u32x4 *oblk = out + first;
 #pragma unroll
       for (int u = 0; u < U; ++u)
-        if (idx[u] < row_frags && !((pend >> u) & 1u)) {
-          out_row[idx[u]] = w[u];
+        if (idx[u] < cnt && !((pend >> u) & 1u)) {
+          oblk[idx[u]] = v[u];
           buf_store<POL_ST>(sentinel4(), r, idx[u] * 16u);
         }
     }
   }
 }
 
-// gather_poll: a 1-D grid of ctas * M workgroups, id = m * ctas + cta; U fragments per
-// thread in flight.
+// gather_poll: the M rows < M as one range of n fragments, U fragments per thread in
+// flight; the grid (at most 1024 workgroups) is resident at once.
 template <int POL_LD, int POL_ST, int U>
 __global__ void __launch_bounds__(256)
-gather_poll_kernel(uint8_t *__restrict__ box, u32x4 *__restrict__ out, uint32_t row_frags, uint32_t ctas,
-                   int copy, uint64_t spin_limit, int poll_all) {
-  const uint32_t m = blockIdx.x / ctas, cta = blockIdx.x - m * ctas;
-  if constexpr (U == 1)
-    poll_row<POL_LD, POL_ST>(box + (size_t)m * row_frags * 16u, out + (size_t)m * row_frags, row_frags, cta, ctas,
-                             copy, spin_limit, poll_all);
-  else
-    poll_row_batch<POL_LD, POL_ST, U>(box + (size_t)m * row_frags * 16u, out + (size_t)m * row_frags, row_frags, cta,
-                                      ctas, copy, spin_limit, poll_all);
+gather_poll_kernel(uint8_t *__restrict__ box, u32x4 *__restrict__ out, uint64_t n, int copy, uint64_t spin_limit,
+                   int poll_all) {
+  poll_range<POL_LD, POL_ST, U>(box, out, n, blockIdx.x, gridDim.x, copy, spin_limit, poll_all);
 }
 
 // gather_push_poll in one launch, as the pages' Gather kernel pushes its shard and then
@@ -172,7 +132,7 @@ struct GatherStepArgs {
   uint32_t frags;      // F = S/4 fragments of one rank's row
   uint32_t M;
   uint32_t per_row;    // producer workgroups per (rank, row)
-  uint32_t ctas;       // poller workgroups per row
+  uint32_t pollers;    // poller workgroups (poll_range over the M gathered rows)
   int copy;
   uint64_t spin_limit;
   int poll_all;
@@ -189,13 +149,8 @@ __global__ void __launch_bounds__(256) gather_push_poll_kernel(GatherStepArgs a)
                          a.frags, chunk, a.per_row);
     return;
   }
-  const uint32_t c = blockIdx.x - producers, m = c / a.ctas, cta = c - m * a.ctas;
-  if constexpr (U == 1)
-    poll_row<POL_LD, POL_ST>(a.box + (size_t)m * row_frags * 16u, a.out + (size_t)m * row_frags, row_frags, cta,
-                             a.ctas, a.copy, a.spin_limit, a.poll_all);
-  else
-    poll_row_batch<POL_LD, POL_ST, U>(a.box + (size_t)m * row_frags * 16u, a.out + (size_t)m * row_frags, row_frags,
-                                      cta, a.ctas, a.copy, a.spin_limit, a.poll_all);
+  poll_range<POL_LD, POL_ST, U>(a.box, a.out, (uint64_t)a.M * row_frags, blockIdx.x - producers, a.pollers, a.copy,
+                                a.spin_limit, a.poll_all);
 }
 
 }  // namespace arn

@@ -4,6 +4,8 @@
 #include <algorithm>
 #include <atomic>
 #include <cstdint>
+#include <map>
+#include <mutex>
 #include <tuple>
 #include <utility>
 
@@ -130,21 +132,47 @@ constexpr int kPolPush = ARNORM_POL_PUSH;
 constexpr int kPolIn = ARNORM_POL_IN;  // the caller's rows read once (residual, own partial)
 constexpr int kPolIO = ARNORM_POL_IO;  // the caller's output rows
 
+// Up to this many rows a whole-row consumer gets one workgroup per row without asking
+// the runtime for the resident grid (any GPU of this family holds that many at once).
+#ifndef ARNORM_WHOLE_ROW_LOOP_MIN_ROWS
+#define ARNORM_WHOLE_ROW_LOOP_MIN_ROWS 128
+#endif
+constexpr int kWholeRowLoopMinRows = ARNORM_WHOLE_ROW_LOOP_MIN_ROWS;
+
 bool aligned16(const void *p) { return p != nullptr && (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 // hipLaunchKernel with the kernel's own parameter types, so every argument is passed
-// exactly as the kernel declares it; returns the launch status.
+// exactly as the kernel declares it, and `lds` bytes of dynamic LDS per workgroup;
+// returns the launch status.
 template <typename... KArgs, typename... Args>
-int launch(void (*kernel)(KArgs...), dim3 grid, dim3 block, hipStream_t stream, Args &&...args) {
+int launch_lds(void (*kernel)(KArgs...), dim3 grid, dim3 block, size_t lds, hipStream_t stream, Args &&...args) {
   std::tuple<KArgs...> values(std::forward<Args>(args)...);
   void *argv[sizeof...(KArgs) > 0 ? sizeof...(KArgs) : 1];
   std::apply([&](auto &...v) {
     int i = 0;
     ((argv[i++] = static_cast<void *>(&v)), ...);
   }, values);
-  const hipError_t e = hipLaunchKernel(reinterpret_cast<const void *>(kernel), grid, block, argv, 0, stream);
+  const hipError_t e = hipLaunchKernel(reinterpret_cast<const void *>(kernel), grid, block, argv, lds, stream);
   return e == hipSuccess ? ARNORM_OK : ARNORM_HIP_ERROR;
 }
+
+template <typename... KArgs, typename... Args>
+int launch(void (*kernel)(KArgs...), dim3 grid, dim3 block, hipStream_t stream, Args &&...args) {
+  return launch_lds(kernel, grid, block, 0, stream, std::forward<Args>(args)...);
+}
+
+// Dynamic LDS (unused by the kernel) that keeps the two-shot owner's reduce, 256-thread
+// workgroups of 45 VGPRs that would otherwise fill all 32 wave slots of a CU, to at most
+// 7 workgroups per CU of gfx950's 160 KB, 28 slots.  The owner keeps one fragment per
+// thread over the whole range (a grid capped at half the GPU measured 10 % slower at
+// M=4096), so a producer launched after it on another stream gets in only while that grid
+// leaves room: measured at TP=8, width 7168, up to M=448 (1568 workgroups), not at M=512
+// (1792, every CU full) or above, where the owner is served in order only (its producer
+// first, or the polls give up at the spin limit).  The LDS costs nothing measurable
+// (M=4096 from HBM: 173.0-175.7 against 171.5-172.7 us without).
+#ifndef ARNORM_OWNER_LDS_BYTES
+#define ARNORM_OWNER_LDS_BYTES (22u * 1024u)
+#endif
 
 // Shape and argument checks shared by arnorm_push / arnorm_reduce_norm.
 int check_box(int parities, int tp, int cap, int parity, int M) {
@@ -176,17 +204,54 @@ int check_twoshot(int parities, int cap, int width, int parity, int M) {
 }
 
 // A row-block poll with copy (the Gather consumer): rows < M of `box`, row_frags
-// fragments each; about one fragment per thread, the grid resident at once.
+// fragments each, as one range; the grid resident at once.
 int launch_poll(uint8_t *box, u32x4 *out, uint32_t row_frags, int M, int copy, hipStream_t stream);
 
 uint8_t *parity_base(int32_t *mailbox, int parity, int tp, int cap) {
   return reinterpret_cast<uint8_t *>(mailbox) + (size_t)parity * tp * cap * arn::kRowBytes;
 }
 
+// Half of the workgroups of `kernel` (nt threads each) that the current device holds at
+// once: compute units x max(1, workgroups per CU / 2), from the occupancy the compiled
+// kernel allows.  A polling grid of that size is resident at once with room beside it on
+// every CU, so a producer launched after it on another stream always gets in.  (A
+// polling grid that fills the GPU exactly does not leave that room: the two-shot owner's
+// reduce, 7 workgroups per CU at most, let a producer in at 1568 workgroups and kept it
+// out at 1792 = 7 x 256.)  Cached per device and kernel; 0 if the runtime cannot tell.
+uint32_t half_resident_grid(const void *kernel, int nt) {
+  static std::mutex mu;
+  static std::map<std::pair<int, const void *>, uint32_t> cache;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  std::lock_guard<std::mutex> lock(mu);
+  const auto key = std::make_pair(dev, kernel);
+  const auto it = cache.find(key);
+  if (it != cache.end()) return it->second;
+  int cus = 0, per_cu = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, nt, 0) != hipSuccess || cus < 1)
+    return 0;
+  const uint32_t grid = (uint32_t)cus * (uint32_t)std::max(1, per_cu / 2);
+  cache.emplace(key, grid);
+  return grid;
+}
+
+// A whole-row consumer: min(M, half_resident_grid) workgroups, each looping over rows
+// (one 896-thread workgroup per CU).  Measured at TP=8, M=4096 (us from HBM / right after
+// the push / push + consumer as the call repeats): 256 workgroups 187.7 / 167.1 /
+// 305.4-305.9, 512 (two per CU, the GPU full) 187.9-190.5 / 167.8-168.5 / 309.0-311.9,
+// 448 194.5-194.9 / 178.5-179.2 / 318.3-318.7, 384 208.7-209.8 / 198.4-198.5 / 338.6-338.8,
+// one workgroup per row (4096, not resident) 183.5-186.8 / 169.3-170.8 / 307.8-316.2.
 template <int TP, bool RES, bool FUSED, int NT>
 int launch_reduce(const arn::ReduceArgs &a, int M, hipStream_t stream) {
-  return launch(arn::reduce_norm_kernel<TP, RES, FUSED, NT, 1, kPolPoll, kPolRearm, kPolIn, kPolIO>, dim3(M), dim3(NT), stream,
-                a);
+  auto kernel = arn::reduce_norm_kernel<TP, RES, FUSED, NT, 1, kPolPoll, kPolRearm, kPolIn, kPolIO>;
+  uint32_t grid = (uint32_t)M;
+  if (M > kWholeRowLoopMinRows) {
+    const uint32_t cap = half_resident_grid(reinterpret_cast<const void *>(kernel), NT);
+    if (cap == 0) return ARNORM_HIP_ERROR;
+    grid = std::min(grid, cap);
+  }
+  return launch(kernel, dim3(grid), dim3(NT), stream, a);
 }
 
 template <int TP, bool RES, bool FUSED, int K>
@@ -240,26 +305,26 @@ int reduce_split(int M, bool have_box) {
   return k;
 }
 
-// Poller workgroups per row: about one fragment per thread, at least one per row, and
-// at most 1024 workgroups of 256 threads in all (half of what 256 CUs hold), so the
-// whole grid is resident at once and a producer running beside it still finds room.
-uint32_t poll_ctas(uint32_t row_frags, int M) {
-  const uint32_t want = (row_frags + 255) / 256;
-  return std::max(1u, std::min(want, 1024u / (uint32_t)M));
-}
-
-// The layout of a Gather poll: fragments per thread in flight (1, or ARNORM_POLL_U when
-// the grid cap leaves threads several fragments) and its workgroups per row.
+// The layout of a Gather poll over n fragments (the rows < M as one range): U fragments
+// per thread in flight and the number of workgroups.  One fragment per thread while that
+// takes at most 1024 workgroups of 256 threads, else ARNORM_POLL_U in flight per thread
+// over at most 1024 workgroups.  1024 workgroups of 256 threads are a quarter of what
+// 256 CUs hold, so the whole grid is resident at once and a producer running beside it
+// on another stream still finds room (a cap of 2048, the full machine, starved a
+// concurrent producer at M=512: the poll spun to its limit and the push ran after).
+// Measured for the one-slot read at M=4096, width 7168 (a copy and re-arm of 58.7 MB, us
+// from HBM): 4 per thread over 1024 workgroups 30.4-31.3, one per thread over the whole
+// range (14,336 workgroups, not resident) 29.7-31.0, one row per workgroup 32.0-32.2.
+constexpr uint32_t kPollMaxGrid = 1024;
 struct PollLayout {
   int u;
-  uint32_t ctas;
+  uint32_t grid;
 };
-PollLayout poll_layout(uint32_t row_frags, int M) {
-  const uint32_t ctas = poll_ctas(row_frags, M);
+PollLayout poll_layout(uint64_t n) {
   int u = g_poll_frags.load(std::memory_order_relaxed);
-  if (u == 0) u = (uint64_t)ctas * 256u >= row_frags ? 1 : ARNORM_POLL_U;
-  if (u == 1) return {1, ctas};
-  return {u, std::max(1u, std::min((row_frags + 256u * u - 1) / (256u * u), ctas))};
+  if (u == 0) u = n <= (uint64_t)kPollMaxGrid * 256u ? 1 : ARNORM_POLL_U;
+  const uint64_t blocks = (n + 256u * u - 1) / (256u * u);
+  return {u, (uint32_t)std::max<uint64_t>(1, std::min<uint64_t>(blocks, kPollMaxGrid))};
 }
 int poll_mode(int automatic) {
   const int mode = g_poll_mode.load(std::memory_order_relaxed);
@@ -267,14 +332,15 @@ int poll_mode(int automatic) {
 }
 
 int launch_poll(uint8_t *box, u32x4 *out, uint32_t row_frags, int M, int copy, hipStream_t stream) {
-  const int poll_all = poll_mode((uint64_t)M * row_frags * 16u <= ARNORM_POLL_ALL_MAX_BYTES);
+  const uint64_t n = (uint64_t)M * row_frags;
+  const int poll_all = poll_mode(n * 16u <= ARNORM_POLL_ALL_MAX_BYTES);
   const uint64_t spin = g_spin_limit.load(std::memory_order_relaxed);
-  const PollLayout l = poll_layout(row_frags, M);
-  if (l.u == 1)  // a fragment per thread, or a loop over them where the grid is capped
-    return launch(arn::gather_poll_kernel<kPolPoll, kPolRearm, 1>, dim3(l.ctas * (unsigned)M), dim3(256), stream,
-                  box, out, row_frags, l.ctas, copy ? 1 : 0, spin, poll_all);
-  return launch(arn::gather_poll_kernel<kPolPoll, kPolRearm, ARNORM_POLL_U>, dim3(l.ctas * (unsigned)M), dim3(256),
-                stream, box, out, row_frags, l.ctas, copy ? 1 : 0, spin, poll_all);
+  const PollLayout l = poll_layout(n);
+  if (l.u == 1)
+    return launch(arn::gather_poll_kernel<kPolPoll, kPolRearm, 1>, dim3(l.grid), dim3(256), stream, box, out, n,
+                  copy ? 1 : 0, spin, poll_all);
+  return launch(arn::gather_poll_kernel<kPolPoll, kPolRearm, ARNORM_POLL_U>, dim3(l.grid), dim3(256), stream, box,
+                out, n, copy ? 1 : 0, spin, poll_all);
 }
 
 // The producer kernel over `frags` fragments per slot of nslots slots.
@@ -343,6 +409,7 @@ int arnorm_reduce_norm(const uint16_t *partial, const uint16_t *residual, const 
   a.res_out = reinterpret_cast<uint8_t *>(residual_out);
   a.box = parity_base(mailbox, parity, tp, cap);
   a.slot_stride = (size_t)cap * arn::kRowBytes;
+  a.rows = (uint32_t)M;
   a.rank = partial ? rank : -1;
   a.eps = eps;
   a.spin_limit = g_spin_limit.load(std::memory_order_relaxed);
@@ -404,6 +471,7 @@ int arnorm_push_reduce_norm(const uint16_t *partials, const uint16_t *residual, 
   a.r.box = parity_base(mailbox, parity, tp, cap);
   a.r.slot_stride = (size_t)cap * arn::kRowBytes;
   a.r.nbox = reinterpret_cast<uint32_t *>(norm_box) + (size_t)parity * cap * arn::kNormBoxRowWords;
+  a.r.rows = (uint32_t)M;
   a.r.rank = -1;
   a.r.eps = eps;
   a.r.spin_limit = g_spin_limit.load(std::memory_order_relaxed);
@@ -491,12 +559,12 @@ int gather_push_poll(const int32_t *shard, int32_t *mailbox, int32_t *out, int t
   a.frags = frags;
   a.M = (uint32_t)M;
   a.per_row = (frags + 255) / 256;
-  const PollLayout l = poll_layout((uint32_t)tp * frags, M);
-  a.ctas = l.ctas;
+  const PollLayout l = poll_layout((uint64_t)M * tp * frags);
+  a.pollers = l.grid;
   a.copy = copy ? 1 : 0;
   a.spin_limit = g_spin_limit.load(std::memory_order_relaxed);
   a.poll_all = poll_mode(1);
-  const dim3 grid(tp * M * a.per_row + M * a.ctas);
+  const dim3 grid(tp * M * a.per_row + a.pollers);
 #define ARNORM_GATHER_STEP(T)                                                                                      \
   case T:                                                                                                          \
     if (l.u == 1) return launch(arn::gather_push_poll_kernel<T, 1, kPolPush, kPolPoll, kPolRearm>, grid, dim3(256), \
@@ -544,14 +612,19 @@ int twoshot_reduce(int32_t *recv, int32_t *gather, int parities, int tp, int cap
   a.spin_limit = g_spin_limit.load(std::memory_order_relaxed);
   a.poll_all = (uint64_t)tp * a.frags * 16u <= ARNORM_POLL_ALL_MAX_BYTES;
   const dim3 grid(std::max(1u, std::min((a.frags + 255) / 256, 16384u)));
+  const size_t lds = ARNORM_OWNER_LDS_BYTES;
   switch (tp) {
-    case 2: return launch(arn::twoshot_reduce_kernel<2, kPolPoll, kPolRearm, kPolPush>, grid, dim3(256), stream, a);
-    case 3: return launch(arn::twoshot_reduce_kernel<3, kPolPoll, kPolRearm, kPolPush>, grid, dim3(256), stream, a);
-    case 4: return launch(arn::twoshot_reduce_kernel<4, kPolPoll, kPolRearm, kPolPush>, grid, dim3(256), stream, a);
-    case 5: return launch(arn::twoshot_reduce_kernel<5, kPolPoll, kPolRearm, kPolPush>, grid, dim3(256), stream, a);
-    case 6: return launch(arn::twoshot_reduce_kernel<6, kPolPoll, kPolRearm, kPolPush>, grid, dim3(256), stream, a);
-    case 7: return launch(arn::twoshot_reduce_kernel<7, kPolPoll, kPolRearm, kPolPush>, grid, dim3(256), stream, a);
-    case 8: return launch(arn::twoshot_reduce_kernel<8, kPolPoll, kPolRearm, kPolPush>, grid, dim3(256), stream, a);
+#define ARNORM_OWNER(T)                                                                                             \
+  case T:                                                                                                           \
+    return launch_lds(arn::twoshot_reduce_kernel<T, kPolPoll, kPolRearm, kPolPush>, grid, dim3(256), lds, stream, a);
+    ARNORM_OWNER(2)
+    ARNORM_OWNER(3)
+    ARNORM_OWNER(4)
+    ARNORM_OWNER(5)
+    ARNORM_OWNER(6)
+    ARNORM_OWNER(7)
+    ARNORM_OWNER(8)
+#undef ARNORM_OWNER
   }
   return ARNORM_NOT_SERVED;
 }
@@ -641,15 +714,19 @@ int arnorm_set_reduce_threads(int threads) {
 
 int arnorm_status(int *status, hipStream_t stream) {
   if (status == nullptr) return ARNORM_BAD_ARG;
+  // The swap is one device atomic, so a timeout that a kernel on another stream records
+  // at any moment lands either in this read or in the next one, never in neither.  The
+  // mutex keeps two host threads from sharing the one g_status_taken word between the
+  // swap and its copy.
+  static std::mutex mu;
+  std::lock_guard<std::mutex> lock(mu);
   if (hipStreamSynchronize(stream) != hipSuccess) return ARNORM_HIP_ERROR;
+  if (launch(arn::status_take_kernel, dim3(1), dim3(64), stream) != ARNORM_OK) return ARNORM_HIP_ERROR;
   unsigned int v = 0;
-  if (hipMemcpyFromSymbol(&v, HIP_SYMBOL(arn::g_status), sizeof(v), 0, hipMemcpyDeviceToHost) != hipSuccess)
+  if (hipMemcpyFromSymbolAsync(&v, HIP_SYMBOL(arn::g_status_taken), sizeof(v), 0, hipMemcpyDeviceToHost, stream) !=
+          hipSuccess ||
+      hipStreamSynchronize(stream) != hipSuccess)
     return ARNORM_HIP_ERROR;
-  if (v != 0) {
-    const unsigned int zero = 0;
-    if (hipMemcpyToSymbol(HIP_SYMBOL(arn::g_status), &zero, sizeof(zero), 0, hipMemcpyHostToDevice) != hipSuccess)
-      return ARNORM_HIP_ERROR;
-  }
   *status = v ? ARNORM_TIMEOUT : ARNORM_OK;
   return ARNORM_OK;
 }
