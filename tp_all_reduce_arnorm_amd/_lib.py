@@ -15,7 +15,7 @@ import torch
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libarnorm.so")
 
-OK, NOT_SERVED, BAD_ARG, HIP_ERROR, TIMEOUT = 0, 1, 2, 3, 4
+OK, NOT_SERVED, BAD_ARG, HIP_ERROR, TIMEOUT, TOO_LARGE = 0, 1, 2, 3, 4, 5
 SENTINEL = 0x80000000
 HIDDEN = 7168
 ROW_WORDS = 3584
@@ -31,6 +31,8 @@ _SIGNATURES = {
                                     _c_int, _c_int, _c_int, _c_int, _c_float, _c_ptr]),
     "arnorm_push_reduce_norm": (_c_int, [_c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_int, _c_int,
                                          _c_int, _c_int, _c_int, _c_float, _c_ptr]),
+    "arnorm_push_reduce_norm_static": (_c_int, [_c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_int, _c_int,
+                                                _c_int, _c_int, _c_int, _c_float, _c_ptr]),
     "gather_push": (_c_int, [_c_ptr, _c_ptr, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_ptr]),
     "gather_poll": (_c_int, [_c_ptr, _c_ptr, _c_int, _c_int, _c_int, _c_int, _c_int, _c_ptr]),
     "gather_push_poll": (_c_int, [_c_ptr, _c_ptr, _c_ptr, _c_int, _c_int, _c_int, _c_int, _c_int, _c_ptr]),
@@ -210,6 +212,33 @@ def arnorm_push_reduce_norm(partials, residual, gamma, mailbox, parity, eps, out
         _ptr(partials, 2, "partials"), _ptr(residual, 2, "residual"), _ptr(gamma, 2, "gamma"),
         _ptr(out, 2, "out"), _ptr(residual_out, 2, "residual_out"), _ptr(mailbox, 4, "mailbox"),
         _ptr(norm_box, 4, "norm_box"), p, tp, cap, parity, m, float(eps), _stream(stream)))
+
+
+def arnorm_push_reduce_norm_static(partials, residual, gamma, mailbox, parity, eps, out, residual_out,
+                                   stream=None):
+    """arnorm_push_reduce_norm whose norm box is the library's own static array: no
+    workspace argument and no allocation, for M <= 64 rows (ArnormError TOO_LARGE above).
+    Calls that overlap on one device race on that array."""
+    if not bf16_served(partials, residual, gamma, out, residual_out):
+        return None
+    _words(mailbox, "mailbox")
+    tp_, m, width = partials.shape
+    if width != HIDDEN:
+        return None
+    p, tp, cap, words = mailbox.shape
+    if words != ROW_WORDS:
+        raise ValueError(f"mailbox rows must be {ROW_WORDS} words, got {words}")
+    if tp_ != tp:
+        raise ValueError(f"partials hold {tp_} ranks, the mailbox {tp} slots")
+    _shape(out, (m, HIDDEN), "out")
+    _shape(residual_out, (m, HIDDEN), "residual_out")
+    _shape(gamma, (HIDDEN,), "gamma")
+    if residual is not None:
+        _shape(residual, (m, HIDDEN), "residual")
+    return _check("arnorm_push_reduce_norm_static", LIB.arnorm_push_reduce_norm_static(
+        _ptr(partials, 2, "partials"), _ptr(residual, 2, "residual"), _ptr(gamma, 2, "gamma"),
+        _ptr(out, 2, "out"), _ptr(residual_out, 2, "residual_out"), _ptr(mailbox, 4, "mailbox"), p, tp, cap, parity,
+        m, float(eps), _stream(stream)))
 
 
 def gather_push(shard, mailbox, tp, rank, stream=None):

@@ -14,9 +14,35 @@
 #include "gather_kernels.hpp"
 #include "twoshot_kernels.hpp"
 
+// The norm box of arnorm_push_reduce_norm_static: 64 rows of 256 words (64 KiB), one
+// parity, on every device the library runs on, held until the process ends.  Host code
+// never uses this name as an address: each device's own address comes from
+// hipGetSymbolAddress (static_scratch below).
+constexpr int kScratchRows = 64;
+static __device__ __align__(256) uint32_t scratch[kScratchRows * arn::kNormBoxRowWords];
+
 namespace {
 
 using arn::u32x4;
+
+// The device address of `scratch` on the current device: looked up with
+// hipGetSymbolAddress on a device's first call, with that device current, and kept.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+uint32_t *g_scratch_ptr[kMaxDevices] = {};
+
+int static_scratch(uint32_t **ptr) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return ARNORM_HIP_ERROR;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void *p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return ARNORM_HIP_ERROR;
+    g_scratch_ptr[dev] = static_cast<uint32_t *>(p);
+  }
+  *ptr = g_scratch_ptr[dev];
+  return ARNORM_OK;
+}
 
 std::atomic<uint64_t> g_spin_limit{uint64_t(1) << 22};
 std::atomic<int> g_reduce_threads{0};
@@ -357,6 +383,117 @@ int launch_push(const void *partial, uint8_t *first, size_t slot_stride, uint32_
   return launch(arn::push_kernel<ARNORM_PUSH_U, kPolPush>, grid, dim3(256), stream, src, first, slot_stride, frags);
 }
 
+// The block of a caller's norm box int32 [parities, cap, 256] that a call of this parity uses.
+uint32_t *norm_box_block(int32_t *norm_box, int parity, int cap) {
+  return reinterpret_cast<uint32_t *>(norm_box) + (size_t)parity * cap * arn::kNormBoxRowWords;
+}
+
+// arnorm_reduce_norm after its argument checks; nbox is the norm box's block of this
+// call's parity (int32 [rows >= M, 256]) or NULL.
+int reduce_norm_launch(const uint16_t *partial, const uint16_t *residual, const uint16_t *gamma, uint16_t *out,
+                       uint16_t *residual_out, int32_t *mailbox, uint32_t *nbox, int tp, int cap, int parity, int rank,
+                       int M, float eps, hipStream_t stream) {
+  arn::ReduceArgs a;
+  a.partial = reinterpret_cast<const uint8_t *>(partial);
+  a.residual = reinterpret_cast<const uint8_t *>(residual);
+  a.gamma = reinterpret_cast<const uint8_t *>(gamma);
+  a.out = reinterpret_cast<uint8_t *>(out);
+  a.res_out = reinterpret_cast<uint8_t *>(residual_out);
+  a.box = parity_base(mailbox, parity, tp, cap);
+  a.slot_stride = (size_t)cap * arn::kRowBytes;
+  a.rows = (uint32_t)M;
+  a.rank = partial ? rank : -1;
+  a.eps = eps;
+  a.spin_limit = g_spin_limit.load(std::memory_order_relaxed);
+  a.poll_all = (uint64_t)tp * M * arn::kRowBytes <= ARNORM_POLL_ALL_MAX_BYTES;
+  const bool res = residual != nullptr;
+  const bool fused = partial != nullptr;
+  const int threads = reduce_threads(M);
+  const int split = reduce_split(M, nbox != nullptr);
+  a.nbox = nbox;
+  switch (tp) {
+    case 2: return launch_reduce_tp<2>(a, res, fused, M, threads, split, stream);
+    case 3: return launch_reduce_tp<3>(a, res, fused, M, threads, split, stream);
+    case 4: return launch_reduce_tp<4>(a, res, fused, M, threads, split, stream);
+    case 5: return launch_reduce_tp<5>(a, res, fused, M, threads, split, stream);
+    case 6: return launch_reduce_tp<6>(a, res, fused, M, threads, split, stream);
+    case 7: return launch_reduce_tp<7>(a, res, fused, M, threads, split, stream);
+    case 8: return launch_reduce_tp<8>(a, res, fused, M, threads, split, stream);
+  }
+  return ARNORM_NOT_SERVED;
+}
+
+// arnorm_push_reduce_norm after its argument checks; nbox is the norm box's block of this
+// call's parity (int32 [rows >= M, 256]) or NULL.
+int push_reduce_norm_launch(const uint16_t *partials, const uint16_t *residual, const uint16_t *gamma,
+                            uint16_t *out, uint16_t *residual_out, int32_t *mailbox, uint32_t *nbox, int parities,
+                            int tp, int cap, int parity, int M, float eps, hipStream_t stream) {
+  // One launch only where its consumer may re-read every slot on each poll pass (a small
+  // grid): measured at TP=8 it is then faster than the pair (M=4: 4.8 against 5.3 us),
+  // while with witness polling (larger M) the pair of launches is faster.  Rows split 7
+  // ways beat 14 (M=4: 4.8 against 5.3 us) and one workgroup per row (6.5 us).
+  const int K = nbox != nullptr ? reduce_split(M, true) : 1;
+  const bool one_launch = (K == 7 || K == 14) && (uint64_t)tp * M * arn::kRowBytes <= ARNORM_POLL_ALL_MAX_BYTES;
+  if (!one_launch) {
+    // the same call as two launches: every rank's push, then the consumer
+    const int rc = arnorm_push(partials, mailbox, parities, tp, cap, parity, 0, tp, M, stream);
+    if (rc != ARNORM_OK) return rc;
+    return reduce_norm_launch(nullptr, residual, gamma, out, residual_out, mailbox, nbox, tp, cap, parity, 0, M, eps,
+                              stream);
+  }
+
+  arn::StepArgs a;
+  a.r.partial = nullptr;
+  a.r.residual = reinterpret_cast<const uint8_t *>(residual);
+  a.r.gamma = reinterpret_cast<const uint8_t *>(gamma);
+  a.r.out = reinterpret_cast<uint8_t *>(out);
+  a.r.res_out = reinterpret_cast<uint8_t *>(residual_out);
+  a.r.box = parity_base(mailbox, parity, tp, cap);
+  a.r.slot_stride = (size_t)cap * arn::kRowBytes;
+  a.r.nbox = nbox;
+  a.r.rows = (uint32_t)M;
+  a.r.rank = -1;
+  a.r.eps = eps;
+  a.r.spin_limit = g_spin_limit.load(std::memory_order_relaxed);
+  a.r.poll_all = (uint64_t)tp * M * arn::kRowBytes <= ARNORM_POLL_ALL_MAX_BYTES;
+  a.partials = reinterpret_cast<const u32x4 *>(partials);
+  a.frags = (uint32_t)M * arn::kRowFrags;
+  const bool few = M <= ARNORM_XCD_ROWS_MAX_M;
+  const int U = few ? ARNORM_STEP_PUSH_U_FEW : ARNORM_STEP_PUSH_U;
+  const uint32_t nt = arn::kRowFrags / K;
+  a.per_slot = (a.frags + nt * U - 1) / (nt * U);
+  a.xcd_rows = few;
+  const dim3 grid(tp * a.per_slot + (few ? (M + 7) / 8 * 8 * K : M * K));
+  const bool res = residual != nullptr;
+#define ARNORM_STEP_LAUNCH_U(TPV, KV, UV)                                                                          \
+  return res ? launch(arn::push_reduce_kernel<TPV, true, KV, UV, kPolPush, kPolPoll, kPolRearm, kPolIn, kPolIO>,    \
+                      grid, dim3(nt), stream, a)                                                                   \
+             : launch(arn::push_reduce_kernel<TPV, false, KV, UV, kPolPush, kPolPoll, kPolRearm, kPolIn, kPolIO>,   \
+                      grid, dim3(nt), stream, a);
+#define ARNORM_STEP_LAUNCH_K(TPV, KV)                                                                              \
+  if (few) ARNORM_STEP_LAUNCH_U(TPV, KV, ARNORM_STEP_PUSH_U_FEW)                                                   \
+  ARNORM_STEP_LAUNCH_U(TPV, KV, ARNORM_STEP_PUSH_U)
+#define ARNORM_STEP_LAUNCH(TPV)                                                                                   \
+  case TPV:                                                                                                      \
+    if (K == 7) {                                                                                                \
+      ARNORM_STEP_LAUNCH_K(TPV, 7)                                                                               \
+    }                                                                                                            \
+    ARNORM_STEP_LAUNCH_K(TPV, 14)
+  switch (tp) {
+    ARNORM_STEP_LAUNCH(2)
+    ARNORM_STEP_LAUNCH(3)
+    ARNORM_STEP_LAUNCH(4)
+    ARNORM_STEP_LAUNCH(5)
+    ARNORM_STEP_LAUNCH(6)
+    ARNORM_STEP_LAUNCH(7)
+    ARNORM_STEP_LAUNCH(8)
+  }
+#undef ARNORM_STEP_LAUNCH
+#undef ARNORM_STEP_LAUNCH_K
+#undef ARNORM_STEP_LAUNCH_U
+  return ARNORM_NOT_SERVED;
+}
+
 }  // namespace
 
 extern "C" {
@@ -401,34 +538,9 @@ int arnorm_reduce_norm(const uint16_t *partial, const uint16_t *residual, const 
     return ARNORM_BAD_ARG;
   if (out == residual_out) return ARNORM_BAD_ARG;
 
-  arn::ReduceArgs a;
-  a.partial = reinterpret_cast<const uint8_t *>(partial);
-  a.residual = reinterpret_cast<const uint8_t *>(residual);
-  a.gamma = reinterpret_cast<const uint8_t *>(gamma);
-  a.out = reinterpret_cast<uint8_t *>(out);
-  a.res_out = reinterpret_cast<uint8_t *>(residual_out);
-  a.box = parity_base(mailbox, parity, tp, cap);
-  a.slot_stride = (size_t)cap * arn::kRowBytes;
-  a.rows = (uint32_t)M;
-  a.rank = partial ? rank : -1;
-  a.eps = eps;
-  a.spin_limit = g_spin_limit.load(std::memory_order_relaxed);
-  a.poll_all = (uint64_t)tp * M * arn::kRowBytes <= ARNORM_POLL_ALL_MAX_BYTES;
-  const bool res = residual != nullptr;
-  const bool fused = partial != nullptr;
-  const int threads = reduce_threads(M);
-  const int split = reduce_split(M, norm_box != nullptr);
-  a.nbox = norm_box ? reinterpret_cast<uint32_t *>(norm_box) + (size_t)parity * cap * arn::kNormBoxRowWords : nullptr;
-  switch (tp) {
-    case 2: return launch_reduce_tp<2>(a, res, fused, M, threads, split, stream);
-    case 3: return launch_reduce_tp<3>(a, res, fused, M, threads, split, stream);
-    case 4: return launch_reduce_tp<4>(a, res, fused, M, threads, split, stream);
-    case 5: return launch_reduce_tp<5>(a, res, fused, M, threads, split, stream);
-    case 6: return launch_reduce_tp<6>(a, res, fused, M, threads, split, stream);
-    case 7: return launch_reduce_tp<7>(a, res, fused, M, threads, split, stream);
-    case 8: return launch_reduce_tp<8>(a, res, fused, M, threads, split, stream);
-  }
-  return ARNORM_NOT_SERVED;
+  return reduce_norm_launch(partial, residual, gamma, out, residual_out, mailbox,
+                            norm_box ? norm_box_block(norm_box, parity, cap) : nullptr, tp, cap, parity, rank, M, eps,
+                            stream);
 }
 
 int arnorm_push_reduce_norm(const uint16_t *partials, const uint16_t *residual, const uint16_t *gamma,
@@ -448,70 +560,36 @@ int arnorm_push_reduce_norm(const uint16_t *partials, const uint16_t *residual, 
   if (out == residual_out) return ARNORM_BAD_ARG;
   if (norm_box && (static_cast<void *>(norm_box) == out || static_cast<void *>(norm_box) == residual_out))
     return ARNORM_BAD_ARG;
-  // One launch only where its consumer may re-read every slot on each poll pass (a small
-  // grid): measured at TP=8 it is then faster than the pair (M=4: 4.8 against 5.3 us),
-  // while with witness polling (larger M) the pair of launches is faster.  Rows split 7
-  // ways beat 14 (M=4: 4.8 against 5.3 us) and one workgroup per row (6.5 us).
-  const int K = norm_box != nullptr ? reduce_split(M, true) : 1;
-  const bool one_launch = (K == 7 || K == 14) && (uint64_t)tp * M * arn::kRowBytes <= ARNORM_POLL_ALL_MAX_BYTES;
-  if (!one_launch) {
-    // the same call as two launches: every rank's push, then the consumer
-    rc = arnorm_push(partials, mailbox, parities, tp, cap, parity, 0, tp, M, stream);
-    if (rc != ARNORM_OK) return rc;
-    return arnorm_reduce_norm(nullptr, residual, gamma, out, residual_out, mailbox, norm_box, parities, tp, cap,
-                              parity, 0, M, eps, stream);
-  }
+  return push_reduce_norm_launch(partials, residual, gamma, out, residual_out, mailbox,
+                                 norm_box ? norm_box_block(norm_box, parity, cap) : nullptr, parities, tp, cap, parity,
+                                 M, eps, stream);
+}
 
-  arn::StepArgs a;
-  a.r.partial = nullptr;
-  a.r.residual = reinterpret_cast<const uint8_t *>(residual);
-  a.r.gamma = reinterpret_cast<const uint8_t *>(gamma);
-  a.r.out = reinterpret_cast<uint8_t *>(out);
-  a.r.res_out = reinterpret_cast<uint8_t *>(residual_out);
-  a.r.box = parity_base(mailbox, parity, tp, cap);
-  a.r.slot_stride = (size_t)cap * arn::kRowBytes;
-  a.r.nbox = reinterpret_cast<uint32_t *>(norm_box) + (size_t)parity * cap * arn::kNormBoxRowWords;
-  a.r.rows = (uint32_t)M;
-  a.r.rank = -1;
-  a.r.eps = eps;
-  a.r.spin_limit = g_spin_limit.load(std::memory_order_relaxed);
-  a.r.poll_all = (uint64_t)tp * M * arn::kRowBytes <= ARNORM_POLL_ALL_MAX_BYTES;
-  a.partials = reinterpret_cast<const u32x4 *>(partials);
-  a.frags = (uint32_t)M * arn::kRowFrags;
-  const bool few = M <= ARNORM_XCD_ROWS_MAX_M;
-  const int U = few ? ARNORM_STEP_PUSH_U_FEW : ARNORM_STEP_PUSH_U;
-  const uint32_t nt = arn::kRowFrags / K;
-  a.per_slot = (a.frags + nt * U - 1) / (nt * U);
-  a.xcd_rows = few;
-  const dim3 grid(tp * a.per_slot + (few ? (M + 7) / 8 * 8 * K : M * K));
-  const bool res = residual != nullptr;
-#define ARNORM_STEP_LAUNCH_U(TPV, KV, UV)                                                                          \
-  return res ? launch(arn::push_reduce_kernel<TPV, true, KV, UV, kPolPush, kPolPoll, kPolRearm, kPolIn, kPolIO>,    \
-                      grid, dim3(nt), stream, a)                                                                   \
-             : launch(arn::push_reduce_kernel<TPV, false, KV, UV, kPolPush, kPolPoll, kPolRearm, kPolIn, kPolIO>,   \
-                      grid, dim3(nt), stream, a);
-#define ARNORM_STEP_LAUNCH_K(TPV, KV)                                                                              \
-  if (few) ARNORM_STEP_LAUNCH_U(TPV, KV, ARNORM_STEP_PUSH_U_FEW)                                                   \
-  ARNORM_STEP_LAUNCH_U(TPV, KV, ARNORM_STEP_PUSH_U)
-#define ARNORM_STEP_LAUNCH(TPV)                                                                                   \
-  case TPV:                                                                                                      \
-    if (K == 7) {                                                                                                \
-      ARNORM_STEP_LAUNCH_K(TPV, 7)                                                                               \
-    }                                                                                                            \
-    ARNORM_STEP_LAUNCH_K(TPV, 14)
-  switch (tp) {
-    ARNORM_STEP_LAUNCH(2)
-    ARNORM_STEP_LAUNCH(3)
-    ARNORM_STEP_LAUNCH(4)
-    ARNORM_STEP_LAUNCH(5)
-    ARNORM_STEP_LAUNCH(6)
-    ARNORM_STEP_LAUNCH(7)
-    ARNORM_STEP_LAUNCH(8)
-  }
-#undef ARNORM_STEP_LAUNCH
-#undef ARNORM_STEP_LAUNCH_K
-#undef ARNORM_STEP_LAUNCH_U
-  return ARNORM_NOT_SERVED;
+int arnorm_push_reduce_norm_static(const uint16_t *partials, const uint16_t *residual, const uint16_t *gamma,
+                                   uint16_t *out, uint16_t *residual_out, int32_t *mailbox, int parities, int tp,
+                                   int cap, int parity, int M, float eps, hipStream_t stream) {
+  int rc = check_box(parities, tp, cap, parity, M);
+  if (rc != ARNORM_OK) return rc;
+  if (!aligned16(partials) || (residual && !aligned16(residual))) return ARNORM_BAD_ARG;
+  if (!aligned16(gamma) || !aligned16(out) || !aligned16(residual_out) || !aligned16(mailbox)) return ARNORM_BAD_ARG;
+  const void *outs[2] = {out, residual_out};
+  const void *ins[4] = {partials, residual, gamma, mailbox};
+  for (const void *o : outs)
+    for (const void *i : ins)
+      if (o == i && !(o == residual_out && i == residual)) return ARNORM_BAD_ARG;
+  if (out == residual_out) return ARNORM_BAD_ARG;
+  if (M > kScratchRows) return ARNORM_TOO_LARGE;
+  uint32_t *nbox = nullptr;
+  rc = static_scratch(&nbox);
+  if (rc != ARNORM_OK) return rc;
+  // the rows this call uses start armed, whatever an earlier call (a timed-out one
+  // included) left there; a fill kernel, not a memset, so that the call stays capturable
+  const size_t nfrag = (size_t)M * arn::kNormBoxRowWords / 4;
+  rc = launch(arn::arm_kernel, dim3((unsigned)((nfrag + 255) / 256)), dim3(256), stream,
+              reinterpret_cast<u32x4 *>(nbox), nfrag, nbox + nfrag * 4, 0, (uint32_t)arn::kSentinel);
+  if (rc != ARNORM_OK) return rc;
+  return push_reduce_norm_launch(partials, residual, gamma, out, residual_out, mailbox, nbox, parities, tp, cap,
+                                 parity, M, eps, stream);
 }
 
 int gather_push(const int32_t *shard, int32_t *mailbox, int tp, int cap, int S, int rank, int nslots, int M,
@@ -738,6 +816,7 @@ const char *arnorm_strerror(int code) {
     case ARNORM_BAD_ARG: return "bad argument";
     case ARNORM_HIP_ERROR: return "HIP runtime error";
     case ARNORM_TIMEOUT: return "poll timed out (re-arm the mailbox)";
+    case ARNORM_TOO_LARGE: return "more rows than the library's static scratch holds";
   }
   return "unknown code";
 }
