@@ -147,7 +147,7 @@ def time_latency(lib, torch, steps, warmup, chunk=200, one_launch=True, m=None):
 
     from tp_all_reduce_arnorm_amd import workloads as wl
 
-    cfg = wl.CONFIGS["tp8_m4"] if m is None else dataclasses.replace(wl.CONFIGS["tp8_m4"], m=m)
+    cfg = wl.CONFIGS["tp8_m4"] if m is None else dataclasses.replace(wl.CONFIGS["tp8_m4"], m=m, cap=max(m, 64))
     src = wl.ArNormInputs(cfg)
     box = torch.empty((2, cfg.tp, cfg.cap, HIDDEN // 2), dtype=torch.int32, device="cuda")
     nbox = torch.empty((2, cfg.cap, 256), dtype=torch.int32, device="cuda")

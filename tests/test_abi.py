@@ -216,8 +216,9 @@ def test_spin_limit_and_threads(L):
     assert L.arnorm_set_spin_limit(12345) == 0
     assert L.arnorm_get_spin_limit() == 12345
     assert L.arnorm_set_spin_limit(old) == 0
-    assert L.arnorm_set_reduce_split(3) == 2
-    for k in (7, 14, 1, 0):
+    for k in (2, 3, 5, 16):
+        assert L.arnorm_set_reduce_split(k) == 2
+    for k in (4, 7, 8, 14, 1, 0):
         assert L.arnorm_set_reduce_split(k) == 0
     assert L.arnorm_set_reduce_threads(300) == 2
     for t in (896, 448, 256, 0):

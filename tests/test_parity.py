@@ -98,16 +98,18 @@ def test_tp8_m64_other_workgroup_sizes(lib, threads):
     run_config(lib, "tp8_m64", calls=4, threads=threads)
 
 
-@pytest.mark.parametrize("split", [0, 7, 14])
+@pytest.mark.parametrize("split", [0, 4, 7, 8, 14])
 @pytest.mark.parametrize("name", ["tp2_m1", "tp8_m4", "tp8_m64"])
 def test_split_rows(lib, name, split):
-    """Rows split over 7 or 14 workgroups (and the automatic choice), the row's sum of
-    squares exchanged through the norm box, which every call leaves re-armed."""
+    """Rows split over 4, 7, 8 or 14 workgroups (and the automatic choice; 4 and 8 leave
+    lanes of each workgroup idle), the row's sum of squares exchanged through the norm
+    box, which every call leaves re-armed."""
     run_config(lib, name, calls=min(wl.CONFIGS[name].calls, 12), split=split)
 
 
 @pytest.mark.parametrize("name,with_box,split", [("tp2_m1", True, 0), ("tp8_m4", True, 0), ("tp8_m64", True, 0), ("tp8_m4", False, 0),
-                                                ("tp2_m1", True, 14), ("tp8_m4", True, 14)])
+                                                ("tp2_m1", True, 14), ("tp8_m4", True, 14), ("tp8_m4", True, 4),
+                                                ("tp8_m4", True, 8), ("tp8_m64", True, 4), ("tp8_m64", True, 8)])
 def test_push_reduce_norm_one_call(lib, name, with_box, split):
     """arnorm_push_reduce_norm (one launch with a norm box where the TP slots of rows < M
     fit 1 MiB, rows split 7 or 14 ways; else the pair of launches) against the oracle's
@@ -137,7 +139,7 @@ def test_push_reduce_norm_one_call(lib, name, with_box, split):
         assert lib.status() == lib.OK
 
 
-@pytest.mark.parametrize("tp,split", [(2, 0), (3, 0), (8, 0), (3, 14), (8, 14)])
+@pytest.mark.parametrize("tp,split", [(2, 0), (3, 0), (8, 0), (3, 14), (8, 14), (5, 4), (8, 8)])
 def test_push_reduce_norm_torture(lib, tp, split):
     say(f"[parity] push_reduce_norm torture tp={tp} split={split}")
     lib.set_reduce_split(split)

@@ -81,6 +81,11 @@ constexpr int kNormBoxRowWords = 256;  // a row's inbox block: [K readers][K wri
 
 constexpr uint32_t kOffNone = 0x80000000u;  // an offset past every resource
 
+// Threads of a workgroup that owns one of a row's K parts (K divides 896): the part's
+// 896 / K fragments, one per thread, rounded up to whole wave64s (K = 4: 224 -> 256,
+// K = 8: 112 -> 128; the lanes past the part idle).  K = 1 is not a split.
+constexpr int split_threads(int K) { return (kRowFrags / K + 63) / 64 * 64; }
+
 // Occupancy target (waves per SIMD) asked of the compiler for a workgroup size.
 constexpr int reduce_occupancy(int nt) {
   return nt == 896 ? ARNORM_WPE_896 : nt == 448 ? ARNORM_WPE_448 : nt == 256 ? ARNORM_WPE_256 : 0;
@@ -88,8 +93,9 @@ constexpr int reduce_occupancy(int nt) {
 
 // K = workgroups per row.  K = 1: one workgroup of NT threads owns the whole row
 // (fragments t, t + NT, ...).  K > 1 (small M, a grid small enough to be resident at
-// once): workgroup k of the row owns fragments k*NT .. k*NT + NT - 1, one per thread
-// (NT * K = 896), so each CU moves 1/K of the row; the row's sum of squares is then
+// once): workgroup k of the row owns fragments k*P .. k*P + P - 1 (P = 896 / K), one per
+// thread (threads t >= P idle: their offsets are out of range), so each CU moves 1/K of
+// the row; the row's sum of squares is then
 // exchanged through the sentinel-armed norm box, itself a small Lamport mailbox: each
 // workgroup writes its part into slot k of every peer's inbox, polls its own inbox,
 // adds the K parts in workgroup order and re-arms its inbox.  A part is a sum of FMA
@@ -106,17 +112,20 @@ __device__ __forceinline__ void reduce_row(const ReduceArgs &a, const uint32_t r
   constexpr int NF = K > 1 ? 1 : (kRowFrags + NT - 1) / NT;  // fragments per thread
   constexpr int NW = NT / 64;
   static_assert(NT % 64 == 0 && NW <= 16, "wave64 workgroups of at most 16 waves");
-  static_assert(K == 1 || (NT * K == kRowFrags && K * K <= kNormBoxRowWords), "a split row is K * NT fragments");
+  static_assert(K == 1 || (kRowFrags % K == 0 && NT == split_threads(K) && K * K <= kNormBoxRowWords),
+                "a split row is K parts of 896 / K fragments");
+  constexpr uint32_t NP = K > 1 ? kRowFrags / K : kRowFrags;  // fragments of this workgroup's part
   __shared__ float wave_sums_buf[2][NW];
   __shared__ float row_total;
   float *wave_sums = wave_sums_buf[it & 1];
 
   const int t = threadIdx.x;
   const size_t row_off = (size_t)row * kRowBytes;
-  const uint32_t base = k * NT;  // first fragment of this workgroup's part of the row
+  const uint32_t base = k * NP;  // first fragment of this workgroup's part of the row
   uint32_t off[NF];
 #pragma unroll
-  for (int f = 0; f < NF; ++f) off[f] = (uint32_t)(base + t + f * NT) * 16u;
+  for (int f = 0; f < NF; ++f)
+    off[f] = (K > 1 && NT > (int)NP && (uint32_t)t >= NP) ? kOffNone : (uint32_t)(base + t + f * NT) * 16u;
 
   const __amdgpu_buffer_rsrc_t gam = make_rsrc(a.gamma, kRowBytes);
   const __amdgpu_buffer_rsrc_t resr = make_rsrc(RES ? a.residual + row_off : nullptr, RES ? kRowBytes : 0);
@@ -311,10 +320,18 @@ __device__ __forceinline__ void reduce_row(const ReduceArgs &a, const uint32_t r
 // K = 1: a grid of at most M workgroups, each taking rows blockIdx.x, blockIdx.x +
 // gridDim.x, ... in turn.  The host caps the grid at what the GPU holds at once with room
 // left beside it, so that a consumer launched before its producer (on another stream)
-// never waits on a row whose workgroup could not be dispatched.  K > 1: the grid lists a
-// row's K workgroups next to each other (id = row * K + k): with workgroups dispatched in
-// id order, the lowest unfinished row always has all of its workgroups dispatched (every
-// lower id has finished), so the exchange cannot deadlock.
+// never waits on a row whose workgroup could not be dispatched.
+//
+// K > 1: the workgroups come in blocks of 8 * K: workgroup c = 8 * K * b + 8 * k + j
+// serves row 8 * b + j, part k (ids past the last row end at once).  The dispatcher hands
+// workgroup ids to the eight XCDs in turn, so a row's K workgroups, whose ids agree mod 8,
+// share one XCD and its L2 for the norm-box exchange; placement only, the results do not
+// depend on it.  Measured at TP=8, push + consumer, us per call (rows split 4 ways, spread
+// / one XCD per row): M=32 5.71-5.74 / 5.64-5.66, M=48 6.31-6.33 / 6.19-6.21, M=64
+// 7.23-7.25 / 6.97-7.00, M=96 and 128 unchanged.  Deadlock freedom: with workgroups
+// dispatched in id order, every workgroup of the lowest unfinished block has been
+// dispatched (every lower id has finished), and a block (8 * K workgroups of at most 256
+// threads) is resident at once many times over.
 template <int TP, bool RES, bool FUSED, int NT, int K, int POL_LD, int POL_ST, int POL_IN, int POL_IO>
 __global__ void __launch_bounds__(NT, reduce_occupancy(NT)) reduce_norm_kernel(ReduceArgs a) {
   if constexpr (K == 1) {
@@ -322,7 +339,10 @@ __global__ void __launch_bounds__(NT, reduce_occupancy(NT)) reduce_norm_kernel(R
     for (uint32_t row = blockIdx.x; row < a.rows; row += gridDim.x, ++it)
       reduce_row<TP, RES, FUSED, NT, 1, POL_LD, POL_ST, POL_IN, POL_IO>(a, row, 0, it);
   } else {
-    reduce_row<TP, RES, FUSED, NT, K, POL_LD, POL_ST, POL_IN, POL_IO>(a, blockIdx.x / K, blockIdx.x % K);
+    const uint32_t c = blockIdx.x, b = c / (8u * K), w = c - b * 8u * K;
+    const uint32_t row = 8u * b + (w & 7u);
+    if (row >= a.rows) return;  // a padding id of the last block
+    reduce_row<TP, RES, FUSED, NT, K, POL_LD, POL_ST, POL_IN, POL_IO>(a, row, w >> 3);
   }
 }
 
@@ -353,8 +373,8 @@ struct StepArgs {
 };
 
 template <int TP, bool RES, int K, int U, int POL_PUSH, int POL_LD, int POL_ST, int POL_IN, int POL_IO>
-__global__ void __launch_bounds__(kRowFrags / K) push_reduce_kernel(StepArgs a) {
-  constexpr int NT = kRowFrags / K;
+__global__ void __launch_bounds__(split_threads(K)) push_reduce_kernel(StepArgs a) {
+  constexpr int NT = split_threads(K);
   const uint32_t producers = TP * a.per_slot;
   if (blockIdx.x < producers) {
     const uint32_t s = blockIdx.x / a.per_slot, p = blockIdx.x - s * a.per_slot;

@@ -98,15 +98,20 @@ std::atomic<int> g_poll_mode{0};   // Gather polls: 0 = automatic, 1 = re-read a
 #ifndef ARNORM_PUSH_MAX_GRID
 #define ARNORM_PUSH_MAX_GRID 16384
 #endif
-// Largest M for which a row is split over 14 (or 7) workgroups when a norm box is given.
-// Measured on MI355X, TP=8, stand-in call (push + consumer): 7 workgroups per row beat
-// one at every M <= 64 (M=4: 5.3 against 6.1 us; M=16: 5.5 against 7.1 us), and 14
-// were slower than 7 everywhere (more exchange, no less per-CU traffic that matters).
-#ifndef ARNORM_SPLIT14_MAX_M
-#define ARNORM_SPLIT14_MAX_M 0
-#endif
+// Rows split over 7 workgroups when a norm box is given and M <= ARNORM_SPLIT7_MAX_M,
+// over 4 up to ARNORM_SPLIT4_MAX_M, else one workgroup per row.  Measured on MI355X at
+// TP=8, us per call (graph replay; arnorm_push_reduce_norm, so one launch up to M=9, the
+// pair above), rows split 1 / 4 / 7 ways: M=8 6.42 / 5.07-5.20 / 4.88-4.96, M=16 6.43-6.48
+// / 5.25-5.31 / 5.06-5.11, M=32 6.73-6.76 / 5.73-5.75 / 5.54-5.59, M=48 7.15-7.17 /
+// 6.34-6.36 / 6.74-6.81, M=64 7.82-8.35 / 7.03-7.07 / 7.32-7.45, M=96 11.20-11.22 /
+// 10.52-10.54 / 10.81-10.88, M=128 12.84-12.85 / 12.62-12.63 / 13.24-13.29, M=192 17.54-17.58
+// / 17.77-17.80, M=256 21.41-21.45 / 21.98-22.03 (14 ways was slower than 7 everywhere,
+// 8 slower than 7 and 4).
 #ifndef ARNORM_SPLIT7_MAX_M
-#define ARNORM_SPLIT7_MAX_M 64
+#define ARNORM_SPLIT7_MAX_M 40
+#endif
+#ifndef ARNORM_SPLIT4_MAX_M
+#define ARNORM_SPLIT4_MAX_M 160
 #endif
 // arnorm_push_reduce_norm, one-launch form: fragments per producer thread per step.
 #ifndef ARNORM_STEP_PUSH_U
@@ -282,14 +287,17 @@ int launch_reduce(const arn::ReduceArgs &a, int M, hipStream_t stream) {
 
 template <int TP, bool RES, bool FUSED, int K>
 int launch_reduce_split(const arn::ReduceArgs &a, int M, hipStream_t stream) {
-  constexpr int NT = arn::kRowFrags / K;
-  return launch(arn::reduce_norm_kernel<TP, RES, FUSED, NT, K, kPolPoll, kPolRearm, kPolIn, kPolIO>, dim3(M * K), dim3(NT),
+  constexpr int NT = arn::split_threads(K);
+  return launch(arn::reduce_norm_kernel<TP, RES, FUSED, NT, K, kPolPoll, kPolRearm, kPolIn, kPolIO>,
+                dim3((M + 7) / 8 * 8 * K), dim3(NT),
                 stream, a);
 }
 
 template <int TP, bool RES, bool FUSED>
 int launch_reduce_nt(const arn::ReduceArgs &a, int M, int threads, int split, hipStream_t stream) {
+  if (split == 4) return launch_reduce_split<TP, RES, FUSED, 4>(a, M, stream);
   if (split == 7) return launch_reduce_split<TP, RES, FUSED, 7>(a, M, stream);
+  if (split == 8) return launch_reduce_split<TP, RES, FUSED, 8>(a, M, stream);
   if (split == 14) return launch_reduce_split<TP, RES, FUSED, 14>(a, M, stream);
   switch (threads) {
     case 896: return launch_reduce<TP, RES, FUSED, 896>(a, M, stream);
@@ -326,7 +334,7 @@ constexpr int kSplitMaxGrid = ARNORM_SPLIT_MAX_GRID;
 int reduce_split(int M, bool have_box) {
   if (!have_box) return 1;
   int k = g_reduce_split.load(std::memory_order_relaxed);
-  if (k == 0) k = M <= ARNORM_SPLIT14_MAX_M ? 14 : M <= ARNORM_SPLIT7_MAX_M ? 7 : 1;
+  if (k == 0) k = M <= ARNORM_SPLIT7_MAX_M ? 7 : M <= ARNORM_SPLIT4_MAX_M ? 4 : 1;
   if (k > 1 && M * k > kSplitMaxGrid) k = 1;
   return k;
 }
@@ -433,7 +441,7 @@ int push_reduce_norm_launch(const uint16_t *partials, const uint16_t *residual, 
   // while with witness polling (larger M) the pair of launches is faster.  Rows split 7
   // ways beat 14 (M=4: 4.8 against 5.3 us) and one workgroup per row (6.5 us).
   const int K = nbox != nullptr ? reduce_split(M, true) : 1;
-  const bool one_launch = (K == 7 || K == 14) && (uint64_t)tp * M * arn::kRowBytes <= ARNORM_POLL_ALL_MAX_BYTES;
+  const bool one_launch = K > 1 && (uint64_t)tp * M * arn::kRowBytes <= ARNORM_POLL_ALL_MAX_BYTES;
   if (!one_launch) {
     // the same call as two launches: every rank's push, then the consumer
     const int rc = arnorm_push(partials, mailbox, parities, tp, cap, parity, 0, tp, M, stream);
@@ -460,7 +468,7 @@ int push_reduce_norm_launch(const uint16_t *partials, const uint16_t *residual, 
   a.frags = (uint32_t)M * arn::kRowFrags;
   const bool few = M <= ARNORM_XCD_ROWS_MAX_M;
   const int U = few ? ARNORM_STEP_PUSH_U_FEW : ARNORM_STEP_PUSH_U;
-  const uint32_t nt = arn::kRowFrags / K;
+  const uint32_t nt = arn::split_threads(K);
   a.per_slot = (a.frags + nt * U - 1) / (nt * U);
   a.xcd_rows = few;
   const dim3 grid(tp * a.per_slot + (few ? (M + 7) / 8 * 8 * K : M * K));
@@ -475,8 +483,14 @@ int push_reduce_norm_launch(const uint16_t *partials, const uint16_t *residual, 
   ARNORM_STEP_LAUNCH_U(TPV, KV, ARNORM_STEP_PUSH_U)
 #define ARNORM_STEP_LAUNCH(TPV)                                                                                   \
   case TPV:                                                                                                      \
+    if (K == 4) {                                                                                                \
+      ARNORM_STEP_LAUNCH_K(TPV, 4)                                                                               \
+    }                                                                                                            \
     if (K == 7) {                                                                                                \
       ARNORM_STEP_LAUNCH_K(TPV, 7)                                                                               \
+    }                                                                                                            \
+    if (K == 8) {                                                                                                \
+      ARNORM_STEP_LAUNCH_K(TPV, 8)                                                                               \
     }                                                                                                            \
     ARNORM_STEP_LAUNCH_K(TPV, 14)
   switch (tp) {
@@ -771,7 +785,7 @@ uint64_t arnorm_get_spin_limit(void) { return g_spin_limit.load(std::memory_orde
 
 int arnorm_set_reduce_split(int workgroups_per_row) {
   const int k = workgroups_per_row;
-  if (k != 0 && k != 1 && k != 7 && k != 14) return ARNORM_BAD_ARG;
+  if (k != 0 && k != 1 && k != 4 && k != 7 && k != 8 && k != 14) return ARNORM_BAD_ARG;
   g_reduce_split.store(k, std::memory_order_relaxed);
   return ARNORM_OK;
 }
