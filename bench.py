@@ -557,15 +557,21 @@ PROFILE_COMMANDS = {
 }
 
 
-def _profiled_sha(log_path):
-    """The kernel-sources hash that a profiled bench run printed (None if absent)."""
+def _profiled_record(log_path):
+    """The JSON record that a profiled bench run printed (None if absent)."""
     try:
         for ln in open(log_path, errors="replace"):
             if ln.startswith('{"mode"'):
-                return json.loads(ln).get("sources_sha")
+                return json.loads(ln)
     except OSError:
         pass
     return None
+
+
+def _profiled_sha(log_path):
+    """The kernel-sources hash that a profiled bench run printed (None if absent)."""
+    rec = _profiled_record(log_path)
+    return rec.get("sources_sha") if rec else None
 
 
 def _short(name):
@@ -639,7 +645,7 @@ def summarize_profiles(outdir):
                     "arnorm_push_reduce_norm launch each (the 8 ranks' pushes and the consumer, rows split "
                     "7 ways through the norm box), then 2000 calls as the pair arnorm_push of 8 slots + "
                     "arnorm_reduce_norm, then 2000 arnorm_push_reduce_norm calls at M=1 (one launch) and "
-                    "2000 at M=64 (the pair)", "arnorm_tp8_m4_kernel_stats.md"),
+                    "2000 at M=64 (the pair, rows split 4 ways)", "arnorm_tp8_m4_kernel_stats.md"),
             ("roof", "ArNorm kernels at TP=8, M=4096, residual: one push of 8 slots + one consumer launch, "
                      "23 times, each launch after a 1 GiB read-only pass (torch's float32 sum) that evicts the "
                      "last-level cache", "arnorm_tp8_m4096_kernel_stats.md"),
@@ -656,7 +662,8 @@ def summarize_profiles(outdir):
             continue
         rows, table = _stats_table(os.path.join(outdir, f"prof_{key}", f"{key}_kernel_stats.csv"),
                                    os.path.join(outdir, f"prof_{key}", f"{key}_kernel_trace.csv"))
-        sha = _profiled_sha(os.path.join(outdir, f"prof_{key}.log"))
+        rec = _profiled_record(os.path.join(outdir, f"prof_{key}.log")) or {}
+        sha = rec.get("sources_sha")
         shapes = _shape_table(os.path.join(outdir, f"prof_{key}", f"{key}_kernel_trace.csv")) if key == "lat" else None
         with open(os.path.join(prof, fname), "w") as f:
             f.write(f"# rocprofv3 kernel statistics: {title}\n\n"
@@ -665,6 +672,10 @@ def summarize_profiles(outdir):
             if shapes:
                 f.write(f"\nThe library's kernels by launch shape (grid size in threads; M=1, 4 and 64 launch "
                         f"different grids):\n\n{shapes}\n")
+            if key == "lat" and rec:
+                f.write("\nThe same profiled run's own figures, HIP events on the stream over the graph replays "
+                        "(µs per call, the profiler attached): " +
+                        ", ".join(f"{k} {v:.3f}" for k, v in rec.items() if k.endswith("per_call")) + "\n")
 
     def counters(key):
         path = os.path.join(outdir, f"pmc_{key}", f"{key}_counter_collection.csv")
