@@ -29,8 +29,9 @@ arm_kernel(u32x4 *__restrict__ buf, size_t nfrag, uint32_t *__restrict__ tail, i
 // ---------------------------------------------------------------------------------
 // arnorm_push: slot s = blockIdx.y of the nslots pushed; each slot's M rows are one
 // contiguous block of `frags` fragments in both the partial rows and the mailbox.
-// U fragments per thread per step, loads first, so a wave has U x 1 KB in flight.
-template <int U, int POL>
+// U fragments per thread per step, loads first, so a wave has U x 1 KB in flight.  The
+// partial rows are read non-temporally (SRC_NT) or with the default policy.
+template <int U, int POL, bool SRC_NT>
 __global__ void __launch_bounds__(256)
 push_kernel(const u32x4 *__restrict__ partial, uint8_t *__restrict__ first_slot,
             size_t slot_stride_bytes, uint32_t frags) {
@@ -43,7 +44,7 @@ push_kernel(const u32x4 *__restrict__ partial, uint8_t *__restrict__ first_slot,
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const uint32_t i = base + u * 256u;
-      if (i < frags) v[u] = nt_load(src + i);
+      if (i < frags) v[u] = SRC_NT ? nt_load(src + i) : src[i];
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {

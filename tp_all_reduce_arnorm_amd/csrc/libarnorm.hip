@@ -76,7 +76,11 @@ std::atomic<int> g_poll_mode{0};   // Gather polls: 0 = automatic, 1 = re-read a
 #endif
 // Producer kernel (arnorm_push, twoshot_push) layout: 2 fragments per thread while a
 // slot's rows total at most ARNORM_PUSH_SMALL_BYTES, else one fragment per thread with
-// up to ARNORM_PUSH_MAX_GRID workgroups per slot (larger pushes loop).  Measured on
+// up to ARNORM_PUSH_MAX_GRID workgroups per slot (larger pushes loop).  The small layout
+// reads the partial rows with the default cache policy, the large one non-temporally:
+// measured at TP=8 (us, default / non-temporal), the call at M=64 as the pair 6.90-6.95 /
+// 7.11-7.19 (M=16 unchanged), the push of 8 slots at M=4096 142.3-142.9 / 133.5-133.8
+// from HBM and the call there 325.9-327.0 / 307.0-312.9.  Measured on
 // MI355X at TP=8.  Small: us per call of the pair push + consumer, graph-replayed,
 // fragments per thread 1 / 2 / 4 / 8: M=16 5.12 / 5.12-5.13 / 5.21-5.22 / 5.47, M=32
 // 5.74 / 5.53-5.54 / 5.63 / 5.80, M=64 7.36 / 7.29-7.30 / 7.53 / 7.50.  Large: the push of
@@ -347,8 +351,9 @@ int reduce_split(int M, bool have_box) {
 // on another stream still finds room (a cap of 2048, the full machine, starved a
 // concurrent producer at M=512: the poll spun to its limit and the push ran after).
 // Measured for the one-slot read at M=4096, width 7168 (a copy and re-arm of 58.7 MB, us
-// from HBM): 4 per thread over 1024 workgroups 30.4-31.3, one per thread over the whole
-// range (14,336 workgroups, not resident) 29.7-31.0, one row per workgroup 32.0-32.2.
+// from HBM): this layout 31.0-31.7, one row per workgroup (the layout before, not resident
+// above 1024 rows) 32.0-32.2; a probe doing only the copy and re-arm, one fragment per
+// thread over the whole range (14,336 workgroups, not resident), 29.7-31.0.
 constexpr uint32_t kPollMaxGrid = 1024;
 struct PollLayout {
   int u;
@@ -386,9 +391,10 @@ int launch_push(const void *partial, uint8_t *first, size_t slot_stride, uint32_
                   (unsigned)nslots);
   const u32x4 *src = reinterpret_cast<const u32x4 *>(partial);
   if (small)
-    return launch(arn::push_kernel<ARNORM_PUSH_U_SMALL, kPolPush>, grid, dim3(256), stream, src, first, slot_stride,
-                  frags);
-  return launch(arn::push_kernel<ARNORM_PUSH_U, kPolPush>, grid, dim3(256), stream, src, first, slot_stride, frags);
+    return launch(arn::push_kernel<ARNORM_PUSH_U_SMALL, kPolPush, false>, grid, dim3(256), stream, src, first,
+                  slot_stride, frags);
+  return launch(arn::push_kernel<ARNORM_PUSH_U, kPolPush, true>, grid, dim3(256), stream, src, first, slot_stride,
+                frags);
 }
 
 // The block of a caller's norm box int32 [parities, cap, 256] that a call of this parity uses.
