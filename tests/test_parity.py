@@ -449,6 +449,54 @@ def test_gather_max_row(lib):
     assert_bits_equal(got, oracle.gather_poll(gbox, 1, True), "gathered words (sampled columns)")
 
 
+def test_gather_range_beyond_4gib(lib):
+    """A Gather whose rows < M span more than the 4 GiB a buffer resource can address: TP=2,
+    the widest row (S = 268,435,452 words per rank, 2,147,483,616 bytes) and M=3, so the
+    poll's flat range is 6.4 GB and every block of it gets a resource of its own.  Shards are
+    drawn on the device (seeded, 3 % sentinel words); a no-copy poll, then a copying one.
+    The mailbox must end re-armed, every gathered word must equal its shard word cleaned,
+    and sampled columns of every row and rank must match the oracle's gather."""
+    import torch
+
+    tp, m = 2, 3
+    s = ((2**31 - 1) // (tp * 4)) // 4 * 4
+    assert tp * s * 4 < 2**31 and m * tp * s * 4 > 2**32
+    free, _ = torch.cuda.mem_get_info()
+    if free < 48 * 2**30:
+        pytest.skip("needs about 32 GB of free device memory")
+    say(f"[parity] gather range beyond 4 GiB: TP={tp}, M={m}, S={s}")
+    gen = torch.Generator(device="cuda").manual_seed(2026)
+    sent = torch.tensor(-(1 << 31), dtype=torch.int32, device="cuda")
+    shards = torch.empty((tp, m, s), dtype=torch.int32, device="cuda")
+    for r in range(tp):
+        for row in range(m):
+            x = torch.randint(-(1 << 31), (1 << 31) - 1, (s,), generator=gen, dtype=torch.int32, device="cuda")
+            x[torch.rand(s, generator=gen, device="cuda") < 0.03] = sent
+            shards[r, row] = x
+            del x
+    box = armed_box((m, tp * s))
+    out = torch.empty((m, tp * s), dtype=torch.int32, device="cuda")
+    assert lib.gather_push(shards, box, tp, 0) is True
+    assert lib.gather_poll(box, tp, m, copy=False) is True
+    assert lib.gather_poll(box, tp, m, out=out, copy=True) is True
+    assert lib.status() == lib.OK
+    for row in range(m):
+        assert bool((box[row] == sent).all()), f"row {row} of the mailbox not re-armed"
+        for r in range(tp):
+            sh = shards[r, row]
+            assert bool((out[row, r * s:(r + 1) * s] == torch.where(sh == sent, torch.zeros_like(sh), sh)).all()), \
+                f"row {row}, rank {r}"
+    rng = np.random.default_rng(8)
+    cols = np.sort(np.concatenate([[0, 1, s - 2, s - 1], 2 + rng.choice(s - 4, 2044, replace=False)]))
+    idx = torch.from_numpy(cols).cuda()
+    sh = host32(shards.index_select(2, idx))
+    got = host32(out.view(m, tp, s).index_select(2, idx)).reshape(m, tp * len(cols))
+    del shards, out, box
+    gbox = oracle.arm(np.empty((m, tp * len(cols)), dtype=np.uint32))
+    oracle.gather_push(gbox, sh, 0)
+    assert_bits_equal(got, oracle.gather_poll(gbox, m, True), "gathered words (sampled columns)")
+
+
 # -- edge cases ------------------------------------------------------------------
 
 
