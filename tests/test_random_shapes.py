@@ -55,10 +55,29 @@ def _draw_twoshot(rng, n):
     return cases
 
 
+def _draw_arnorm_wide(rng, n):
+    """Larger caps (up to 300 rows: the 4-way split up to M=160 and the whole-row grid that
+    loops over rows above 128), the splits of 4 and 8 ways, and the call with the library's
+    own norm box (M <= 64)."""
+    cases = []
+    for i in range(n):
+        tp = int(rng.integers(2, 9))
+        cap = int(rng.integers(1, 301))
+        m = int(rng.integers(1, cap + 1))
+        form = str(rng.choice(["pair", "one_call", "fused", "static"]))
+        if form == "static" and m > 64:
+            form = "one_call"
+        cases.append(dict(tp=tp, cap=cap, m=m, parities=int(rng.integers(1, 4)), residual=bool(rng.integers(0, 2)),
+                          torture=bool(rng.integers(0, 2)), form=form, split=int(rng.choice([0, 1, 4, 8])),
+                          threads=int(rng.choice([0, 448, 256])), rank=int(rng.integers(0, tp)), seed=4000 + i))
+    return cases
+
+
 _RNG = np.random.default_rng(20251202)
 ARNORM_CASES = _draw_arnorm(_RNG, 64)
 GATHER_CASES = _draw_gather(_RNG, 40)
 TWOSHOT_CASES = _draw_twoshot(_RNG, 40)
+ARNORM_WIDE_CASES = _draw_arnorm_wide(np.random.default_rng(20251203), 32)
 
 
 def _case_id(c):
@@ -83,6 +102,16 @@ def _bf16_rows(rng, shape):
 @pytest.mark.parametrize("c", ARNORM_CASES, ids=_case_id)
 def test_random_arnorm(lib, c):
     say(f"[random] arnorm {_case_id(c)}")
+    _run_arnorm_case(lib, c)
+
+
+@pytest.mark.parametrize("c", ARNORM_WIDE_CASES, ids=_case_id)
+def test_random_arnorm_wide(lib, c):
+    say(f"[random] arnorm wide {_case_id(c)}")
+    _run_arnorm_case(lib, c)
+
+
+def _run_arnorm_case(lib, c):
     rng = np.random.default_rng(c["seed"])
     tp, cap, m, parities = c["tp"], c["cap"], c["m"], c["parities"]
     lib.set_reduce_split(c["split"])
@@ -114,6 +143,9 @@ def test_random_arnorm(lib, c):
             assert lib.arnorm_push(dev16(p), box_d, parity, 0) is True
             oracle.arnorm_push(box_h, p, parity, 0)
             assert lib.arnorm_reduce_norm(res_d, g_d, box_d, parity, EPS, out_d, rout_d, norm_box=nbox) is True
+        elif c["form"] == "static":
+            assert lib.arnorm_push_reduce_norm_static(dev16(p), res_d, g_d, box_d, parity, EPS, out_d, rout_d) is True
+            oracle.arnorm_push(box_h, p, parity, 0)
         else:
             box_arg = nbox if c["form"] == "one_call" else None
             assert lib.arnorm_push_reduce_norm(dev16(p), res_d, g_d, box_d, parity, EPS, out_d, rout_d,
