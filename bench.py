@@ -835,7 +835,8 @@ def main():
         "higher_is_better": False,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "f32",
+        "io_dtype": "bf16: BF16 rows in and out, FP32 adds, products and norm, one BF16 rounding per stage",
         "data": "synthetic",
         "config": {
             "workload": "ArNorm TP=8 M=4 width 7168, residual=False, 2 parities alternating: one "
