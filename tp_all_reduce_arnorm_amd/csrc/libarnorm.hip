@@ -161,6 +161,17 @@ std::atomic<int> g_poll_mode{0};   // Gather polls: 0 = automatic, 1 = re-read a
 #ifndef ARNORM_TWOSHOT_STEP_MAX_BYTES
 #define ARNORM_TWOSHOT_STEP_MAX_BYTES (1u << 20)
 #endif
+// The one-launch two-shot call places an owner workgroup and the reader of the same
+// fragments on one XCD always, and their producers too from this many blocks of 256
+// fragments per slot (below it, the producers of a few blocks would crowd a few XCDs while
+// the others idle).  Measured at TP=8, width 7168, us per call (spread as before / owner
+// and reader aligned / everything aligned), blocks = 3.5 M: M=1 4.74-4.81 / 4.56-4.61 /
+// 4.89-4.92, M=2 4.89-4.90 / 4.68-4.70 / 4.99-5.02, M=4 5.23-5.25 / 5.02 / 5.61-5.62, M=6
+// 5.32-5.34 / 5.15-5.17 / 5.88-5.93, M=7 5.45-5.48 / 5.22-5.26 / 4.91-4.93, M=8
+// 5.98-6.00 / 5.75-5.77 / 4.94-4.96, M=9 5.04-5.11 / 5.16-5.18 / 5.06-5.09.
+#ifndef ARNORM_TWOSHOT_ALIGN_PRODUCERS_MIN
+#define ARNORM_TWOSHOT_ALIGN_PRODUCERS_MIN 24
+#endif
 constexpr int kPolPoll = ARNORM_POL_POLL;
 constexpr int kPolRearm = ARNORM_POL_REARM;
 constexpr int kPolPush = ARNORM_POL_PUSH;
@@ -764,7 +775,9 @@ int twoshot_push_reduce_read(const uint16_t *partial, int32_t *recv, int32_t *ga
   a.partial = reinterpret_cast<const u32x4 *>(partial);
   a.out = reinterpret_cast<u32x4 *>(out);
   a.per_slot = a.red_ctas = a.read_ctas = (frags + 255) / 256;
-  const dim3 grid(tp * a.per_slot + a.red_ctas + a.read_ctas);
+  a.red_span = (a.red_ctas + 7) / 8 * 8;
+  a.prod_span = a.per_slot >= ARNORM_TWOSHOT_ALIGN_PRODUCERS_MIN ? (a.per_slot + 7) / 8 * 8 : a.per_slot;
+  const dim3 grid(tp * a.prod_span + a.red_span + a.read_ctas);
   switch (tp) {
 #define ARNORM_TWOSHOT_STEP(T)                                                                                      \
   case T:                                                                                                           \
