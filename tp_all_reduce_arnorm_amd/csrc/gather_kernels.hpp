@@ -123,15 +123,26 @@ gather_poll_kernel(uint8_t *__restrict__ box, u32x4 *__restrict__ out, uint64_t 
 }
 
 // gather_push_poll in one launch, as the pages' Gather kernel pushes its shard and then
-// polls the gathered row: workgroups [0, TP*M*per_row) are the producers of every rank's
-// shard rows (the lowest ids, dispatched first), the rest poll the M gathered rows.
+// polls the gathered row: workgroups [0, producers) push every rank's shard rows (the
+// lowest ids, dispatched first), the rest poll the M gathered rows.
+//
+// The producers work by block of the gathered range, as the pollers do: producer b writes
+// the range's fragments b*256 .. b*256+255, each from the rank and row it belongs to, and
+// with the automatic poll layout (one fragment per thread; at most 128 blocks here, so a
+// poller each) poller b polls exactly those.  `producers` is
+// the block count rounded up to a multiple of 8 (the padding ids end at once), so that
+// producer b and poller b, whose ids then agree mod 8, sit on one XCD (workgroup ids go to
+// the eight XCDs in turn).  Measured at TP=8, µs per call, a producer per (rank, row) / per
+// block: S=896 M=1 2.63-2.65 / 2.63-2.64, M=4 2.85-2.86 / 2.63, M=8 3.00-3.01 / 2.73-2.74,
+// M=16 3.10-3.12 / 2.89-2.92; S=448 M=8 2.90-2.94 / 2.75-2.77, M=32 3.25-3.26 / 3.02;
+// S=10240 M=1 2.79-2.80 / 2.80.  Without the padding, S=896 M=1 (7 blocks) took 2.72.
 struct GatherStepArgs {
   const u32x4 *shard;  // [TP, M, F]
   uint8_t *box;        // [cap, TP*F*16 B]
   u32x4 *out;          // [M, TP*F]
   uint32_t frags;      // F = S/4 fragments of one rank's row
   uint32_t M;
-  uint32_t per_row;    // producer workgroups per (rank, row)
+  uint32_t producers;  // producer workgroups: ceil(M*TP*F / 256) rounded up to a multiple of 8
   uint32_t pollers;    // poller workgroups (poll_range over the M gathered rows)
   int copy;
   uint64_t spin_limit;
@@ -141,16 +152,18 @@ struct GatherStepArgs {
 template <int TP, int U, int POL_PUSH, int POL_LD, int POL_ST>
 __global__ void __launch_bounds__(256) gather_push_poll_kernel(GatherStepArgs a) {
   const uint32_t row_frags = TP * a.frags;
-  const uint32_t producers = TP * a.M * a.per_row;
-  if (blockIdx.x < producers) {
-    const uint32_t sm = blockIdx.x / a.per_row, chunk = blockIdx.x - sm * a.per_row;  // sm = s * M + m
-    const uint32_t s = sm / a.M, m = sm - s * a.M;
-    push_frags<POL_PUSH>(a.shard + (size_t)sm * a.frags, a.box + ((size_t)m * row_frags + (size_t)s * a.frags) * 16u,
-                         a.frags, chunk, a.per_row);
+  const uint32_t n = a.M * row_frags;  // the gathered range: the host keeps it within 512 KiB
+  if (blockIdx.x < a.producers) {
+    const uint32_t i = blockIdx.x * 256u + threadIdx.x;
+    if (i >= n) return;
+    // fragment i of the gathered rows: row m, rank s's shard, its fragment j
+    const uint32_t m = i / row_frags, c = i - m * row_frags, s = c / a.frags, j = c - s * a.frags;
+    const __amdgpu_buffer_rsrc_t r = make_rsrc(a.box, n * 16u);
+    buf_store<POL_PUSH>(clean4(nt_load(a.shard + ((size_t)s * a.M + m) * a.frags + j)), r, i * 16u);
     return;
   }
-  poll_range<POL_LD, POL_ST, U>(a.box, a.out, (uint64_t)a.M * row_frags, blockIdx.x - producers, a.pollers, a.copy,
-                                a.spin_limit, a.poll_all);
+  poll_range<POL_LD, POL_ST, U>(a.box, a.out, n, blockIdx.x - a.producers, a.pollers, a.copy, a.spin_limit,
+                                a.poll_all);
 }
 
 }  // namespace arn

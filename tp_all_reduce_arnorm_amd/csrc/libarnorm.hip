@@ -156,6 +156,7 @@ std::atomic<int> g_poll_mode{0};   // Gather polls: 0 = automatic, 1 = re-read a
 #ifndef ARNORM_GATHER_STEP_MAX_BYTES
 #define ARNORM_GATHER_STEP_MAX_BYTES (1u << 19)
 #endif
+static_assert(ARNORM_GATHER_STEP_MAX_BYTES <= (1u << 30), "the one-launch Gather range is one buffer resource");
 // twoshot_push_reduce_read runs as one launch when the TP slots of rows < M total at
 // most this many bytes, else as its three launches.
 #ifndef ARNORM_TWOSHOT_STEP_MAX_BYTES
@@ -667,13 +668,14 @@ int gather_push_poll(const int32_t *shard, int32_t *mailbox, int32_t *out, int t
   a.out = reinterpret_cast<u32x4 *>(out);
   a.frags = frags;
   a.M = (uint32_t)M;
-  a.per_row = (frags + 255) / 256;
-  const PollLayout l = poll_layout((uint64_t)M * tp * frags);
+  const uint32_t n = (uint32_t)M * tp * frags;
+  a.producers = ((n + 255) / 256 + 7) / 8 * 8;
+  const PollLayout l = poll_layout(n);
   a.pollers = l.grid;
   a.copy = copy ? 1 : 0;
   a.spin_limit = g_spin_limit.load(std::memory_order_relaxed);
   a.poll_all = poll_mode(1);
-  const dim3 grid(tp * M * a.per_row + a.pollers);
+  const dim3 grid(a.producers + a.pollers);
 #define ARNORM_GATHER_STEP(T)                                                                                      \
   case T:                                                                                                          \
     if (l.u == 1) return launch(arn::gather_push_poll_kernel<T, 1, kPolPush, kPolPoll, kPolRearm>, grid, dim3(256), \
