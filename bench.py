@@ -650,8 +650,9 @@ def summarize_profiles(outdir):
                      "23 times, each launch after a 1 GiB read-only pass (torch's float32 sum) that evicts the "
                      "last-level cache", "arnorm_tp8_m4096_kernel_stats.md"),
             ("gather", "Gather at TP=8, S=896 words, cap=64, HIP-graph replay: 2000 gather_push_poll calls "
-                       "at M=32 (917504 B, so run as the pair gather_push of 8 slots + gather_poll with "
-                       "copy), 2000 calls of that pair, then 2000 one-launch gather_push_poll calls at M=4",
+                       "at M=32 (917504 B, within the 1 MiB one-launch limit, so one launch each), 2000 calls "
+                       "of the pair gather_push of 8 slots + gather_poll with copy at M=32, then 2000 "
+                       "one-launch gather_push_poll calls at M=4",
              "gather_tp8_m32_s896_kernel_stats.md"),
             ("twoshot", "Two-shot all-reduce stand-in (owners = 1): TP=8, M=4 graph-replayed calls, 2000 as "
                         "one twoshot_push_reduce_read launch each, then 2000 as the three launches (push, "
@@ -664,13 +665,15 @@ def summarize_profiles(outdir):
                                    os.path.join(outdir, f"prof_{key}", f"{key}_kernel_trace.csv"))
         rec = _profiled_record(os.path.join(outdir, f"prof_{key}.log")) or {}
         sha = rec.get("sources_sha")
-        shapes = _shape_table(os.path.join(outdir, f"prof_{key}", f"{key}_kernel_trace.csv")) if key == "lat" else None
+        shapes = _shape_table(os.path.join(outdir, f"prof_{key}", f"{key}_kernel_trace.csv")) \
+            if key in ("lat", "gather") else None
         with open(os.path.join(prof, fname), "w") as f:
             f.write(f"# rocprofv3 kernel statistics: {title}\n\n"
                     f"Command, from the repository root on one MI355X:\n\n    {PROFILE_COMMANDS[key]}\n\n"
                     f"Kernel sources sha256[:16] = `{sha}`.\n\n{table}\n")
             if shapes:
-                f.write(f"\nThe library's kernels by launch shape (grid size in threads; M=1, 4 and 64 launch "
+                which = "M=1, 4 and 64" if key == "lat" else "M=32 and M=4"
+                f.write(f"\nThe library's kernels by launch shape (grid size in threads; {which} launch "
                         f"different grids):\n\n{shapes}\n")
             if key == "lat" and rec:
                 f.write("\nThe same profiled run's own figures, HIP events on the stream over the graph replays "
@@ -885,9 +888,10 @@ def main():
         },
         "gather": {
             "workload": "Gather TP=8 M=32 S=896 words cap=64: gather_push_poll with copy, HIP-graph replay "
-                        "(917504 B of gathered rows, above the 512 KiB one-launch limit, so it runs as "
-                        "the pair gather_push + gather_poll; the gather_tp8_m4 and logits_m1 drafter_shapes "
-                        "entries are one-launch calls); two_launch_us_per_call is the pair itself",
+                        "(917504 B of gathered rows, within the 1 MiB one-launch limit, so every rank's push "
+                        "and the pollers run as one launch; of the drafter_shapes entries the logits at "
+                        "M=4 (1.25 MiB) run as the pair gather_push + gather_poll, the others in one "
+                        "launch); two_launch_us_per_call is the pair itself",
             "us_per_call": round(gather_us, 3), "two_launch_us_per_call": round(gather_pair_us, 3),
             "push_algorithmic_bytes": gpb, "poll_algorithmic_bytes": gqb,
             "drafter_shapes": shapes,

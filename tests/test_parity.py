@@ -249,12 +249,13 @@ def test_drafter_gather_shapes(lib, name, m, tp):
         assert np.array_equal(blk[:, 1::2][~sent], src[:, 1::2][~sent]) and np.all(blk[:, 1::2][sent] == 0)
 
 
-@pytest.mark.parametrize("name,m", [("gather_tp8_m32", 32), ("gather_tp8_m32", 16), ("gather_tp8_m32", 1), ("ctx", 64), ("logits", 4),
+@pytest.mark.parametrize("name,m", [("gather_tp8_m32", 32), ("gather_tp8_m32", 16), ("gather_tp8_m32", 1),
+                                    ("gather_tp8_m32", 36), ("gather_tp8_m32", 37), ("ctx", 64), ("logits", 4),
                                     ("logits", 2), ("logits", 1)])
 def test_gather_push_poll_one_call(lib, name, m):
-    """gather_push_poll (one launch for calls within 512 KiB, else the pair) against the
-    oracle's push of every rank followed by its poll: copy, then no-copy followed by a
-    copying poll."""
+    """gather_push_poll (one launch for calls within 1 MiB, else the pair; S=896 at M=36 is
+    the last row count within it, M=37 the first above) against the oracle's push of every
+    rank followed by its poll: copy, then no-copy followed by a copying poll."""
     import dataclasses
 
     import torch
@@ -281,7 +282,8 @@ def test_gather_push_poll_one_call(lib, name, m):
 
 
 @pytest.mark.parametrize("u,mode", [(1, 2), (4, 1), (4, 2)])
-@pytest.mark.parametrize("name,m", [("gather_tp8_m32", 16), ("gather_tp8_m32", 1), ("logits", 1)])
+@pytest.mark.parametrize("name,m", [("gather_tp8_m32", 36), ("gather_tp8_m32", 16), ("gather_tp8_m32", 1), ("ctx", 64),
+                                    ("logits", 1)])
 def test_gather_poll_layouts_one_launch(lib, name, m, u, mode):
     """gather_push_poll in one launch, its pollers forced to 1 or 4 fragments per thread and
     to re-read or witness waits: the producers in the same grid are still writing when
@@ -309,7 +311,7 @@ def test_gather_poll_layouts_one_launch(lib, name, m, u, mode):
 @pytest.mark.parametrize("tp,m,s", [(8, 4096, 896), (2, 4096, 4), (4, 1024, 10240), (2, 70000, 4)])
 def test_gather_large(lib, tp, m, s):
     """Large gathers with M = cap: up to 168 MB of shards as the pair of launches, at S=4
-    one launch of 12288 workgroups, and M = 70000 rows (more than a grid's second
+    one launch over 4096 rows of 2 ranks, and M = 70000 rows (more than a grid's second
     dimension holds); through gather_push_poll with copy, then no copy followed by a
     copying gather_poll; every word and the whole mailbox compared with the oracle."""
     import dataclasses

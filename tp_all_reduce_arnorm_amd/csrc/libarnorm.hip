@@ -149,12 +149,14 @@ std::atomic<int> g_poll_mode{0};   // Gather polls: 0 = automatic, 1 = re-read a
 #endif
 // gather_push_poll runs as one launch when the gathered rows total at most this many
 // bytes, its pollers re-reading every pending fragment per pass, else as the pair
-// gather_push + gather_poll.  Measured on MI355X at TP=8 (HIP-graph replay, µs per
-// call, one launch vs pair): M=1 S=896 3.0 vs 3.9+, M=16 S=896 3.9 vs 4.8, M=1 S=10240
-// 3.2 vs 3.8, M=2 S=10240 4.1 vs 4.1, M=32 S=896 4.6 vs 4.4; above about half a MiB
-// the pollers' re-reads cost more than the launch they save.
+// gather_push + gather_poll.  Measured on MI355X at TP=8 (HIP-graph replay, µs per call,
+// the pair / one launch): S=896 M=24 3.80-3.83 / 3.12-3.14, M=32 3.81 / 3.23-3.25, M=64
+// (1.8 MB) 4.39-4.40 / 7.31-7.38; S=448 M=48 3.82-4.00 / 3.12-3.14, M=64 3.88-3.98 /
+// 3.24-3.25; S=10240 M=2 3.77-3.90 / 3.09-3.11, M=4 (1.25 MiB) 4.21-4.22 / 4.50-4.58, M=8
+// 4.71-4.80 / 8.68-8.84.  Above 1 MiB the pollers' re-reads cost more than the launch
+// they save.
 #ifndef ARNORM_GATHER_STEP_MAX_BYTES
-#define ARNORM_GATHER_STEP_MAX_BYTES (1u << 19)
+#define ARNORM_GATHER_STEP_MAX_BYTES (1u << 20)
 #endif
 static_assert(ARNORM_GATHER_STEP_MAX_BYTES <= (1u << 30), "the one-launch Gather range is one buffer resource");
 // twoshot_push_reduce_read runs as one launch when the TP slots of rows < M total at
