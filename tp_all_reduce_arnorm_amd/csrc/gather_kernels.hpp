@@ -48,11 +48,15 @@ gather_push_kernel(const u32x4 *__restrict__ shard, uint8_t *__restrict__ box, u
 // watches one witness (the first pending fragment of its lowest waiting lane; every lane
 // loads the same 16 B) and its lanes re-read their own pending fragments only once that is
 // published; a small range (poll_all) re-reads every pending fragment on each pass
-// instead, so the data arrives with the news.  The copy is stored with the default cache
-// policy, as the ArNorm consumer stores its rows: the last-level cache keeps it for the
-// next reader (a non-temporal store made the one-slot read at M=4096, width 7168, 35.0
-// against 32.0 us from HBM, and changed nothing at small M).
-template <int POL_LD, int POL_ST, int U>
+// instead, so the data arrives with the news.  The copy is stored with the cache policy
+// POL_CP through a buffer resource per block.  Device scope (sc1) measured best: with the
+// default policy the one-slot read at M=4096, width 7168 fetched 2 MB more than the 58.7
+// MB it reads (1.0135 x its algorithmic bytes in all; 1.0004 with sc1) and took 31.6-31.8
+// against 29.3-30.2 us from HBM; TP=8 Gathers at M=4 (one launch) 2.72-2.74 against
+// 2.55-2.58 us, logits at M=4 (the pair) 4.20-4.21 against 3.97-3.98, the two-shot call at
+// M=4 5.03-5.05 against 4.91-4.92.  A non-temporal store was slower (35.0 against 32.0 us
+// at M=4096).
+template <int POL_LD, int POL_ST, int POL_CP, int U>
 __device__ __forceinline__ void poll_range(uint8_t *box, u32x4 *out, uint64_t n, uint32_t w, uint32_t W, int copy,
                                            uint64_t spin_limit, int poll_all) {
   constexpr uint32_t kBlk = 256u * U;
@@ -102,11 +106,11 @@ __device__ __forceinline__ void poll_range(uint8_t *box, u32x4 *out, uint64_t n,
         }
     }
     if (copy) {
-      u32x4 *oblk = out + first;
+      const __amdgpu_buffer_rsrc_t o = make_rsrc(out + first, cnt * 16u);
 #pragma unroll
       for (int u = 0; u < U; ++u)
         if (idx[u] < cnt && !((pend >> u) & 1u)) {
-          oblk[idx[u]] = v[u];
+          buf_store<POL_CP>(v[u], o, idx[u] * 16u);
           buf_store<POL_ST>(sentinel4(), r, idx[u] * 16u);
         }
     }
@@ -115,11 +119,11 @@ __device__ __forceinline__ void poll_range(uint8_t *box, u32x4 *out, uint64_t n,
 
 // gather_poll: the M rows < M as one range of n fragments, U fragments per thread in
 // flight; the grid (at most 1024 workgroups) is resident at once.
-template <int POL_LD, int POL_ST, int U>
+template <int POL_LD, int POL_ST, int POL_CP, int U>
 __global__ void __launch_bounds__(256)
 gather_poll_kernel(uint8_t *__restrict__ box, u32x4 *__restrict__ out, uint64_t n, int copy, uint64_t spin_limit,
                    int poll_all) {
-  poll_range<POL_LD, POL_ST, U>(box, out, n, blockIdx.x, gridDim.x, copy, spin_limit, poll_all);
+  poll_range<POL_LD, POL_ST, POL_CP, U>(box, out, n, blockIdx.x, gridDim.x, copy, spin_limit, poll_all);
 }
 
 // gather_push_poll in one launch, as the pages' Gather kernel pushes its shard and then
@@ -149,7 +153,7 @@ struct GatherStepArgs {
   int poll_all;
 };
 
-template <int TP, int U, int POL_PUSH, int POL_LD, int POL_ST>
+template <int TP, int U, int POL_PUSH, int POL_LD, int POL_ST, int POL_CP>
 __global__ void __launch_bounds__(256) gather_push_poll_kernel(GatherStepArgs a) {
   const uint32_t row_frags = TP * a.frags;
   const uint32_t n = a.M * row_frags;  // the gathered range: the host keeps it within 1 MiB
@@ -162,7 +166,7 @@ __global__ void __launch_bounds__(256) gather_push_poll_kernel(GatherStepArgs a)
     buf_store<POL_PUSH>(clean4(nt_load(a.shard + ((size_t)s * a.M + m) * a.frags + j)), r, i * 16u);
     return;
   }
-  poll_range<POL_LD, POL_ST, U>(a.box, a.out, n, blockIdx.x - a.producers, a.pollers, a.copy, a.spin_limit,
+  poll_range<POL_LD, POL_ST, POL_CP, U>(a.box, a.out, n, blockIdx.x - a.producers, a.pollers, a.copy, a.spin_limit,
                                 a.poll_all);
 }
 

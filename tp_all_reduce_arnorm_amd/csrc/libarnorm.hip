@@ -55,10 +55,14 @@ std::atomic<int> g_poll_mode{0};   // Gather polls: 0 = automatic, 1 = re-read a
 // (nothing reads the sentinel back until the next push of that parity overwrites it);
 // the residual (and the own partial of the fused form), read once, is non-temporal
 // (TP=8, M=4096: 84 against 83.4 % of 8 TB/s right after the push, 75.2 against 74.3 %
-// from HBM); the output rows use the default policy.  Measured on MI355X at TP=8, M=4096: the
-// non-temporal re-arm took the consumer from 201 to 169 us, while a non-temporal slot
-// read slowed it (183 us) and a non-temporal push slowed the small-M calls.  The
-// macros let a build measure other choices.
+// from HBM).  Measured on MI355X at TP=8, M=4096: the non-temporal re-arm took the
+// consumer from 201 to 169 us, while a non-temporal slot read slowed it (183 us) and a
+// non-temporal push slowed the small-M calls.  The ArNorm output rows (out, residual_out)
+// and the polls' copies (Gather out, the two-shot read) are stored at device scope too:
+// against the default policy, the consumer at M=4096 from HBM 186.2-186.7 against
+// 188.0-188.6 us (right after the push unchanged, 165.9-167.3 against 166.6-166.8), the
+// ArNorm call at M=64 6.74-6.81 against 6.91-6.93 us and at M=8 4.92 against 4.96; the
+// copies as in poll_range.  The macros let a build measure other choices.
 #ifndef ARNORM_POL_POLL
 #define ARNORM_POL_POLL 16
 #endif
@@ -72,7 +76,10 @@ std::atomic<int> g_poll_mode{0};   // Gather polls: 0 = automatic, 1 = re-read a
 #define ARNORM_POL_IN 2
 #endif
 #ifndef ARNORM_POL_IO
-#define ARNORM_POL_IO 0
+#define ARNORM_POL_IO 16
+#endif
+#ifndef ARNORM_POL_COPY
+#define ARNORM_POL_COPY 16
 #endif
 // Producer kernel (arnorm_push, twoshot_push) layout: 2 fragments per thread while a
 // slot's rows total at most ARNORM_PUSH_SMALL_BYTES, else one fragment per thread with
@@ -180,6 +187,7 @@ constexpr int kPolRearm = ARNORM_POL_REARM;
 constexpr int kPolPush = ARNORM_POL_PUSH;
 constexpr int kPolIn = ARNORM_POL_IN;  // the caller's rows read once (residual, own partial)
 constexpr int kPolIO = ARNORM_POL_IO;  // the caller's output rows
+constexpr int kPolCopy = ARNORM_POL_COPY;  // a poll's copy of the rows it read
 
 // Up to this many rows a whole-row consumer gets one workgroup per row without asking
 // the runtime for the resident grid (any GPU of this family holds that many at once).
@@ -390,9 +398,11 @@ int launch_poll(uint8_t *box, u32x4 *out, uint32_t row_frags, int M, int copy, h
   const uint64_t spin = g_spin_limit.load(std::memory_order_relaxed);
   const PollLayout l = poll_layout(n);
   if (l.u == 1)
-    return launch(arn::gather_poll_kernel<kPolPoll, kPolRearm, 1>, dim3(l.grid), dim3(256), stream, box, out, n,
+    return launch(arn::gather_poll_kernel<kPolPoll, kPolRearm, kPolCopy, 1>, dim3(l.grid), dim3(256), stream, box,
+                  out, n,
                   copy ? 1 : 0, spin, poll_all);
-  return launch(arn::gather_poll_kernel<kPolPoll, kPolRearm, ARNORM_POLL_U>, dim3(l.grid), dim3(256), stream, box,
+  return launch(arn::gather_poll_kernel<kPolPoll, kPolRearm, kPolCopy, ARNORM_POLL_U>, dim3(l.grid), dim3(256), stream,
+                box,
                 out, n, copy ? 1 : 0, spin, poll_all);
 }
 
@@ -680,10 +690,11 @@ int gather_push_poll(const int32_t *shard, int32_t *mailbox, int32_t *out, int t
   const dim3 grid(a.producers + a.pollers);
 #define ARNORM_GATHER_STEP(T)                                                                                      \
   case T:                                                                                                          \
-    if (l.u == 1) return launch(arn::gather_push_poll_kernel<T, 1, kPolPush, kPolPoll, kPolRearm>, grid, dim3(256), \
-                                stream, a);                                                                        \
-    return launch(arn::gather_push_poll_kernel<T, ARNORM_POLL_U, kPolPush, kPolPoll, kPolRearm>, grid, dim3(256),    \
-                  stream, a);
+    if (l.u == 1)                                                                                                  \
+      return launch(arn::gather_push_poll_kernel<T, 1, kPolPush, kPolPoll, kPolRearm, kPolCopy>, grid, dim3(256),  \
+                    stream, a);                                                                                    \
+    return launch(arn::gather_push_poll_kernel<T, ARNORM_POLL_U, kPolPush, kPolPoll, kPolRearm, kPolCopy>, grid,   \
+                  dim3(256), stream, a);
   switch (tp) {
     ARNORM_GATHER_STEP(2)
     ARNORM_GATHER_STEP(3)
@@ -785,7 +796,8 @@ int twoshot_push_reduce_read(const uint16_t *partial, int32_t *recv, int32_t *ga
   switch (tp) {
 #define ARNORM_TWOSHOT_STEP(T)                                                                                      \
   case T:                                                                                                           \
-    return launch(arn::twoshot_step_kernel<T, kPolPush, kPolPoll, kPolRearm, kPolPush>, grid, dim3(256), stream, a);
+    return launch(arn::twoshot_step_kernel<T, kPolPush, kPolPoll, kPolRearm, kPolPush, kPolCopy>, grid, dim3(256),    \
+                  stream, a);
     ARNORM_TWOSHOT_STEP(2)
     ARNORM_TWOSHOT_STEP(3)
     ARNORM_TWOSHOT_STEP(4)
