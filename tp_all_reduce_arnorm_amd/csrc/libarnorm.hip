@@ -137,8 +137,29 @@ std::atomic<int> g_poll_mode{0};   // Gather polls: 0 = automatic, 1 = re-read a
 //   then 4 fragments per producer thread (2 / 4): M=2 4.49 / 4.41, M=3 4.52 / 4.46,
 //   M=4 4.61 / 4.50, M=5 4.70 / 4.82, M=6 4.80 / 4.91;
 // the exchange stays in one L2 while the rows are few, and crowds the XCDs after.
+// Above this M the one-launch kernel also re-arms the slots it read with
+// ARNORM_POL_REARM_STEP (device scope without the non-temporal bit) instead of
+// ARNORM_POL_REARM.  Measured later, on six boxes, the rows on one XCD with 4 fragments
+// per producer thread and non-temporal re-arms (as above) against the consumers spread
+// with 2 per thread and device-scope re-arms, medians of 4-8 alternations per box, us:
+// M=1 4.09-4.12 / 4.10-4.11 (the spread layout with non-temporal re-arms: 4.35-4.36);
+// M=2 4.25-4.31 / 4.10-4.16 on every box; M=3 4.31-4.34 / 4.13-4.14; M=4 4.34-4.38 /
+// 4.11-4.33 on five boxes and 4.43 / 4.59 on the sixth; M=8 4.90-5.06 / 4.74-4.97;
+// M=9 5.00-5.10 / 4.86-5.03; M=5..7 mixed, -0.25..+0.12.  So one XCD per row for M=1 only.
 #ifndef ARNORM_XCD_ROWS_MAX_M
-#define ARNORM_XCD_ROWS_MAX_M 4
+#define ARNORM_XCD_ROWS_MAX_M 1
+#endif
+// The re-arm stores inside the one-launch calls (ArNorm from M=2, the Gather and the
+// two-shot call), whose pollers re-read lines while their producers write them: device
+// scope without the non-temporal bit.  Against ARNORM_POL_REARM (medians of 4
+// alternations on one box, us per call): Gathers at TP=8, S=896, M=4 2.54 / 2.28, M=16
+// 2.77 / 2.38, M=32 3.29 / 2.99; logits at M=1 2.68 / 2.34; the context-projection gather
+// (S=448, M=64) 3.25 / 2.97; the two-shot call at M=1 4.50 / 4.09, M=4 4.91 / 4.53, M=8
+// 4.70 / 4.29.  The launches that run after their producer (the pair of ArNorm launches,
+// gather_poll, twoshot_reduce and twoshot_read) keep ARNORM_POL_REARM: the ArNorm pair at
+// M=12..128 measured the same with either, and the M=4096 kernels faster with it.
+#ifndef ARNORM_POL_REARM_STEP
+#define ARNORM_POL_REARM_STEP 16
 #endif
 #ifndef ARNORM_STEP_PUSH_U_FEW
 #define ARNORM_STEP_PUSH_U_FEW 4
@@ -184,6 +205,7 @@ static_assert(ARNORM_GATHER_STEP_MAX_BYTES <= (1u << 30), "the one-launch Gather
 #endif
 constexpr int kPolPoll = ARNORM_POL_POLL;
 constexpr int kPolRearm = ARNORM_POL_REARM;
+constexpr int kPolRearmStep = ARNORM_POL_REARM_STEP;  // re-arms inside the one-launch calls
 constexpr int kPolPush = ARNORM_POL_PUSH;
 constexpr int kPolIn = ARNORM_POL_IN;  // the caller's rows read once (residual, own partial)
 constexpr int kPolIO = ARNORM_POL_IO;  // the caller's output rows
@@ -503,14 +525,14 @@ int push_reduce_norm_launch(const uint16_t *partials, const uint16_t *residual, 
   a.xcd_rows = few;
   const dim3 grid(tp * a.per_slot + (few ? (M + 7) / 8 * 8 * K : M * K));
   const bool res = residual != nullptr;
-#define ARNORM_STEP_LAUNCH_U(TPV, KV, UV)                                                                          \
-  return res ? launch(arn::push_reduce_kernel<TPV, true, KV, UV, kPolPush, kPolPoll, kPolRearm, kPolIn, kPolIO>,    \
-                      grid, dim3(nt), stream, a)                                                                   \
-             : launch(arn::push_reduce_kernel<TPV, false, KV, UV, kPolPush, kPolPoll, kPolRearm, kPolIn, kPolIO>,   \
-                      grid, dim3(nt), stream, a);
+#define ARNORM_STEP_LAUNCH_U(TPV, KV, UV, PR)                                                                      \
+  return res ? launch(arn::push_reduce_kernel<TPV, true, KV, UV, kPolPush, kPolPoll, PR, kPolIn, kPolIO>, grid,     \
+                      dim3(nt), stream, a)                                                                         \
+             : launch(arn::push_reduce_kernel<TPV, false, KV, UV, kPolPush, kPolPoll, PR, kPolIn, kPolIO>, grid,    \
+                      dim3(nt), stream, a);
 #define ARNORM_STEP_LAUNCH_K(TPV, KV)                                                                              \
-  if (few) ARNORM_STEP_LAUNCH_U(TPV, KV, ARNORM_STEP_PUSH_U_FEW)                                                   \
-  ARNORM_STEP_LAUNCH_U(TPV, KV, ARNORM_STEP_PUSH_U)
+  if (few) ARNORM_STEP_LAUNCH_U(TPV, KV, ARNORM_STEP_PUSH_U_FEW, kPolRearm)                                        \
+  ARNORM_STEP_LAUNCH_U(TPV, KV, ARNORM_STEP_PUSH_U, kPolRearmStep)
 #define ARNORM_STEP_LAUNCH(TPV)                                                                                   \
   case TPV:                                                                                                      \
     if (K == 4) {                                                                                                \
@@ -691,10 +713,11 @@ int gather_push_poll(const int32_t *shard, int32_t *mailbox, int32_t *out, int t
 #define ARNORM_GATHER_STEP(T)                                                                                      \
   case T:                                                                                                          \
     if (l.u == 1)                                                                                                  \
-      return launch(arn::gather_push_poll_kernel<T, 1, kPolPush, kPolPoll, kPolRearm, kPolCopy>, grid, dim3(256),  \
+      return launch(arn::gather_push_poll_kernel<T, 1, kPolPush, kPolPoll, kPolRearmStep, kPolCopy>, grid,         \
+                    dim3(256),                                                                                     \
                     stream, a);                                                                                    \
-    return launch(arn::gather_push_poll_kernel<T, ARNORM_POLL_U, kPolPush, kPolPoll, kPolRearm, kPolCopy>, grid,   \
-                  dim3(256), stream, a);
+    return launch(arn::gather_push_poll_kernel<T, ARNORM_POLL_U, kPolPush, kPolPoll, kPolRearmStep, kPolCopy>,     \
+                  grid, dim3(256), stream, a);
   switch (tp) {
     ARNORM_GATHER_STEP(2)
     ARNORM_GATHER_STEP(3)
@@ -796,7 +819,8 @@ int twoshot_push_reduce_read(const uint16_t *partial, int32_t *recv, int32_t *ga
   switch (tp) {
 #define ARNORM_TWOSHOT_STEP(T)                                                                                      \
   case T:                                                                                                           \
-    return launch(arn::twoshot_step_kernel<T, kPolPush, kPolPoll, kPolRearm, kPolPush, kPolCopy>, grid, dim3(256),    \
+    return launch(arn::twoshot_step_kernel<T, kPolPush, kPolPoll, kPolRearmStep, kPolPush, kPolCopy>, grid,          \
+                  dim3(256),                                                                                        \
                   stream, a);
     ARNORM_TWOSHOT_STEP(2)
     ARNORM_TWOSHOT_STEP(3)
