@@ -650,7 +650,7 @@ def summarize_profiles(outdir):
                      "23 times, each launch after a 1 GiB read-only pass (torch's float32 sum) that evicts the "
                      "last-level cache", "arnorm_tp8_m4096_kernel_stats.md"),
             ("gather", "Gather at TP=8, S=896 words, cap=64, HIP-graph replay: 2000 gather_push_poll calls "
-                       "at M=32 (917504 B, within the 1 MiB one-launch limit, so one launch each), 2000 calls "
+                       "at M=32 (917504 B, within the 1.5 MiB one-launch limit, so one launch each), 2000 calls "
                        "of the pair gather_push of 8 slots + gather_poll with copy at M=32, then 2000 "
                        "one-launch gather_push_poll calls at M=4",
              "gather_tp8_m32_s896_kernel_stats.md"),
@@ -888,10 +888,9 @@ def main():
         },
         "gather": {
             "workload": "Gather TP=8 M=32 S=896 words cap=64: gather_push_poll with copy, HIP-graph replay "
-                        "(917504 B of gathered rows, within the 1 MiB one-launch limit, so every rank's push "
-                        "and the pollers run as one launch; of the drafter_shapes entries the logits at "
-                        "M=4 (1.25 MiB) run as the pair gather_push + gather_poll, the others in one "
-                        "launch); two_launch_us_per_call is the pair itself",
+                        "(917504 B of gathered rows, within the 1.5 MiB one-launch limit, so every rank's push "
+                        "and the pollers run as one launch, as do all drafter_shapes entries); "
+                        "two_launch_us_per_call is the pair gather_push + gather_poll",
             "us_per_call": round(gather_us, 3), "two_launch_us_per_call": round(gather_pair_us, 3),
             "push_algorithmic_bytes": gpb, "poll_algorithmic_bytes": gqb,
             "drafter_shapes": shapes,

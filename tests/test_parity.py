@@ -250,11 +250,11 @@ def test_drafter_gather_shapes(lib, name, m, tp):
 
 
 @pytest.mark.parametrize("name,m", [("gather_tp8_m32", 32), ("gather_tp8_m32", 16), ("gather_tp8_m32", 1),
-                                    ("gather_tp8_m32", 36), ("gather_tp8_m32", 37), ("ctx", 64), ("logits", 4),
+                                    ("gather_tp8_m32", 54), ("gather_tp8_m32", 55), ("ctx", 64), ("logits", 4),
                                     ("logits", 2), ("logits", 1)])
 def test_gather_push_poll_one_call(lib, name, m):
-    """gather_push_poll (one launch for calls within 1 MiB, else the pair; S=896 at M=36 is
-    the last row count within it, M=37 the first above) against the oracle's push of every
+    """gather_push_poll (one launch for calls within 1.5 MiB, else the pair; S=896 at M=54 is
+    the last row count within it, M=55 the first above) against the oracle's push of every
     rank followed by its poll: copy, then no-copy followed by a copying poll."""
     import dataclasses
 
@@ -282,8 +282,8 @@ def test_gather_push_poll_one_call(lib, name, m):
 
 
 @pytest.mark.parametrize("u,mode", [(1, 2), (4, 1), (4, 2)])
-@pytest.mark.parametrize("name,m", [("gather_tp8_m32", 36), ("gather_tp8_m32", 16), ("gather_tp8_m32", 1), ("ctx", 64),
-                                    ("logits", 1)])
+@pytest.mark.parametrize("name,m", [("gather_tp8_m32", 54), ("gather_tp8_m32", 16), ("gather_tp8_m32", 1), ("ctx", 64),
+                                    ("logits", 4), ("logits", 1)])
 def test_gather_poll_layouts_one_launch(lib, name, m, u, mode):
     """gather_push_poll in one launch, its pollers forced to 1 or 4 fragments per thread and
     to re-read or witness waits: the producers in the same grid are still writing when

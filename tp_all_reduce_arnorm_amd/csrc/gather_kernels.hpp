@@ -132,7 +132,7 @@ gather_poll_kernel(uint8_t *__restrict__ box, u32x4 *__restrict__ out, uint64_t 
 //
 // The producers work by block of the gathered range, as the pollers do: producer b writes
 // the range's fragments b*256 .. b*256+255, each from the rank and row it belongs to, and
-// with the automatic poll layout (one fragment per thread; at most 256 blocks here, so a
+// with the automatic poll layout (one fragment per thread; at most 384 blocks here, so a
 // poller each) poller b polls exactly those.  `producers` is
 // the block count rounded up to a multiple of 8 (the padding ids end at once), so that
 // producer b and poller b, whose ids then agree mod 8, sit on one XCD (workgroup ids go to
@@ -156,7 +156,7 @@ struct GatherStepArgs {
 template <int TP, int U, int POL_PUSH, int POL_LD, int POL_ST, int POL_CP>
 __global__ void __launch_bounds__(256) gather_push_poll_kernel(GatherStepArgs a) {
   const uint32_t row_frags = TP * a.frags;
-  const uint32_t n = a.M * row_frags;  // the gathered range: the host keeps it within 1 MiB
+  const uint32_t n = a.M * row_frags;  // the gathered range: the host keeps it within 1.5 MiB
   if (blockIdx.x < a.producers) {
     const uint32_t i = blockIdx.x * 256u + threadIdx.x;
     if (i >= n) return;

@@ -178,13 +178,13 @@ std::atomic<int> g_poll_mode{0};   // Gather polls: 0 = automatic, 1 = re-read a
 // gather_push_poll runs as one launch when the gathered rows total at most this many
 // bytes, its pollers re-reading every pending fragment per pass, else as the pair
 // gather_push + gather_poll.  Measured on MI355X at TP=8 (HIP-graph replay, µs per call,
-// the pair / one launch): S=896 M=24 3.80-3.83 / 3.12-3.14, M=32 3.81 / 3.23-3.25, M=64
-// (1.8 MB) 4.39-4.40 / 7.31-7.38; S=448 M=48 3.82-4.00 / 3.12-3.14, M=64 3.88-3.98 /
-// 3.24-3.25; S=10240 M=2 3.77-3.90 / 3.09-3.11, M=4 (1.25 MiB) 4.21-4.22 / 4.50-4.58, M=8
-// 4.71-4.80 / 8.68-8.84.  Above 1 MiB the pollers' re-reads cost more than the launch
-// they save.
+// the pair / one launch, the one launch re-arming with ARNORM_POL_REARM_STEP): S=896 M=32
+// (0.92 MB) 3.66-3.72 / 2.99, M=40 (1.15 MB) 3.90 / 3.24, M=48 (1.38 MB) 3.98 / 3.51, M=52
+// (1.49 MB) 4.01 / 3.67, M=56 (1.61 MB) 4.04 / 3.91, M=60 (1.72 MB) 4.06 / 4.42, M=64 4.13 /
+// 4.90; S=10240 M=4 (1.31 MB) 3.96-3.97 / 3.47-3.48, M=5 (1.64 MB) 4.09 / 4.28, M=6 4.18 /
+// 5.74.  Above about 1.6 MB the pollers' re-reads cost more than the launch they save.
 #ifndef ARNORM_GATHER_STEP_MAX_BYTES
-#define ARNORM_GATHER_STEP_MAX_BYTES (1u << 20)
+#define ARNORM_GATHER_STEP_MAX_BYTES (3u << 19)
 #endif
 static_assert(ARNORM_GATHER_STEP_MAX_BYTES <= (1u << 30), "the one-launch Gather range is one buffer resource");
 // twoshot_push_reduce_read runs as one launch when the TP slots of rows < M total at
