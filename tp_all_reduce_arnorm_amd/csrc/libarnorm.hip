@@ -188,9 +188,14 @@ std::atomic<int> g_poll_mode{0};   // Gather polls: 0 = automatic, 1 = re-read a
 #endif
 static_assert(ARNORM_GATHER_STEP_MAX_BYTES <= (1u << 30), "the one-launch Gather range is one buffer resource");
 // twoshot_push_reduce_read runs as one launch when the TP slots of rows < M total at
-// most this many bytes, else as its three launches.
+// most this many bytes, its owners and readers re-reading every pending fragment on each
+// poll pass, else as its three launches.  Measured at TP=8, width 7168, with the re-arms of
+// ARNORM_POL_REARM_STEP (us per call, medians of 3 on one box, three launches / one):
+// M=10 6.34 / 4.88-4.90, M=12 6.37 / 4.85-4.86, M=16 6.43-6.44 / 4.82-4.83, M=24 6.58-6.66 /
+// 5.66-5.71, M=32 6.84-6.87 / 6.50-6.59, M=40 7.16-7.18 / 7.16-7.19, M=48 7.48-7.54 /
+// 7.77-7.84, M=96 11.38-11.45 / 11.63-11.81, M=128 13.11-13.12 / 13.69-13.75.
 #ifndef ARNORM_TWOSHOT_STEP_MAX_BYTES
-#define ARNORM_TWOSHOT_STEP_MAX_BYTES (1u << 20)
+#define ARNORM_TWOSHOT_STEP_MAX_BYTES (4u << 20)
 #endif
 // The one-launch two-shot call places an owner workgroup and the reader of the same
 // fragments on one XCD always, and their producers too from this many blocks of 256
@@ -809,7 +814,7 @@ int twoshot_push_reduce_read(const uint16_t *partial, int32_t *recv, int32_t *ga
   a.r.slot_stride = (size_t)cap * row_bytes;
   a.r.frags = frags;
   a.r.spin_limit = g_spin_limit.load(std::memory_order_relaxed);
-  a.r.poll_all = (uint64_t)tp * frags * 16u <= ARNORM_POLL_ALL_MAX_BYTES;
+  a.r.poll_all = 1;
   a.partial = reinterpret_cast<const u32x4 *>(partial);
   a.out = reinterpret_cast<u32x4 *>(out);
   a.per_slot = a.red_ctas = a.read_ctas = (frags + 255) / 256;
