@@ -129,30 +129,27 @@ std::atomic<int> g_poll_mode{0};   // Gather polls: 0 = automatic, 1 = re-read a
 #define ARNORM_STEP_PUSH_U 2
 #endif
 // arnorm_push_reduce_norm, one-launch form, few rows: up to this M a row's consumer
-// workgroups are placed on one XCD (push_reduce_kernel, xcd_rows) and the producers take
-// ARNORM_STEP_PUSH_U_FEW fragments per thread (half as many producer workgroups).
-// Measured on MI355X at TP=8 (us per call, HIP-graph replay):
-//   one XCD per row (spread / one XCD): M=1 4.44 / 4.21, M=2 4.52 / 4.44, M=3 4.58 /
-//   4.56, M=4 4.64 / 4.59, M=5 4.67 / 4.69, M=6 4.74 / 4.91, M=8 5.14 / 5.21;
-//   then 4 fragments per producer thread (2 / 4): M=2 4.49 / 4.41, M=3 4.52 / 4.46,
-//   M=4 4.61 / 4.50, M=5 4.70 / 4.82, M=6 4.80 / 4.91;
-// the exchange stays in one L2 while the rows are few, and crowds the XCDs after.
-// Above this M the one-launch kernel also re-arms the slots it read with
-// ARNORM_POL_REARM_STEP (device scope without the non-temporal bit) instead of
-// ARNORM_POL_REARM.  Measured later, on six boxes, the rows on one XCD with 4 fragments
-// per producer thread and non-temporal re-arms (as above) against the consumers spread
-// with 2 per thread and device-scope re-arms, medians of 4-8 alternations per box, us:
-// M=1 4.09-4.12 / 4.10-4.11 (the spread layout with non-temporal re-arms: 4.35-4.36);
-// M=2 4.25-4.31 / 4.10-4.16 on every box; M=3 4.31-4.34 / 4.13-4.14; M=4 4.34-4.38 /
-// 4.11-4.33 on five boxes and 4.43 / 4.59 on the sixth; M=8 4.90-5.06 / 4.74-4.97;
-// M=9 5.00-5.10 / 4.86-5.03; M=5..7 mixed, -0.25..+0.12.  So one XCD per row for M=1 only.
+// workgroups are placed on one XCD (push_reduce_kernel, xcd_rows), above it they are
+// spread over the XCDs.  Measured on MI355X at TP=8, us per call, HIP-graph replay,
+// medians of 4 alternations per box (fresh buffers each time), 2 fragments per producer
+// thread and device-scope re-arms (ARNORM_POL_REARM_STEP) in both, one XCD per row /
+// spread: M=1 3.73-3.88 / 4.12-4.14, M=2 3.96-4.00 / 4.13, M=3 3.99-4.02 / 4.11-4.19, M=4
+// 4.21-4.44 / 4.14-4.35.  Earlier layouts, on six boxes: one XCD per row up to M=4 with 4
+// fragments per producer thread and non-temporal re-arms took M=1 4.09-4.12, M=2
+// 4.25-4.31, M=3 4.31-4.34, M=4 4.34-4.43; one XCD per row with 4 per thread and
+// device-scope re-arms M=1 4.15, M=4 4.78-4.84; spread with non-temporal re-arms M=1
+// 4.35-4.36, M=4 4.51-4.52.  With few rows a row's norm-box exchange stays in one L2;
+// from M=4 the rows crowd their XCDs.
 #ifndef ARNORM_XCD_ROWS_MAX_M
-#define ARNORM_XCD_ROWS_MAX_M 1
+#define ARNORM_XCD_ROWS_MAX_M 3
 #endif
-// The re-arm stores inside the one-launch calls (ArNorm from M=2, the Gather and the
-// two-shot call), whose pollers re-read lines while their producers write them: device
-// scope without the non-temporal bit.  Against ARNORM_POL_REARM (medians of 4
-// alternations on one box, us per call): Gathers at TP=8, S=896, M=4 2.54 / 2.28, M=16
+// The re-arm stores inside the one-launch calls (ArNorm, the Gather and the two-shot
+// call), whose pollers re-read lines while their producers write them: device scope
+// without the non-temporal bit.  ArNorm: see ARNORM_XCD_ROWS_MAX_M, and on six boxes, the
+// consumers spread with these re-arms against one XCD per row with non-temporal ones,
+// M=2 4.25-4.31 / 4.10-4.16, M=4 4.34-4.38 / 4.11-4.33 on five boxes (4.43 / 4.59 on the
+// sixth), M=8 4.90-5.06 / 4.74-4.97, M=9 5.00-5.10 / 4.86-5.03, M=5..7 mixed, -0.25..+0.12.
+// The others against ARNORM_POL_REARM (medians of 4 alternations on one box, us per call): Gathers at TP=8, S=896, M=4 2.54 / 2.28, M=16
 // 2.77 / 2.38, M=32 3.29 / 2.99; logits at M=1 2.68 / 2.34; the context-projection gather
 // (S=448, M=64) 3.25 / 2.97; the two-shot call at M=1 4.50 / 4.09, M=4 4.91 / 4.53, M=8
 // 4.70 / 4.29.  The launches that run after their producer (the pair of ArNorm launches,
@@ -160,9 +157,6 @@ std::atomic<int> g_poll_mode{0};   // Gather polls: 0 = automatic, 1 = re-read a
 // M=12..128 measured the same with either, and the M=4096 kernels faster with it.
 #ifndef ARNORM_POL_REARM_STEP
 #define ARNORM_POL_REARM_STEP 16
-#endif
-#ifndef ARNORM_STEP_PUSH_U_FEW
-#define ARNORM_STEP_PUSH_U_FEW 4
 #endif
 // Fragments per thread in flight in a Gather poll whose grid is capped below a thread
 // per fragment.
@@ -524,20 +518,19 @@ int push_reduce_norm_launch(const uint16_t *partials, const uint16_t *residual, 
   a.partials = reinterpret_cast<const u32x4 *>(partials);
   a.frags = (uint32_t)M * arn::kRowFrags;
   const bool few = M <= ARNORM_XCD_ROWS_MAX_M;
-  const int U = few ? ARNORM_STEP_PUSH_U_FEW : ARNORM_STEP_PUSH_U;
+  const int U = ARNORM_STEP_PUSH_U;
   const uint32_t nt = arn::split_threads(K);
   a.per_slot = (a.frags + nt * U - 1) / (nt * U);
   a.xcd_rows = few;
   const dim3 grid(tp * a.per_slot + (few ? (M + 7) / 8 * 8 * K : M * K));
   const bool res = residual != nullptr;
-#define ARNORM_STEP_LAUNCH_U(TPV, KV, UV, PR)                                                                      \
-  return res ? launch(arn::push_reduce_kernel<TPV, true, KV, UV, kPolPush, kPolPoll, PR, kPolIn, kPolIO>, grid,     \
-                      dim3(nt), stream, a)                                                                         \
-             : launch(arn::push_reduce_kernel<TPV, false, KV, UV, kPolPush, kPolPoll, PR, kPolIn, kPolIO>, grid,    \
-                      dim3(nt), stream, a);
 #define ARNORM_STEP_LAUNCH_K(TPV, KV)                                                                              \
-  if (few) ARNORM_STEP_LAUNCH_U(TPV, KV, ARNORM_STEP_PUSH_U_FEW, kPolRearm)                                        \
-  ARNORM_STEP_LAUNCH_U(TPV, KV, ARNORM_STEP_PUSH_U, kPolRearmStep)
+  return res ? launch(arn::push_reduce_kernel<TPV, true, KV, ARNORM_STEP_PUSH_U, kPolPush, kPolPoll, kPolRearmStep,  \
+                                              kPolIn, kPolIO>,                                                     \
+                      grid, dim3(nt), stream, a)                                                                   \
+             : launch(arn::push_reduce_kernel<TPV, false, KV, ARNORM_STEP_PUSH_U, kPolPush, kPolPoll, kPolRearmStep, \
+                                              kPolIn, kPolIO>,                                                     \
+                      grid, dim3(nt), stream, a);
 #define ARNORM_STEP_LAUNCH(TPV)                                                                                   \
   case TPV:                                                                                                      \
     if (K == 4) {                                                                                                \
@@ -561,7 +554,6 @@ int push_reduce_norm_launch(const uint16_t *partials, const uint16_t *residual, 
   }
 #undef ARNORM_STEP_LAUNCH
 #undef ARNORM_STEP_LAUNCH_K
-#undef ARNORM_STEP_LAUNCH_U
   return ARNORM_NOT_SERVED;
 }
 
