@@ -124,6 +124,18 @@ std::atomic<int> g_poll_mode{0};   // Gather polls: 0 = automatic, 1 = re-read a
 #ifndef ARNORM_SPLIT4_MAX_M
 #define ARNORM_SPLIT4_MAX_M 160
 #endif
+// The one-launch call splits rows 8 ways from ARNORM_STEP_SPLIT8_MIN_M to
+// ARNORM_STEP_SPLIT8_MAX_M rows (when the split is automatic).  Measured at TP=8 with the
+// one-launch layout and re-arms below, us per call, 7 / 8 ways, three boxes: M=4
+// 4.10-4.37 / 4.22-4.31 (7 kept), M=5 4.49-4.63 / 4.31-4.48, M=6 4.68-4.74 / 4.60-4.69,
+// M=7 4.74-4.80 / 4.69-4.71, M=8 4.82-4.92 / 4.81-4.88, M=9 4.98-5.02 / 4.85-4.90.  The pair
+// of launches keeps 7 (M=9: 4.94-5.03 against 5.00-5.08 with 8).
+#ifndef ARNORM_STEP_SPLIT8_MIN_M
+#define ARNORM_STEP_SPLIT8_MIN_M 5
+#endif
+#ifndef ARNORM_STEP_SPLIT8_MAX_M
+#define ARNORM_STEP_SPLIT8_MAX_M 9
+#endif
 // arnorm_push_reduce_norm, one-launch form: fragments per producer thread per step.
 #ifndef ARNORM_STEP_PUSH_U
 #define ARNORM_STEP_PUSH_U 2
@@ -491,8 +503,11 @@ int push_reduce_norm_launch(const uint16_t *partials, const uint16_t *residual, 
   // grid): measured at TP=8 it is then faster than the pair (M=4: 4.8 against 5.3 us),
   // while with witness polling (larger M) the pair of launches is faster.  Rows split 7
   // ways beat 14 (M=4: 4.8 against 5.3 us) and one workgroup per row (6.5 us).
-  const int K = nbox != nullptr ? reduce_split(M, true) : 1;
+  int K = nbox != nullptr ? reduce_split(M, true) : 1;
   const bool one_launch = K > 1 && (uint64_t)tp * M * arn::kRowBytes <= ARNORM_POLL_ALL_MAX_BYTES;
+  if (one_launch && g_reduce_split.load(std::memory_order_relaxed) == 0 && M >= ARNORM_STEP_SPLIT8_MIN_M &&
+      M <= ARNORM_STEP_SPLIT8_MAX_M)
+    K = 8;
   if (!one_launch) {
     // the same call as two launches: every rank's push, then the consumer
     const int rc = arnorm_push(partials, mailbox, parities, tp, cap, parity, 0, tp, M, stream);
