@@ -117,9 +117,13 @@ std::atomic<int> g_poll_mode{0};   // Gather polls: 0 = automatic, 1 = re-read a
 // 6.34-6.36 / 6.74-6.81, M=64 7.82-8.35 / 7.03-7.07 / 7.32-7.45, M=96 11.20-11.22 /
 // 10.52-10.54 / 10.81-10.88, M=128 12.84-12.85 / 12.62-12.63 / 13.24-13.29, M=192 17.54-17.58
 // / 17.77-17.80, M=256 21.41-21.45 / 21.98-22.03 (14 ways was slower than 7 everywhere,
-// 8 slower than 7 and 4).
+// 8 slower than 7 and 4).  Measured again with the rows of a split on one XCD (4 / 7 ways):
+// M=32 5.57-5.60 / 5.41-5.42, M=33 5.61-5.67 / 5.58-5.62, M=34 5.64-5.72 / 5.89-5.93, M=36
+// 5.77-5.81 / 6.11-6.18, M=40 5.90-5.92 / 6.27-6.28, M=48 6.14-6.15 / 6.58-6.63: 7 ways
+// while an XCD's 32 CUs hold its rows' workgroups (4 rows of 7 each up to M=32), 4 from
+// M=34.
 #ifndef ARNORM_SPLIT7_MAX_M
-#define ARNORM_SPLIT7_MAX_M 40
+#define ARNORM_SPLIT7_MAX_M 33
 #endif
 #ifndef ARNORM_SPLIT4_MAX_M
 #define ARNORM_SPLIT4_MAX_M 160
