@@ -56,7 +56,7 @@ def _draw_twoshot(rng, n):
 
 
 def _draw_arnorm_wide(rng, n):
-    """Larger caps (up to 300 rows: the 4-way split up to M=160 and the whole-row grid that
+    """Larger caps (up to 300 rows: the 4-way split up to M=128 and the whole-row grid that
     loops over rows above 128), the splits of 4 and 8 ways, and the call with the library's
     own norm box (M <= 64)."""
     cases = []

@@ -121,12 +121,14 @@ std::atomic<int> g_poll_mode{0};   // Gather polls: 0 = automatic, 1 = re-read a
 // M=32 5.57-5.60 / 5.41-5.42, M=33 5.61-5.67 / 5.58-5.62, M=34 5.64-5.72 / 5.89-5.93, M=36
 // 5.77-5.81 / 6.11-6.18, M=40 5.90-5.92 / 6.27-6.28, M=48 6.14-6.15 / 6.58-6.63: 7 ways
 // while an XCD's 32 CUs hold its rows' workgroups (4 rows of 7 each up to M=32), 4 from
-// M=34.
+// M=34.  And 1 way / 4 ways: M=120 12.18-12.22 / 12.00-12.02, M=128 12.52-12.64 /
+// 12.40-12.49, M=130 12.74-12.79 / 13.48-13.50, M=136 13.04-13.09 / 13.93-13.96, M=160
+// 14.82-14.92 / 15.62-15.67, M=192 17.31-17.32 / 17.73-17.76: 4 ways up to M=128.
 #ifndef ARNORM_SPLIT7_MAX_M
 #define ARNORM_SPLIT7_MAX_M 33
 #endif
 #ifndef ARNORM_SPLIT4_MAX_M
-#define ARNORM_SPLIT4_MAX_M 160
+#define ARNORM_SPLIT4_MAX_M 128
 #endif
 // The one-launch call splits rows 8 ways from ARNORM_STEP_SPLIT8_MIN_M to
 // ARNORM_STEP_SPLIT8_MAX_M rows (when the split is automatic).  Measured at TP=8 with the
