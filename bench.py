@@ -645,7 +645,7 @@ def summarize_profiles(outdir):
                     "arnorm_push_reduce_norm launch each (the 8 ranks' pushes and the consumer, rows split "
                     "7 ways through the norm box), then 2000 calls as the pair arnorm_push of 8 slots + "
                     "arnorm_reduce_norm, then 2000 arnorm_push_reduce_norm calls at M=1 (one launch) and "
-                    "2000 at M=64 (the pair, rows split 4 ways)", "arnorm_tp8_m4_kernel_stats.md"),
+                    "2000 at M=64 (one launch, rows split 4 ways)", "arnorm_tp8_m4_kernel_stats.md"),
             ("roof", "ArNorm kernels at TP=8, M=4096, residual: one push of 8 slots + one consumer launch, "
                      "23 times, each launch after a 1 GiB read-only pass (torch's float32 sum) that evicts the "
                      "last-level cache", "arnorm_tp8_m4096_kernel_stats.md"),

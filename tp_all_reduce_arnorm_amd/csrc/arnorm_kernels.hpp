@@ -76,6 +76,7 @@ struct ReduceArgs {
   int poll_all;             // later poll passes re-read every slot (small grids) instead of a witness
   float eps;
   uint64_t spin_limit;
+  uint32_t poll_delay;      // s_sleep(1) steps (64 cycles each) before the first poll pass
 };
 
 constexpr int kNormBoxRowWords = 256;  // a row's inbox block: [K readers][K writers], K <= 14
@@ -139,6 +140,10 @@ __device__ __forceinline__ void reduce_row(const ReduceArgs &a, const uint32_t r
     const bool own = FUSED && s == a.rank;
     slot[s] = make_rsrc(a.box + s * a.slot_stride + row_off, own ? 0u : (uint32_t)kRowBytes);
   }
+
+  // In a launch that also holds the producers, wait about as long as their stores take
+  // before the first poll pass: re-reading lines while they are written slows the stores.
+  for (uint32_t i = 0; i < a.poll_delay; ++i) __builtin_amdgcn_s_sleep(1);
 
   // issue every load: gamma (L2-resident), residual, own partial, the TP slots
   u32x4 g[NF], res[NF], mine[NF], raw[TP][NF];

@@ -187,6 +187,32 @@ std::atomic<int> g_poll_mode{0};   // Gather polls: 0 = automatic, 1 = re-read a
 #ifndef ARNORM_POLL_ALL_MAX_BYTES
 #define ARNORM_POLL_ALL_MAX_BYTES (1u << 20)
 #endif
+// arnorm_push_reduce_norm runs as one launch (with a norm box) up to ARNORM_STEP_MAX_M rows
+// whose TP slots total at most ARNORM_STEP_MAX_BYTES, else as the pair.  Its consumers wait
+// ARNORM_STEP_POLL_DELAY s_sleep steps of 64 cycles (ARNORM_STEP_POLL_DELAY_SPLIT4 for rows
+// split 4 ways) before their first poll pass, about as long as the producers' stores take
+// to land: polling the lines while they are written slowed the stores.  Measured at TP=8,
+// us per call, medians of 2 (delay 0 / 16 / 24 / 32 / 48 steps): M=1 3.81 / 3.96-3.98 /
+// 3.69 / 3.89 / 4.32, M=4 4.22-4.25 / 3.98-4.05 / 4.12 / 4.32-4.33 / 4.75-4.76, M=8
+// 4.86-4.90 / 4.51-4.54 / 4.17-4.18 / 4.39-4.40 / 4.81, M=16 5.44 / 4.73 / 4.30 / 4.51 /
+// 4.94-4.95, M=32 6.80-6.81 / 5.18 / 4.56 / 4.77 / 5.20; split 4 ways M=34 6.26-6.27 / - /
+// 5.28-5.30 / 4.79-4.80 / 5.22, M=40 6.56 / - / 5.56 / 4.95 / 5.36-5.37, M=64 7.85-7.88 / - /
+// 6.84-6.86 / 6.61-6.62 / 6.31-6.38; the pair at M=32 5.38, M=40 5.90, M=64 6.75-6.79.
+// On a second box, delay 0 / 24 / 32: TP=8 M=4 4.10-4.11 / 3.96 / 4.16, M=40 6.54 / 5.52-5.53
+// / 4.96-4.97, M=64 7.83-7.85 / 6.83-6.85 / 6.66-6.67; TP=4 M=16 4.60-4.67 / 3.76-3.85 /
+// 3.97-4.06; TP=2 M=4 3.78-3.83 / 3.53 / 3.74.
+#ifndef ARNORM_STEP_MAX_BYTES
+#define ARNORM_STEP_MAX_BYTES (7u << 20)
+#endif
+#ifndef ARNORM_STEP_MAX_M
+#define ARNORM_STEP_MAX_M 64
+#endif
+#ifndef ARNORM_STEP_POLL_DELAY
+#define ARNORM_STEP_POLL_DELAY 24
+#endif
+#ifndef ARNORM_STEP_POLL_DELAY_SPLIT4
+#define ARNORM_STEP_POLL_DELAY_SPLIT4 32
+#endif
 // gather_push_poll runs as one launch when the gathered rows total at most this many
 // bytes, its pollers re-reading every pending fragment per pass, else as the pair
 // gather_push + gather_poll.  Measured on MI355X at TP=8 (HIP-graph replay, µs per call,
@@ -480,6 +506,7 @@ int reduce_norm_launch(const uint16_t *partial, const uint16_t *residual, const 
   a.slot_stride = (size_t)cap * arn::kRowBytes;
   a.rows = (uint32_t)M;
   a.rank = partial ? rank : -1;
+  a.poll_delay = 0;
   a.eps = eps;
   a.spin_limit = g_spin_limit.load(std::memory_order_relaxed);
   a.poll_all = (uint64_t)tp * M * arn::kRowBytes <= ARNORM_POLL_ALL_MAX_BYTES;
@@ -505,12 +532,12 @@ int reduce_norm_launch(const uint16_t *partial, const uint16_t *residual, const 
 int push_reduce_norm_launch(const uint16_t *partials, const uint16_t *residual, const uint16_t *gamma,
                             uint16_t *out, uint16_t *residual_out, int32_t *mailbox, uint32_t *nbox, int parities,
                             int tp, int cap, int parity, int M, float eps, hipStream_t stream) {
-  // One launch only where its consumer may re-read every slot on each poll pass (a small
-  // grid): measured at TP=8 it is then faster than the pair (M=4: 4.8 against 5.3 us),
-  // while with witness polling (larger M) the pair of launches is faster.  Rows split 7
-  // ways beat 14 (M=4: 4.8 against 5.3 us) and one workgroup per row (6.5 us).
+  // One launch where its consumers, re-reading every slot on each poll pass after the
+  // delay below, beat the pair (see ARNORM_STEP_MAX_BYTES).  Rows split 7 ways beat 14 (M=4:
+  // 4.8 against 5.3 us) and one workgroup per row (6.5 us).
   int K = nbox != nullptr ? reduce_split(M, true) : 1;
-  const bool one_launch = K > 1 && (uint64_t)tp * M * arn::kRowBytes <= ARNORM_POLL_ALL_MAX_BYTES;
+  const bool one_launch =
+      K > 1 && M <= ARNORM_STEP_MAX_M && (uint64_t)tp * M * arn::kRowBytes <= ARNORM_STEP_MAX_BYTES;
   if (one_launch && g_reduce_split.load(std::memory_order_relaxed) == 0 && M >= ARNORM_STEP_SPLIT8_MIN_M &&
       M <= ARNORM_STEP_SPLIT8_MAX_M)
     K = 8;
@@ -535,7 +562,8 @@ int push_reduce_norm_launch(const uint16_t *partials, const uint16_t *residual, 
   a.r.rank = -1;
   a.r.eps = eps;
   a.r.spin_limit = g_spin_limit.load(std::memory_order_relaxed);
-  a.r.poll_all = (uint64_t)tp * M * arn::kRowBytes <= ARNORM_POLL_ALL_MAX_BYTES;
+  a.r.poll_all = 1;
+  a.r.poll_delay = K == 4 ? ARNORM_STEP_POLL_DELAY_SPLIT4 : ARNORM_STEP_POLL_DELAY;
   a.partials = reinterpret_cast<const u32x4 *>(partials);
   a.frags = (uint32_t)M * arn::kRowFrags;
   const bool few = M <= ARNORM_XCD_ROWS_MAX_M;
