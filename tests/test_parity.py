@@ -257,12 +257,14 @@ def test_drafter_gather_shapes(lib, name, m, tp):
 
 
 @pytest.mark.parametrize("name,m", [("gather_tp8_m32", 32), ("gather_tp8_m32", 16), ("gather_tp8_m32", 1),
-                                    ("gather_tp8_m32", 54), ("gather_tp8_m32", 55), ("ctx", 64), ("logits", 4),
+                                    ("gather_tp8_m32", 54), ("gather_tp8_m32", 64), ("ctx", 64), ("logits", 4),
+                                    ("logits", 25), ("logits", 26),
                                     ("logits", 2), ("logits", 1)])
 def test_gather_push_poll_one_call(lib, name, m):
-    """gather_push_poll (one launch for calls within 1.5 MiB, else the pair; S=896 at M=54 is
-    the last row count within it, M=55 the first above) against the oracle's push of every
-    rank followed by its poll: copy, then no-copy followed by a copying poll."""
+    """gather_push_poll (one launch for calls within 8 MiB, else the pair; the logits rows,
+    S=10240, fit 25 rows in it, not 26; its poll delay steps up above 2 and 4 MiB) against
+    the oracle's push of every rank followed by its poll: copy, then no-copy followed by a
+    copying poll."""
     import dataclasses
 
     import torch

@@ -191,14 +191,14 @@ def test_one_call_workloads(lib, name, calls):
 
 
 @pytest.mark.parametrize("tp,m", [(2, 13), (3, 13), (4, 13), (5, 13), (6, 9), (7, 9), (8, 9), (8, 13), (8, 1),
-                                  (8, 6), (8, 7), (8, 8), (8, 36), (8, 37)])
+                                  (8, 6), (8, 7), (8, 8), (8, 73), (8, 74)])
 def test_one_call_torture(lib, tp, m):
     """Torture rows through the one call, one launch where the TP slots of rows < M fit
-    4 MiB (at TP=8 M=36 is the last row count within it, M=37 the first above), with the
+    8 MiB (at TP=8 M=73 is the last row count within it, M=74 the first above), with the
     other parity published and left untouched.  The one launch pads its producer groups to
-    multiples of 8 workgroups from 24 per slot: TP=2..5 at M=13 and TP=8 at M=7, 8, 13 and
-    36 take the padded layout, TP=8 at M=6 the largest unpadded one, and M=9 (32 per slot)
-    needs no padding."""
+    multiples of 8 workgroups from 24 per slot: TP=2..5 at M=13 and TP=8 at M=7, 8 and 13
+    take the padded layout, TP=8 at M=6 the largest unpadded one, and M=9 and 73 (32 and 256
+    per slot) need no padding."""
     say(f"[twoshot] one call torture tp={tp} m={m}")
     rng = np.random.default_rng(400 + 16 * tp + m)
     cap = max(17, m)

@@ -132,8 +132,8 @@ gather_poll_kernel(uint8_t *__restrict__ box, u32x4 *__restrict__ out, uint64_t 
 //
 // The producers work by block of the gathered range, as the pollers do: producer b writes
 // the range's fragments b*256 .. b*256+255, each from the rank and row it belongs to, and
-// with the automatic poll layout (one fragment per thread; at most 384 blocks here, so a
-// poller each) poller b polls exactly those.  `producers` is
+// with the automatic poll layout (one fragment per thread while the range has at most 1024
+// blocks, so a poller each) poller b polls exactly those.  `producers` is
 // the block count rounded up to a multiple of 8 (the padding ids end at once), so that
 // producer b and poller b, whose ids then agree mod 8, sit on one XCD (workgroup ids go to
 // the eight XCDs in turn).  Measured at TP=8, µs per call, a producer per (rank, row) / per
@@ -151,12 +151,13 @@ struct GatherStepArgs {
   int copy;
   uint64_t spin_limit;
   int poll_all;
+  uint32_t poll_delay;  // s_sleep(1) steps (64 cycles each) before a poller's first pass
 };
 
 template <int TP, int U, int POL_PUSH, int POL_LD, int POL_ST, int POL_CP>
 __global__ void __launch_bounds__(256) gather_push_poll_kernel(GatherStepArgs a) {
   const uint32_t row_frags = TP * a.frags;
-  const uint32_t n = a.M * row_frags;  // the gathered range: the host keeps it within 1.5 MiB
+  const uint32_t n = a.M * row_frags;  // the gathered range: the host keeps it within 8 MiB
   if (blockIdx.x < a.producers) {
     const uint32_t i = blockIdx.x * 256u + threadIdx.x;
     if (i >= n) return;
@@ -166,6 +167,9 @@ __global__ void __launch_bounds__(256) gather_push_poll_kernel(GatherStepArgs a)
     buf_store<POL_PUSH>(clean4(nt_load(a.shard + ((size_t)s * a.M + m) * a.frags + j)), r, i * 16u);
     return;
   }
+  // wait about as long as the producers' stores take: polling lines while they are written
+  // slows the stores
+  for (uint32_t i = 0; i < a.poll_delay; ++i) __builtin_amdgcn_s_sleep(1);
   poll_range<POL_LD, POL_ST, POL_CP, U>(a.box, a.out, n, blockIdx.x - a.producers, a.pollers, a.copy, a.spin_limit,
                                 a.poll_all);
 }

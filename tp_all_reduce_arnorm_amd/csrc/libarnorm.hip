@@ -214,26 +214,42 @@ std::atomic<int> g_poll_mode{0};   // Gather polls: 0 = automatic, 1 = re-read a
 #define ARNORM_STEP_POLL_DELAY_SPLIT4 32
 #endif
 // gather_push_poll runs as one launch when the gathered rows total at most this many
-// bytes, its pollers re-reading every pending fragment per pass, else as the pair
-// gather_push + gather_poll.  Measured on MI355X at TP=8 (HIP-graph replay, µs per call,
-// the pair / one launch, the one launch re-arming with ARNORM_POL_REARM_STEP): S=896 M=32
-// (0.92 MB) 3.66-3.72 / 2.99, M=40 (1.15 MB) 3.90 / 3.24, M=48 (1.38 MB) 3.98 / 3.51, M=52
-// (1.49 MB) 4.01 / 3.67, M=56 (1.61 MB) 4.04 / 3.91, M=60 (1.72 MB) 4.06 / 4.42, M=64 4.13 /
-// 4.90; S=10240 M=4 (1.31 MB) 3.96-3.97 / 3.47-3.48, M=5 (1.64 MB) 4.09 / 4.28, M=6 4.18 /
-// 5.74.  Above about 1.6 MB the pollers' re-reads cost more than the launch they save.
+// bytes, its pollers waiting ARNORM_GATHER_STEP_POLL_DELAY s_sleep steps (24 above 2 MiB,
+// 32 above 4 MiB) and then re-reading every pending fragment per pass, else as the pair
+// gather_push + gather_poll.  Measured on MI355X at TP=8 (HIP-graph replay, us per call,
+// medians of 2, the pair / one launch with delay 0 / 16 / 24 / 32): S=896 M=4 3.50 / 2.33-2.36
+// / 2.27-2.28 / 2.49 / 2.70, M=32 3.66-3.72 / 2.70-2.71 / 2.43 / 2.64-2.65 / 2.86, M=64 (1.84
+// MB) 4.16 / 5.47-5.56 / 2.66-2.68 / 2.87-2.89 / 3.08-3.10; S=10240 M=1 3.53 / 2.39-2.40 /
+// 2.32 / 2.53 / 2.74, M=4 3.97 / 3.69-3.76 / 2.57 / 2.77-2.78 / 2.99, M=8 (2.6 MB) 4.48 /
+// 5.68-5.73 / 3.45-3.47 / 3.13-3.14 / 3.35-3.37, M=16 (5.2 MB) 5.81 / - / 5.35 / 4.66 / 4.62,
+// M=32 (10.5 MB) 8.50 / - / 8.32 / 8.49 / 8.60.
 #ifndef ARNORM_GATHER_STEP_MAX_BYTES
-#define ARNORM_GATHER_STEP_MAX_BYTES (3u << 19)
+#define ARNORM_GATHER_STEP_MAX_BYTES (8u << 20)
+#endif
+#ifndef ARNORM_GATHER_STEP_POLL_DELAY
+#define ARNORM_GATHER_STEP_POLL_DELAY 16
 #endif
 static_assert(ARNORM_GATHER_STEP_MAX_BYTES <= (1u << 30), "the one-launch Gather range is one buffer resource");
+// Steps of the one-launch Gather's poll delay for a gathered range of `bytes`.
+uint32_t gather_step_delay(uint64_t bytes) {
+  return bytes <= (2u << 20) ? ARNORM_GATHER_STEP_POLL_DELAY
+                             : bytes <= (4u << 20) ? ARNORM_GATHER_STEP_POLL_DELAY + 8 : ARNORM_GATHER_STEP_POLL_DELAY + 16;
+}
 // twoshot_push_reduce_read runs as one launch when the TP slots of rows < M total at
-// most this many bytes, its owners and readers re-reading every pending fragment on each
-// poll pass, else as its three launches.  Measured at TP=8, width 7168, with the re-arms of
-// ARNORM_POL_REARM_STEP (us per call, medians of 3 on one box, three launches / one):
-// M=10 6.34 / 4.88-4.90, M=12 6.37 / 4.85-4.86, M=16 6.43-6.44 / 4.82-4.83, M=24 6.58-6.66 /
-// 5.66-5.71, M=32 6.84-6.87 / 6.50-6.59, M=40 7.16-7.18 / 7.16-7.19, M=48 7.48-7.54 /
-// 7.77-7.84, M=96 11.38-11.45 / 11.63-11.81, M=128 13.11-13.12 / 13.69-13.75.
+// most this many bytes, its owners and readers waiting ARNORM_TWOSHOT_STEP_POLL_DELAY
+// s_sleep steps and then re-reading every pending fragment on each poll pass, else as its
+// three launches.  Measured at TP=8, width 7168, with the re-arms of ARNORM_POL_REARM_STEP
+// (us per call, medians of 2, three launches / one launch with delay 0 / 16 / 24 / 32):
+// M=1 - / 4.04-4.06 / 3.86-3.87 / 4.07 / 4.27-4.29, M=4 6.22-6.29 / 4.44-4.45 / 4.05-4.06 /
+// 4.26-4.27 / 4.47-4.48, M=16 6.43-6.44 / 4.75 / 4.29-4.30 / 4.50-4.51 / 4.71-4.72, M=32
+// 6.84-6.87 / 6.65 / 4.82-4.83 / 4.99-5.00 / 5.20-5.22, M=48 7.48-7.54 / 7.94-7.95 / 5.59-5.63
+// / 5.72-5.77 / 5.93-5.98, M=64 8.17-8.23 / 7.51 / 6.47-6.68 / 6.69-6.74 / 6.91-6.97, M=96
+// 11.45 / - / 11.53 / 11.19 / 11.09, M=128 13.19 / - / 13.43 / 13.27 / 13.23.
 #ifndef ARNORM_TWOSHOT_STEP_MAX_BYTES
-#define ARNORM_TWOSHOT_STEP_MAX_BYTES (4u << 20)
+#define ARNORM_TWOSHOT_STEP_MAX_BYTES (8u << 20)
+#endif
+#ifndef ARNORM_TWOSHOT_STEP_POLL_DELAY
+#define ARNORM_TWOSHOT_STEP_POLL_DELAY 16
 #endif
 // The one-launch two-shot call places an owner workgroup and the reader of the same
 // fragments on one XCD always, and their producers too from this many blocks of 256
@@ -755,6 +771,7 @@ int gather_push_poll(const int32_t *shard, int32_t *mailbox, int32_t *out, int t
   a.copy = copy ? 1 : 0;
   a.spin_limit = g_spin_limit.load(std::memory_order_relaxed);
   a.poll_all = poll_mode(1);
+  a.poll_delay = gather_step_delay((uint64_t)n * 16u);
   const dim3 grid(a.producers + a.pollers);
 #define ARNORM_GATHER_STEP(T)                                                                                      \
   case T:                                                                                                          \
@@ -861,6 +878,7 @@ int twoshot_push_reduce_read(const uint16_t *partial, int32_t *recv, int32_t *ga
   a.per_slot = a.red_ctas = a.read_ctas = (frags + 255) / 256;
   a.red_span = (a.red_ctas + 7) / 8 * 8;
   a.prod_span = a.per_slot >= ARNORM_TWOSHOT_ALIGN_PRODUCERS_MIN ? (a.per_slot + 7) / 8 * 8 : a.per_slot;
+  a.poll_delay = ARNORM_TWOSHOT_STEP_POLL_DELAY;
   const dim3 grid(tp * a.prod_span + a.red_span + a.read_ctas);
   switch (tp) {
 #define ARNORM_TWOSHOT_STEP(T)                                                                                      \
