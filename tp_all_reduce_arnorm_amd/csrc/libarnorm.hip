@@ -200,7 +200,11 @@ std::atomic<int> g_poll_mode{0};   // Gather polls: 0 = automatic, 1 = re-read a
 // 6.84-6.86 / 6.61-6.62 / 6.31-6.38; the pair at M=32 5.38, M=40 5.90, M=64 6.75-6.79.
 // On a second box, delay 0 / 24 / 32: TP=8 M=4 4.10-4.11 / 3.96 / 4.16, M=40 6.54 / 5.52-5.53
 // / 4.96-4.97, M=64 7.83-7.85 / 6.83-6.85 / 6.66-6.67; TP=4 M=16 4.60-4.67 / 3.76-3.85 /
-// 3.97-4.06; TP=2 M=4 3.78-3.83 / 3.53 / 3.74.
+// 3.97-4.06; TP=2 M=4 3.78-3.83 / 3.53 / 3.74.  Finer, on two more boxes (delay 16 / 18 / 20 /
+// 22 / 24): M=1 4.06-4.11 / 3.82-3.98 / 3.70-3.74 / 3.75-3.76 / 3.78-3.83, M=4 4.07-4.16 /
+// 3.87-3.90 / 3.84-3.89 / 3.92-3.94 / 3.96-3.99, M=8 4.47-4.55 / 4.44 / 4.08-4.16 / 4.08 /
+// 4.12-4.14, M=16 4.58-4.64 / 4.48-4.54 / 4.08-4.13 / 4.11-4.16 / 4.15-4.22.  Too short a
+// delay falls off a cliff (16 to 18 here); 22 keeps a margin above it.
 #ifndef ARNORM_STEP_MAX_BYTES
 #define ARNORM_STEP_MAX_BYTES (7u << 20)
 #endif
@@ -208,26 +212,29 @@ std::atomic<int> g_poll_mode{0};   // Gather polls: 0 = automatic, 1 = re-read a
 #define ARNORM_STEP_MAX_M 64
 #endif
 #ifndef ARNORM_STEP_POLL_DELAY
-#define ARNORM_STEP_POLL_DELAY 24
+#define ARNORM_STEP_POLL_DELAY 22
 #endif
 #ifndef ARNORM_STEP_POLL_DELAY_SPLIT4
 #define ARNORM_STEP_POLL_DELAY_SPLIT4 32
 #endif
 // gather_push_poll runs as one launch when the gathered rows total at most this many
-// bytes, its pollers waiting ARNORM_GATHER_STEP_POLL_DELAY s_sleep steps (24 above 2 MiB,
-// 32 above 4 MiB) and then re-reading every pending fragment per pass, else as the pair
+// bytes, its pollers waiting ARNORM_GATHER_STEP_POLL_DELAY s_sleep steps (8 more above 2
+// MiB, 16 more above 4 MiB) and then re-reading every pending fragment per pass, else as the pair
 // gather_push + gather_poll.  Measured on MI355X at TP=8 (HIP-graph replay, us per call,
 // medians of 2, the pair / one launch with delay 0 / 16 / 24 / 32): S=896 M=4 3.50 / 2.33-2.36
 // / 2.27-2.28 / 2.49 / 2.70, M=32 3.66-3.72 / 2.70-2.71 / 2.43 / 2.64-2.65 / 2.86, M=64 (1.84
 // MB) 4.16 / 5.47-5.56 / 2.66-2.68 / 2.87-2.89 / 3.08-3.10; S=10240 M=1 3.53 / 2.39-2.40 /
 // 2.32 / 2.53 / 2.74, M=4 3.97 / 3.69-3.76 / 2.57 / 2.77-2.78 / 2.99, M=8 (2.6 MB) 4.48 /
 // 5.68-5.73 / 3.45-3.47 / 3.13-3.14 / 3.35-3.37, M=16 (5.2 MB) 5.81 / - / 5.35 / 4.66 / 4.62,
-// M=32 (10.5 MB) 8.50 / - / 8.32 / 8.49 / 8.60.
+// M=32 (10.5 MB) 8.50 / - / 8.32 / 8.49 / 8.60.  Finer, on two boxes (delay 10 / 12 / 14 /
+// 16): S=896 M=4 2.20 / 2.17-2.19 / 2.23 / 2.25-2.29, M=32 2.73 / 2.35-2.39 / 2.38-2.39 /
+// 2.43-2.44; logits M=4 2.74-2.75 / 2.43-2.48 / 2.51-2.52 / 2.55-2.57: 14 keeps a margin above
+// the cliff at 10.
 #ifndef ARNORM_GATHER_STEP_MAX_BYTES
 #define ARNORM_GATHER_STEP_MAX_BYTES (8u << 20)
 #endif
 #ifndef ARNORM_GATHER_STEP_POLL_DELAY
-#define ARNORM_GATHER_STEP_POLL_DELAY 16
+#define ARNORM_GATHER_STEP_POLL_DELAY 14
 #endif
 static_assert(ARNORM_GATHER_STEP_MAX_BYTES <= (1u << 30), "the one-launch Gather range is one buffer resource");
 // Steps of the one-launch Gather's poll delay for a gathered range of `bytes`.
@@ -244,12 +251,15 @@ uint32_t gather_step_delay(uint64_t bytes) {
 // 4.26-4.27 / 4.47-4.48, M=16 6.43-6.44 / 4.75 / 4.29-4.30 / 4.50-4.51 / 4.71-4.72, M=32
 // 6.84-6.87 / 6.65 / 4.82-4.83 / 4.99-5.00 / 5.20-5.22, M=48 7.48-7.54 / 7.94-7.95 / 5.59-5.63
 // / 5.72-5.77 / 5.93-5.98, M=64 8.17-8.23 / 7.51 / 6.47-6.68 / 6.69-6.74 / 6.91-6.97, M=96
-// 11.45 / - / 11.53 / 11.19 / 11.09, M=128 13.19 / - / 13.43 / 13.27 / 13.23.
+// 11.45 / - / 11.53 / 11.19 / 11.09, M=128 13.19 / - / 13.43 / 13.27 / 13.23.  Finer, on two
+// boxes (delay 4 / 6 / 8 / 10 / 12): M=1 3.91 / 3.77-3.81 / 3.68-3.70 / 3.69-3.70 / 3.74-3.75,
+// M=4 4.03-4.06 / 3.92-3.95 / 3.86-3.89 / 3.87-3.89 / 3.91-3.95, M=16 4.26-4.28 / 4.20 /
+// 4.12-4.14 / 4.13-4.14 / 4.16-4.17.
 #ifndef ARNORM_TWOSHOT_STEP_MAX_BYTES
 #define ARNORM_TWOSHOT_STEP_MAX_BYTES (8u << 20)
 #endif
 #ifndef ARNORM_TWOSHOT_STEP_POLL_DELAY
-#define ARNORM_TWOSHOT_STEP_POLL_DELAY 16
+#define ARNORM_TWOSHOT_STEP_POLL_DELAY 10
 #endif
 // The one-launch two-shot call places an owner workgroup and the reader of the same
 // fragments on one XCD always, and their producers too from this many blocks of 256
