@@ -361,21 +361,19 @@ __global__ void __launch_bounds__(NT, reduce_occupancy(NT)) reduce_norm_kernel(R
 // consumers, split K ways (896/K threads each), which poll until the producers' stores
 // land, re-arm and reduce.
 //
-// Consumer layout.  By default consumer c serves row c / K, part c % K.  With xcd_rows
-// the consumers come in blocks of 8 * K: consumer c = 8 * K * b + 8 * k + j serves row
-// 8 * b + j, part k (ids past the last row end at once).  The dispatcher hands workgroup
-// ids to the eight XCDs in turn, so a row's K workgroups, whose ids then agree mod 8,
-// share one XCD and its L2 for the norm-box exchange.  Placement only: the results do
-// not depend on it.  A block's rows then interleave in id order, so the argument that
-// the lowest unfinished row has all its workgroups dispatched needs the block (8 * K
-// workgroups of at most 128 threads) resident at once, which any GPU of this family
-// holds many times over.
+// Consumer layout: the consumers come in blocks of 8 * K.  Consumer c = 8 * K * b + 8 * k +
+// j serves row 8 * b + j, part k (ids past the last row end at once).  The dispatcher
+// hands workgroup ids to the eight XCDs in turn, so a row's K workgroups, whose ids then
+// agree mod 8, share one XCD and its L2 for the norm-box exchange.  Placement only: the
+// results do not depend on it.  A block's rows interleave in id order, so the argument
+// that the lowest unfinished row has all its workgroups dispatched needs the block (8 * K
+// workgroups of at most 256 threads) resident at once, which any GPU of this family holds
+// many times over.
 struct StepArgs {
   ReduceArgs r;
   const u32x4 *partials;  // [TP, M, 896]
   uint32_t frags;         // M * 896: one slot's fragments, one block in the mailbox
   uint32_t per_slot;      // producer workgroups per slot
-  int xcd_rows;           // the consumer layout above
 };
 
 template <int TP, bool RES, int K, int U, int POL_PUSH, int POL_LD, int POL_ST, int POL_IN, int POL_IO>
@@ -402,14 +400,10 @@ __global__ void __launch_bounds__(split_threads(K)) push_reduce_kernel(StepArgs 
     return;
   }
   const uint32_t c = blockIdx.x - producers;
-  if (a.xcd_rows) {
-    const uint32_t b = c / (8u * K), w = c - b * 8u * K;
-    const uint32_t row = 8u * b + (w & 7u);
-    if (row >= a.frags / kRowFrags) return;  // a padding id of the last block
-    reduce_row<TP, RES, false, NT, K, POL_LD, POL_ST, POL_IN, POL_IO>(a.r, row, w >> 3);
-    return;
-  }
-  reduce_row<TP, RES, false, NT, K, POL_LD, POL_ST, POL_IN, POL_IO>(a.r, c / K, c % K);
+  const uint32_t b = c / (8u * K), w = c - b * 8u * K;
+  const uint32_t row = 8u * b + (w & 7u);
+  if (row >= a.frags / kRowFrags) return;  // a padding id of the last block
+  reduce_row<TP, RES, false, NT, K, POL_LD, POL_ST, POL_IN, POL_IO>(a.r, row, w >> 3);
 }
 
 }  // namespace arn

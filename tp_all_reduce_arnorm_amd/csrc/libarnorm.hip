@@ -120,50 +120,36 @@ std::atomic<int> g_poll_mode{0};   // Gather polls: 0 = automatic, 1 = re-read a
 // 8 slower than 7 and 4).  Measured again with the rows of a split on one XCD (4 / 7 ways):
 // M=32 5.57-5.60 / 5.41-5.42, M=33 5.61-5.67 / 5.58-5.62, M=34 5.64-5.72 / 5.89-5.93, M=36
 // 5.77-5.81 / 6.11-6.18, M=40 5.90-5.92 / 6.27-6.28, M=48 6.14-6.15 / 6.58-6.63: 7 ways
-// while an XCD's 32 CUs hold its rows' workgroups (4 rows of 7 each up to M=32), 4 from
-// M=34.  And 1 way / 4 ways: M=120 12.18-12.22 / 12.00-12.02, M=128 12.52-12.64 /
+// while an XCD's 32 CUs hold its rows' workgroups (4 rows of 7 each up to M=32).  At M=33,
+// with the one launch's poll delay and a row on one XCD there too, 4 / 7 ways: one launch
+// 4.68-4.69 / 4.93-4.95, the pair 5.67-5.70 / 5.92-5.96; so 4 from M=33.  And 1 way / 4 ways: M=120 12.18-12.22 / 12.00-12.02, M=128 12.52-12.64 /
 // 12.40-12.49, M=130 12.74-12.79 / 13.48-13.50, M=136 13.04-13.09 / 13.93-13.96, M=160
 // 14.82-14.92 / 15.62-15.67, M=192 17.31-17.32 / 17.73-17.76: 4 ways up to M=128.
 #ifndef ARNORM_SPLIT7_MAX_M
-#define ARNORM_SPLIT7_MAX_M 33
+#define ARNORM_SPLIT7_MAX_M 32
 #endif
 #ifndef ARNORM_SPLIT4_MAX_M
 #define ARNORM_SPLIT4_MAX_M 128
-#endif
-// The one-launch call splits rows 8 ways from ARNORM_STEP_SPLIT8_MIN_M to
-// ARNORM_STEP_SPLIT8_MAX_M rows (when the split is automatic).  Measured at TP=8 with the
-// one-launch layout and re-arms below, us per call, 7 / 8 ways, three boxes: M=4
-// 4.10-4.37 / 4.22-4.31 (7 kept), M=5 4.49-4.63 / 4.31-4.48, M=6 4.68-4.74 / 4.60-4.69,
-// M=7 4.74-4.80 / 4.69-4.71, M=8 4.82-4.92 / 4.81-4.88, M=9 4.98-5.02 / 4.85-4.90.  The pair
-// of launches keeps 7 (M=9: 4.94-5.03 against 5.00-5.08 with 8).
-#ifndef ARNORM_STEP_SPLIT8_MIN_M
-#define ARNORM_STEP_SPLIT8_MIN_M 5
-#endif
-#ifndef ARNORM_STEP_SPLIT8_MAX_M
-#define ARNORM_STEP_SPLIT8_MAX_M 9
 #endif
 // arnorm_push_reduce_norm, one-launch form: fragments per producer thread per step.
 #ifndef ARNORM_STEP_PUSH_U
 #define ARNORM_STEP_PUSH_U 2
 #endif
-// arnorm_push_reduce_norm, one-launch form, few rows: up to this M a row's consumer
-// workgroups are placed on one XCD (push_reduce_kernel, xcd_rows), above it they are
-// spread over the XCDs.  Measured on MI355X at TP=8, us per call, HIP-graph replay,
-// medians of 4 alternations per box (fresh buffers each time), 2 fragments per producer
-// thread and device-scope re-arms (ARNORM_POL_REARM_STEP) in both, one XCD per row /
-// spread: M=1 3.73-3.88 / 4.12-4.14, M=2 3.96-4.00 / 4.13, M=3 3.99-4.02 / 4.11-4.19, M=4
-// 4.21-4.44 / 4.14-4.35.  Earlier layouts, on six boxes: one XCD per row up to M=4 with 4
-// fragments per producer thread and non-temporal re-arms took M=1 4.09-4.12, M=2
-// 4.25-4.31, M=3 4.31-4.34, M=4 4.34-4.43; one XCD per row with 4 per thread and
-// device-scope re-arms M=1 4.15, M=4 4.78-4.84; spread with non-temporal re-arms M=1
-// 4.35-4.36, M=4 4.51-4.52.  With few rows a row's norm-box exchange stays in one L2;
-// from M=4 the rows crowd their XCDs.
-#ifndef ARNORM_XCD_ROWS_MAX_M
-#define ARNORM_XCD_ROWS_MAX_M 3
-#endif
+// arnorm_push_reduce_norm, one-launch form: a row's consumer workgroups are placed on one
+// XCD (push_reduce_kernel), at every M, and rows split the automatic K ways (7, or 4 from
+// M=34).  Measured on MI355X at TP=8 with the poll delay below, us per call, HIP-graph
+// replay, medians of 3 alternations on one box (fresh buffers each time).  One XCD per row
+// against spread rows (workgroup c serving row c / K, part c % K): M=1 3.74 / 3.89, M=2
+// 3.82 / 3.94, M=4 3.83-3.84 / 3.91, M=5 3.83 / 3.98, M=6 3.88 / 3.99, M=8 3.89 / 4.00;
+// up to M=64 against one XCD per row only to M=8: M=12 4.07 / 4.11, M=16 4.11 / 4.16, M=24
+// 4.35 / 4.33, M=32 4.45 / 4.49, M=40 4.95 / 4.96, M=48 5.10 / 5.22, M=64 6.59 / 6.68.
+// Without the delay, spread rows had won from M=4 (4.14-4.35 against 4.21-4.44) and 8 ways
+// had beaten 7 at M=5..9; with it, 7 / 8 ways on spread rows, two runs: M=4 3.95-3.96 /
+// 4.06, M=5 4.00-4.02 / 4.07-4.09, M=6 4.03 / 4.10-4.11, M=7 4.03 / 4.09-4.12, M=8
+// 4.02-4.05 / 4.11-4.13, M=9 4.10 / 4.17-4.19.
 // The re-arm stores inside the one-launch calls (ArNorm, the Gather and the two-shot
 // call), whose pollers re-read lines while their producers write them: device scope
-// without the non-temporal bit.  ArNorm: see ARNORM_XCD_ROWS_MAX_M, and on six boxes, the
+// without the non-temporal bit.  ArNorm, before the poll delay, on six boxes: the
 // consumers spread with these re-arms against one XCD per row with non-temporal ones,
 // M=2 4.25-4.31 / 4.10-4.16, M=4 4.34-4.38 / 4.11-4.33 on five boxes (4.43 / 4.59 on the
 // sixth), M=8 4.90-5.06 / 4.74-4.97, M=9 5.00-5.10 / 4.86-5.03, M=5..7 mixed, -0.25..+0.12.
@@ -204,7 +190,11 @@ std::atomic<int> g_poll_mode{0};   // Gather polls: 0 = automatic, 1 = re-read a
 // 22 / 24): M=1 4.06-4.11 / 3.82-3.98 / 3.70-3.74 / 3.75-3.76 / 3.78-3.83, M=4 4.07-4.16 /
 // 3.87-3.90 / 3.84-3.89 / 3.92-3.94 / 3.96-3.99, M=8 4.47-4.55 / 4.44 / 4.08-4.16 / 4.08 /
 // 4.12-4.14, M=16 4.58-4.64 / 4.48-4.54 / 4.08-4.13 / 4.11-4.16 / 4.15-4.22.  Too short a
-// delay falls off a cliff (16 to 18 here); 22 keeps a margin above it.
+// delay falls off a cliff (16 to 18 here); 22 keeps a margin above it.  Rows split 4 ways
+// wait one step more per row above ARNORM_STEP_POLL_DELAY_RAMP_M: with a row on one XCD,
+// medians of 3 alternations (delay 32 / 40 / 48 / 56): M=33 4.69 / 4.90 / 5.12 / 5.32, M=40
+// 4.86 / 5.06 / 5.28 / 5.48, M=48 5.13 / 5.22 / 5.44 / 5.64, M=56 5.68 / 5.40 / 5.61 / 5.82,
+// M=64 6.50 / 6.37 / 6.11 / 6.13.
 #ifndef ARNORM_STEP_MAX_BYTES
 #define ARNORM_STEP_MAX_BYTES (7u << 20)
 #endif
@@ -216,6 +206,9 @@ std::atomic<int> g_poll_mode{0};   // Gather polls: 0 = automatic, 1 = re-read a
 #endif
 #ifndef ARNORM_STEP_POLL_DELAY_SPLIT4
 #define ARNORM_STEP_POLL_DELAY_SPLIT4 32
+#endif
+#ifndef ARNORM_STEP_POLL_DELAY_RAMP_M
+#define ARNORM_STEP_POLL_DELAY_RAMP_M 48
 #endif
 // gather_push_poll runs as one launch when the gathered rows total at most this many
 // bytes, its pollers waiting ARNORM_GATHER_STEP_POLL_DELAY s_sleep steps (8 more above 2
@@ -561,12 +554,9 @@ int push_reduce_norm_launch(const uint16_t *partials, const uint16_t *residual, 
   // One launch where its consumers, re-reading every slot on each poll pass after the
   // delay below, beat the pair (see ARNORM_STEP_MAX_BYTES).  Rows split 7 ways beat 14 (M=4:
   // 4.8 against 5.3 us) and one workgroup per row (6.5 us).
-  int K = nbox != nullptr ? reduce_split(M, true) : 1;
+  const int K = nbox != nullptr ? reduce_split(M, true) : 1;
   const bool one_launch =
       K > 1 && M <= ARNORM_STEP_MAX_M && (uint64_t)tp * M * arn::kRowBytes <= ARNORM_STEP_MAX_BYTES;
-  if (one_launch && g_reduce_split.load(std::memory_order_relaxed) == 0 && M >= ARNORM_STEP_SPLIT8_MIN_M &&
-      M <= ARNORM_STEP_SPLIT8_MAX_M)
-    K = 8;
   if (!one_launch) {
     // the same call as two launches: every rank's push, then the consumer
     const int rc = arnorm_push(partials, mailbox, parities, tp, cap, parity, 0, tp, M, stream);
@@ -589,15 +579,24 @@ int push_reduce_norm_launch(const uint16_t *partials, const uint16_t *residual, 
   a.r.eps = eps;
   a.r.spin_limit = g_spin_limit.load(std::memory_order_relaxed);
   a.r.poll_all = 1;
-  a.r.poll_delay = K == 4 ? ARNORM_STEP_POLL_DELAY_SPLIT4 : ARNORM_STEP_POLL_DELAY;
+  a.r.poll_delay = K != 4 ? ARNORM_STEP_POLL_DELAY
+                          : ARNORM_STEP_POLL_DELAY_SPLIT4 +
+                                (M > ARNORM_STEP_POLL_DELAY_RAMP_M ? M - ARNORM_STEP_POLL_DELAY_RAMP_M : 0);
   a.partials = reinterpret_cast<const u32x4 *>(partials);
   a.frags = (uint32_t)M * arn::kRowFrags;
-  const bool few = M <= ARNORM_XCD_ROWS_MAX_M;
   const int U = ARNORM_STEP_PUSH_U;
   const uint32_t nt = arn::split_threads(K);
+  // Workgroups of at most 128 threads (rows split 7 ways) come in an even number of
+  // producers per slot (an extra one finds no fragments and ends).  With an odd count, from
+  // M=14 the call paid most of a poll round trip more: TP=8, medians of 3 alternations, odd
+  // / rounded up to even, M=14 4.12 / 3.99, M=15 4.16 / 3.98, M=18 4.32 / 4.07, M=22 4.66 /
+  // 4.17, M=23 4.71 / 4.15, M=26 4.75 / 4.24, M=27 4.77 / 4.23, M=30 5.02 / 4.40, M=31 5.17 /
+  // 4.48 (two more boxes: M=30 5.08, 4.81 / 4.39, 4.47), the other row counts within 0.02.
+  // Rows split 4 ways (256 threads) keep the count: there rounding moved the slow row counts
+  // about (M=39 4.87 / 5.41, M=47 5.09 / 5.74, M=61 6.31 / 6.07).
   a.per_slot = (a.frags + nt * U - 1) / (nt * U);
-  a.xcd_rows = few;
-  const dim3 grid(tp * a.per_slot + (few ? (M + 7) / 8 * 8 * K : M * K));
+  if (nt <= 128) a.per_slot += a.per_slot & 1u;
+  const dim3 grid(tp * a.per_slot + (M + 7) / 8 * 8 * K);
   const bool res = residual != nullptr;
 #define ARNORM_STEP_LAUNCH_K(TPV, KV)                                                                              \
   return res ? launch(arn::push_reduce_kernel<TPV, true, KV, ARNORM_STEP_PUSH_U, kPolPush, kPolPoll, kPolRearmStep,  \
