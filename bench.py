@@ -264,7 +264,7 @@ def gather_bytes(tp, m, s, copy=True):
 
 def time_gather(lib, torch, calls=2000, chunk=200, name="gather_tp8_m32", one_launch=True, m=None):
     """µs per Gather call, graph-replayed: gather_push_poll (every rank's push and the
-    copying poll, one launch for calls within 1 MiB), or with one_launch False the pair
+    copying poll, one launch for calls within 8 MiB of gathered rows), or with one_launch False the pair
     gather_push + gather_poll.  gather_tp8_m32 is TP=8, M=32, S=896; ctx and logits are the
     drafter's context-projection and lm_head shapes; m overrides the row count."""
     import dataclasses
