@@ -384,12 +384,18 @@ __global__ void __launch_bounds__(split_threads(K)) push_reduce_kernel(StepArgs 
     const uint32_t s = blockIdx.x / a.per_slot, p = blockIdx.x - s * a.per_slot;
     const u32x4 *src = a.partials + (size_t)s * a.frags;
     const __amdgpu_buffer_rsrc_t dst = make_rsrc(a.r.box + s * a.r.slot_stride, a.frags * 16u);
+    // The partial rows are read with the default cache policy: a caller's rows, just
+    // written by the step before, are usually still in the last-level cache.  Non-temporal
+    // loads fetched them from HBM, and from M=55 a few producers then ended late enough to
+    // cost 0.4-1.2 us per call (TP=8, medians of 3 alternations, non-temporal / default: M=55
+    // 5.78 / 5.37, M=59 6.66 / 5.64, M=62 6.98 / 5.80, M=63 6.76 / 5.83, M=64 6.28 / 5.88;
+    // M=1..56 within 0.02).
     for (uint32_t i0 = p * NT * U + threadIdx.x; i0 < a.frags; i0 += a.per_slot * NT * U) {
       u32x4 v[U];
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const uint32_t i = i0 + u * NT;
-        if (i < a.frags) v[u] = nt_load(src + i);
+        if (i < a.frags) v[u] = src[i];
       }
 #pragma unroll
       for (int u = 0; u < U; ++u) {

@@ -191,10 +191,11 @@ std::atomic<int> g_poll_mode{0};   // Gather polls: 0 = automatic, 1 = re-read a
 // 3.87-3.90 / 3.84-3.89 / 3.92-3.94 / 3.96-3.99, M=8 4.47-4.55 / 4.44 / 4.08-4.16 / 4.08 /
 // 4.12-4.14, M=16 4.58-4.64 / 4.48-4.54 / 4.08-4.13 / 4.11-4.16 / 4.15-4.22.  Too short a
 // delay falls off a cliff (16 to 18 here); 22 keeps a margin above it.  Rows split 4 ways
-// wait one step more per row above ARNORM_STEP_POLL_DELAY_RAMP_M: with a row on one XCD,
-// medians of 3 alternations (delay 32 / 40 / 48 / 56): M=33 4.69 / 4.90 / 5.12 / 5.32, M=40
-// 4.86 / 5.06 / 5.28 / 5.48, M=48 5.13 / 5.22 / 5.44 / 5.64, M=56 5.68 / 5.40 / 5.61 / 5.82,
-// M=64 6.50 / 6.37 / 6.11 / 6.13.
+// wait one step more per two rows above ARNORM_STEP_POLL_DELAY_RAMP_M (M=64: 40 steps).
+// With the producers' default-policy loads, medians of 3 alternations, constant delay 32 /
+// 36: M=40 4.90 / 4.99, M=48 5.15 / 5.14, M=56 5.66 / 5.34, M=64 6.36 / 5.85; the ramp of one
+// step per row (M=64: 48 steps) / this one, medians of 4: M=56 5.41 / 5.34, M=60 5.67 /
+// 5.59, M=64 5.88 / 5.67, M=33..51 within 0.03.
 #ifndef ARNORM_STEP_MAX_BYTES
 #define ARNORM_STEP_MAX_BYTES (7u << 20)
 #endif
@@ -581,7 +582,7 @@ int push_reduce_norm_launch(const uint16_t *partials, const uint16_t *residual, 
   a.r.poll_all = 1;
   a.r.poll_delay = K != 4 ? ARNORM_STEP_POLL_DELAY
                           : ARNORM_STEP_POLL_DELAY_SPLIT4 +
-                                (M > ARNORM_STEP_POLL_DELAY_RAMP_M ? M - ARNORM_STEP_POLL_DELAY_RAMP_M : 0);
+                                (M > ARNORM_STEP_POLL_DELAY_RAMP_M ? (M - ARNORM_STEP_POLL_DELAY_RAMP_M + 1) / 2 : 0);
   a.partials = reinterpret_cast<const u32x4 *>(partials);
   a.frags = (uint32_t)M * arn::kRowFrags;
   const int U = ARNORM_STEP_PUSH_U;
@@ -593,7 +594,8 @@ int push_reduce_norm_launch(const uint16_t *partials, const uint16_t *residual, 
   // 4.17, M=23 4.71 / 4.15, M=26 4.75 / 4.24, M=27 4.77 / 4.23, M=30 5.02 / 4.40, M=31 5.17 /
   // 4.48 (two more boxes: M=30 5.08, 4.81 / 4.39, 4.47), the other row counts within 0.02.
   // Rows split 4 ways (256 threads) keep the count: there rounding moved the slow row counts
-  // about (M=39 4.87 / 5.41, M=47 5.09 / 5.74, M=61 6.31 / 6.07).
+  // about (M=39 4.87 / 5.41, M=47 5.09 / 5.74, M=61 6.31 / 6.07, measured while the producers
+  // read their rows with non-temporal loads).
   a.per_slot = (a.frags + nt * U - 1) / (nt * U);
   if (nt <= 128) a.per_slot += a.per_slot & 1u;
   const dim3 grid(tp * a.per_slot + (M + 7) / 8 * 8 * K);
