@@ -238,8 +238,8 @@ uint32_t gather_step_delay(uint64_t bytes) {
 }
 // twoshot_push_reduce_read runs as one launch when the TP slots of rows < M total at
 // most this many bytes, its owners and readers waiting ARNORM_TWOSHOT_STEP_POLL_DELAY
-// s_sleep steps and then re-reading every pending fragment on each poll pass, else as its
-// three launches.  Measured at TP=8, width 7168, with the re-arms of ARNORM_POL_REARM_STEP
+// s_sleep steps (6 more above 2 MiB of slots) and then re-reading every pending fragment
+// on each poll pass, else as its three launches.  Measured at TP=8, width 7168, with the re-arms of ARNORM_POL_REARM_STEP
 // (us per call, medians of 2, three launches / one launch with delay 0 / 16 / 24 / 32):
 // M=1 - / 4.04-4.06 / 3.86-3.87 / 4.07 / 4.27-4.29, M=4 6.22-6.29 / 4.44-4.45 / 4.05-4.06 /
 // 4.26-4.27 / 4.47-4.48, M=16 6.43-6.44 / 4.75 / 4.29-4.30 / 4.50-4.51 / 4.71-4.72, M=32
@@ -248,13 +248,20 @@ uint32_t gather_step_delay(uint64_t bytes) {
 // 11.45 / - / 11.53 / 11.19 / 11.09, M=128 13.19 / - / 13.43 / 13.27 / 13.23.  Finer, on two
 // boxes (delay 4 / 6 / 8 / 10 / 12): M=1 3.91 / 3.77-3.81 / 3.68-3.70 / 3.69-3.70 / 3.74-3.75,
 // M=4 4.03-4.06 / 3.92-3.95 / 3.86-3.89 / 3.87-3.89 / 3.91-3.95, M=16 4.26-4.28 / 4.20 /
-// 4.12-4.14 / 4.13-4.14 / 4.16-4.17.
+// 4.12-4.14 / 4.13-4.14 / 4.16-4.17.  Above 2 MiB (M=18 at TP=8) 16 steps: medians of 3 on
+// one box, delay 10 / 16 / 24: M=16 4.13 / 4.25 / 4.47, M=20 4.43 / 4.37 / 4.58, M=24 4.93 /
+// 4.50 / 4.70, M=28 5.43 / 4.67 / 4.84, M=32 5.74 / 4.82 / 4.97, M=40 6.01 / 5.33 / 5.44, M=48
+// 6.07 / 5.67 / 5.73, M=56 6.14 / 6.20 / 6.41, M=64 6.82 / 6.53 / 6.71, M=73 7.38 / 7.19 / 7.34.
 #ifndef ARNORM_TWOSHOT_STEP_MAX_BYTES
 #define ARNORM_TWOSHOT_STEP_MAX_BYTES (8u << 20)
 #endif
 #ifndef ARNORM_TWOSHOT_STEP_POLL_DELAY
 #define ARNORM_TWOSHOT_STEP_POLL_DELAY 10
 #endif
+// Steps of the one-launch two-shot call's poll delay for TP slots of `bytes` (rows < M).
+uint32_t twoshot_step_delay(uint64_t bytes) {
+  return bytes <= (2u << 20) ? ARNORM_TWOSHOT_STEP_POLL_DELAY : ARNORM_TWOSHOT_STEP_POLL_DELAY + 6;
+}
 // The one-launch two-shot call places an owner workgroup and the reader of the same
 // fragments on one XCD always, and their producers too from this many blocks of 256
 // fragments per slot (below it, the producers of a few blocks would crowd a few XCDs while
@@ -889,7 +896,7 @@ int twoshot_push_reduce_read(const uint16_t *partial, int32_t *recv, int32_t *ga
   a.per_slot = a.red_ctas = a.read_ctas = (frags + 255) / 256;
   a.red_span = (a.red_ctas + 7) / 8 * 8;
   a.prod_span = a.per_slot >= ARNORM_TWOSHOT_ALIGN_PRODUCERS_MIN ? (a.per_slot + 7) / 8 * 8 : a.per_slot;
-  a.poll_delay = ARNORM_TWOSHOT_STEP_POLL_DELAY;
+  a.poll_delay = twoshot_step_delay((uint64_t)tp * frags * 16u);
   const dim3 grid(tp * a.prod_span + a.red_span + a.read_ctas);
   switch (tp) {
 #define ARNORM_TWOSHOT_STEP(T)                                                                                      \
