@@ -148,9 +148,9 @@ def test_push_reduce_norm_torture(lib, tp, split, m):
     one launch (a row's workgroups on one XCD, in blocks of 8 rows) takes 7 parts at M=3
     (one short block), 4, 5, 9 (a full block and one row), 13, 14 and 31 (an odd producer
     count per slot, rounded up to even: the extra producer has no fragments) and 32, and 4
-    parts at M=33, 34 and 64 (the last row count in one launch); forced splits of 4, 8 and
-    14 ways run at M=13; from M=65 the pair of launches runs, rows split 4 ways up to
-    M=128 and one workgroup per row at M=129."""
+    parts at M=33, 34, 64, 65 and 128 (the last row count in one launch; from about M=100
+    the grid is larger than what the GPU holds at once); forced splits of 4, 8 and 14 ways
+    run at M=13; at M=129 the pair of launches runs, one workgroup per row."""
     say(f"[parity] push_reduce_norm torture tp={tp} split={split} m={m}")
     lib.set_reduce_split(split)
     rng = np.random.default_rng(170 + tp + 32 * m)

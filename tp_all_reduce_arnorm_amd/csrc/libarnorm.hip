@@ -195,12 +195,19 @@ std::atomic<int> g_poll_mode{0};   // Gather polls: 0 = automatic, 1 = re-read a
 // With the producers' default-policy loads, medians of 3 alternations, constant delay 32 /
 // 36: M=40 4.90 / 4.99, M=48 5.15 / 5.14, M=56 5.66 / 5.34, M=64 6.36 / 5.85; the ramp of one
 // step per row (M=64: 48 steps) / this one, medians of 4: M=56 5.41 / 5.34, M=60 5.67 /
-// 5.59, M=64 5.88 / 5.67, M=33..51 within 0.03.
+// 5.59, M=64 5.88 / 5.67, M=33..51 within 0.03.  The ramp ends at ARNORM_STEP_POLL_DELAY_RAMP_END
+// rows: above it a constant 40 steps measured best or within 0.15 us (one launch, medians of
+// 3, the ramp continued / constant 24 / 32 / 40): M=65 6.34 / 6.74 / 6.45 / 6.33, M=80 7.12 /
+// 7.41 / 7.20 / 7.02, M=96 8.83 / 8.89 / 8.83 / 8.77, M=112 10.58 / 9.90 / 9.96 / 9.91, M=128
+// 12.08 / 11.64 / 11.45 / 11.40.  The one launch beats the pair up to M=128 (the pair: M=65
+// 7.57, M=80 9.02, M=96 10.46, M=112 11.50, M=128 12.48); from about M=100 at TP=8 its grid is
+// larger than what the GPU holds at once, which the dispatch order allows (producers wait on
+// nothing, and a row's consumers come in one block).
 #ifndef ARNORM_STEP_MAX_BYTES
-#define ARNORM_STEP_MAX_BYTES (7u << 20)
+#define ARNORM_STEP_MAX_BYTES (16u << 20)
 #endif
 #ifndef ARNORM_STEP_MAX_M
-#define ARNORM_STEP_MAX_M 64
+#define ARNORM_STEP_MAX_M 128
 #endif
 #ifndef ARNORM_STEP_POLL_DELAY
 #define ARNORM_STEP_POLL_DELAY 22
@@ -210,6 +217,9 @@ std::atomic<int> g_poll_mode{0};   // Gather polls: 0 = automatic, 1 = re-read a
 #endif
 #ifndef ARNORM_STEP_POLL_DELAY_RAMP_M
 #define ARNORM_STEP_POLL_DELAY_RAMP_M 48
+#endif
+#ifndef ARNORM_STEP_POLL_DELAY_RAMP_END
+#define ARNORM_STEP_POLL_DELAY_RAMP_END 64
 #endif
 // gather_push_poll runs as one launch when the gathered rows total at most this many
 // bytes, its pollers waiting ARNORM_GATHER_STEP_POLL_DELAY s_sleep steps (8 more above 2
@@ -589,7 +599,10 @@ int push_reduce_norm_launch(const uint16_t *partials, const uint16_t *residual, 
   a.r.poll_all = 1;
   a.r.poll_delay = K != 4 ? ARNORM_STEP_POLL_DELAY
                           : ARNORM_STEP_POLL_DELAY_SPLIT4 +
-                                (M > ARNORM_STEP_POLL_DELAY_RAMP_M ? (M - ARNORM_STEP_POLL_DELAY_RAMP_M + 1) / 2 : 0);
+                                (M > ARNORM_STEP_POLL_DELAY_RAMP_M
+                                     ? ((M < ARNORM_STEP_POLL_DELAY_RAMP_END ? M : ARNORM_STEP_POLL_DELAY_RAMP_END) -
+                                        ARNORM_STEP_POLL_DELAY_RAMP_M + 1) / 2
+                                     : 0);
   a.partials = reinterpret_cast<const u32x4 *>(partials);
   a.frags = (uint32_t)M * arn::kRowFrags;
   const int U = ARNORM_STEP_PUSH_U;
