@@ -200,14 +200,21 @@ std::atomic<int> g_poll_mode{0};   // Gather polls: 0 = automatic, 1 = re-read a
 // 3, the ramp continued / constant 24 / 32 / 40): M=65 6.34 / 6.74 / 6.45 / 6.33, M=80 7.12 /
 // 7.41 / 7.20 / 7.02, M=96 8.83 / 8.89 / 8.83 / 8.77, M=112 10.58 / 9.90 / 9.96 / 9.91, M=128
 // 12.08 / 11.64 / 11.45 / 11.40.  The one launch beats the pair up to M=128 (the pair: M=65
-// 7.57, M=80 9.02, M=96 10.46, M=112 11.50, M=128 12.48); from about M=100 at TP=8 its grid is
-// larger than what the GPU holds at once, which the dispatch order allows (producers wait on
-// nothing, and a row's consumers come in one block).
+// 7.57, M=80 9.02, M=96 10.46, M=112 11.50, M=128 12.48), and with rows split 4 ways up to
+// ARNORM_STEP_SPLIT4_MAX_M also above, where the pair takes whole rows (one launch / the
+// pair, medians of 3: M=129 11.32 / 12.79, M=144 12.60 / 13.63, M=160 14.05 / 15.02, M=192
+// 16.68 / 17.32, M=224 18.54 / 19.26, M=256 20.63 / 21.25; the pair with 4-way rows was
+// slower still, M=192 17.65).  From about M=100 at TP=8 its grid is larger than what the
+// GPU holds at once, which the dispatch order allows (producers wait on nothing, and a row's
+// consumers come in one block).
 #ifndef ARNORM_STEP_MAX_BYTES
-#define ARNORM_STEP_MAX_BYTES (16u << 20)
+#define ARNORM_STEP_MAX_BYTES (32u << 20)
 #endif
 #ifndef ARNORM_STEP_MAX_M
-#define ARNORM_STEP_MAX_M 128
+#define ARNORM_STEP_MAX_M 256
+#endif
+#ifndef ARNORM_STEP_SPLIT4_MAX_M
+#define ARNORM_STEP_SPLIT4_MAX_M 256
 #endif
 #ifndef ARNORM_STEP_POLL_DELAY
 #define ARNORM_STEP_POLL_DELAY 22
@@ -572,7 +579,12 @@ int push_reduce_norm_launch(const uint16_t *partials, const uint16_t *residual, 
   // One launch where its consumers, re-reading every slot on each poll pass after the
   // delay below, beat the pair (see ARNORM_STEP_MAX_BYTES).  Rows split 7 ways beat 14 (M=4:
   // 4.8 against 5.3 us) and one workgroup per row (6.5 us).
-  const int K = nbox != nullptr ? reduce_split(M, true) : 1;
+  int K = nbox != nullptr ? reduce_split(M, true) : 1;
+  // the automatic split takes whole rows above ARNORM_SPLIT4_MAX_M (the pair's crossover);
+  // the one launch keeps rows split 4 ways up to ARNORM_STEP_SPLIT4_MAX_M
+  if (nbox != nullptr && K == 1 && g_reduce_split.load(std::memory_order_relaxed) == 0 &&
+      M <= ARNORM_STEP_SPLIT4_MAX_M && M * 4 <= kSplitMaxGrid)
+    K = 4;
   const bool one_launch =
       K > 1 && M <= ARNORM_STEP_MAX_M && (uint64_t)tp * M * arn::kRowBytes <= ARNORM_STEP_MAX_BYTES;
   if (!one_launch) {
