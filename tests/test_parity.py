@@ -142,15 +142,17 @@ def test_push_reduce_norm_one_call(lib, name, with_box, split):
 @pytest.mark.parametrize("tp,split,m", [(2, 0, 13), (3, 0, 13), (8, 0, 13), (3, 14, 13), (8, 14, 13), (5, 4, 13),
                                         (8, 8, 13), (8, 0, 3), (8, 0, 4), (8, 0, 5), (8, 0, 9), (4, 0, 7),
                                         (8, 0, 14), (8, 0, 31), (8, 0, 32), (8, 0, 33), (8, 0, 34), (8, 0, 64),
-                                        (8, 0, 65), (8, 0, 128), (8, 0, 129), (8, 0, 256), (8, 0, 257)])
+                                        (8, 0, 65), (8, 0, 128), (8, 0, 129), (8, 0, 256), (8, 0, 257),
+                                        (8, 0, 512), (8, 0, 513)])
 def test_push_reduce_norm_torture(lib, tp, split, m):
     """Torture rows through arnorm_push_reduce_norm.  With the automatic split at TP=8 the
     one launch (a row's workgroups on one XCD, in blocks of 8 rows) takes 7 parts at M=3
     (one short block), 4, 5, 9 (a full block and one row), 13, 14 and 31 (an odd producer
     count per slot, rounded up to even: the extra producer has no fragments) and 32, and 4
-    parts at M=33, 34, 64, 65, 128, 129 and 256 (the last row count in one launch; from
-    about M=100 the grid is larger than what the GPU holds at once); forced splits of 4, 8
-    and 14 ways run at M=13; at M=257 the pair of launches runs, one workgroup per row."""
+    parts at M=33, 34, 64, 65, 128, 129 and 256 (from about M=100 the grid is larger than
+    what the GPU holds at once), and 2 parts at M=257 and 512 (the last row count in one
+    launch); forced splits of 4, 8 and 14 ways run at M=13; at M=513 the pair of launches
+    runs, one workgroup per row."""
     say(f"[parity] push_reduce_norm torture tp={tp} split={split} m={m}")
     lib.set_reduce_split(split)
     rng = np.random.default_rng(170 + tp + 32 * m)

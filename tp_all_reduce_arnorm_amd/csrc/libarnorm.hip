@@ -175,8 +175,8 @@ std::atomic<int> g_poll_mode{0};   // Gather polls: 0 = automatic, 1 = re-read a
 #endif
 // arnorm_push_reduce_norm runs as one launch (with a norm box) up to ARNORM_STEP_MAX_M rows
 // whose TP slots total at most ARNORM_STEP_MAX_BYTES, else as the pair.  Its consumers wait
-// ARNORM_STEP_POLL_DELAY s_sleep steps of 64 cycles (ARNORM_STEP_POLL_DELAY_SPLIT4 for rows
-// split 4 ways) before their first poll pass, about as long as the producers' stores take
+// ARNORM_STEP_POLL_DELAY s_sleep steps of 64 cycles (ARNORM_STEP_POLL_DELAY_SPLIT4 and its ramp
+// for rows split 4 or 2 ways) before their first poll pass, about as long as the producers' stores take
 // to land: polling the lines while they are written slowed the stores.  Measured at TP=8,
 // us per call, medians of 2 (delay 0 / 16 / 24 / 32 / 48 steps): M=1 3.81 / 3.96-3.98 /
 // 3.69 / 3.89 / 4.32, M=4 4.22-4.25 / 3.98-4.05 / 4.12 / 4.32-4.33 / 4.75-4.76, M=8
@@ -204,17 +204,23 @@ std::atomic<int> g_poll_mode{0};   // Gather polls: 0 = automatic, 1 = re-read a
 // ARNORM_STEP_SPLIT4_MAX_M also above, where the pair takes whole rows (one launch / the
 // pair, medians of 3: M=129 11.32 / 12.79, M=144 12.60 / 13.63, M=160 14.05 / 15.02, M=192
 // 16.68 / 17.32, M=224 18.54 / 19.26, M=256 20.63 / 21.25; the pair with 4-way rows was
-// slower still, M=192 17.65).  From about M=100 at TP=8 its grid is larger than what the
-// GPU holds at once, which the dispatch order allows (producers wait on nothing, and a row's
-// consumers come in one block).
+// slower still, M=192 17.65), and then with rows split 2 ways (448-thread workgroups) up
+// to ARNORM_STEP_SPLIT2_MAX_M, where the split grid reaches its cap (one launch / the pair:
+// M=257 20.04 / 23.64, M=300 22.68 / 25.79, M=384 28.56 / 30.85, M=448 33.29 / 34.46, M=512
+// 38.02 / 38.65).  From about M=100 at TP=8 its grid is larger than what the GPU holds at
+// once, which the dispatch order allows (producers wait on nothing, and a row's consumers
+// come in one block).
 #ifndef ARNORM_STEP_MAX_BYTES
-#define ARNORM_STEP_MAX_BYTES (32u << 20)
+#define ARNORM_STEP_MAX_BYTES (64u << 20)
 #endif
 #ifndef ARNORM_STEP_MAX_M
-#define ARNORM_STEP_MAX_M 256
+#define ARNORM_STEP_MAX_M 512
 #endif
 #ifndef ARNORM_STEP_SPLIT4_MAX_M
 #define ARNORM_STEP_SPLIT4_MAX_M 256
+#endif
+#ifndef ARNORM_STEP_SPLIT2_MAX_M
+#define ARNORM_STEP_SPLIT2_MAX_M 512
 #endif
 #ifndef ARNORM_STEP_POLL_DELAY
 #define ARNORM_STEP_POLL_DELAY 22
@@ -581,10 +587,14 @@ int push_reduce_norm_launch(const uint16_t *partials, const uint16_t *residual, 
   // 4.8 against 5.3 us) and one workgroup per row (6.5 us).
   int K = nbox != nullptr ? reduce_split(M, true) : 1;
   // the automatic split takes whole rows above ARNORM_SPLIT4_MAX_M (the pair's crossover);
-  // the one launch keeps rows split 4 ways up to ARNORM_STEP_SPLIT4_MAX_M
-  if (nbox != nullptr && K == 1 && g_reduce_split.load(std::memory_order_relaxed) == 0 &&
-      M <= ARNORM_STEP_SPLIT4_MAX_M && M * 4 <= kSplitMaxGrid)
-    K = 4;
+  // the one launch keeps rows split 4 ways up to ARNORM_STEP_SPLIT4_MAX_M, then 2 ways up to
+  // ARNORM_STEP_SPLIT2_MAX_M
+  if (nbox != nullptr && K == 1 && g_reduce_split.load(std::memory_order_relaxed) == 0) {
+    if (M <= ARNORM_STEP_SPLIT4_MAX_M && M * 4 <= kSplitMaxGrid)
+      K = 4;
+    else if (M <= ARNORM_STEP_SPLIT2_MAX_M && M * 2 <= kSplitMaxGrid)
+      K = 2;
+  }
   const bool one_launch =
       K > 1 && M <= ARNORM_STEP_MAX_M && (uint64_t)tp * M * arn::kRowBytes <= ARNORM_STEP_MAX_BYTES;
   if (!one_launch) {
@@ -609,7 +619,7 @@ int push_reduce_norm_launch(const uint16_t *partials, const uint16_t *residual, 
   a.r.eps = eps;
   a.r.spin_limit = g_spin_limit.load(std::memory_order_relaxed);
   a.r.poll_all = 1;
-  a.r.poll_delay = K != 4 ? ARNORM_STEP_POLL_DELAY
+  a.r.poll_delay = K != 4 && K != 2 ? ARNORM_STEP_POLL_DELAY
                           : ARNORM_STEP_POLL_DELAY_SPLIT4 +
                                 (M > ARNORM_STEP_POLL_DELAY_RAMP_M
                                      ? ((M < ARNORM_STEP_POLL_DELAY_RAMP_END ? M : ARNORM_STEP_POLL_DELAY_RAMP_END) -
@@ -641,6 +651,9 @@ int push_reduce_norm_launch(const uint16_t *partials, const uint16_t *residual, 
                       grid, dim3(nt), stream, a);
 #define ARNORM_STEP_LAUNCH(TPV)                                                                                   \
   case TPV:                                                                                                      \
+    if (K == 2) {                                                                                                \
+      ARNORM_STEP_LAUNCH_K(TPV, 2)                                                                               \
+    }                                                                                                            \
     if (K == 4) {                                                                                                \
       ARNORM_STEP_LAUNCH_K(TPV, 4)                                                                               \
     }                                                                                                            \
