@@ -264,7 +264,7 @@ def gather_bytes(tp, m, s, copy=True):
 
 def time_gather(lib, torch, calls=2000, chunk=200, name="gather_tp8_m32", one_launch=True, m=None):
     """µs per Gather call, graph-replayed: gather_push_poll (every rank's push and the
-    copying poll, one launch for calls within 8 MiB of gathered rows), or with one_launch False the pair
+    copying poll, one launch for calls within 32 MiB of gathered rows), or with one_launch False the pair
     gather_push + gather_poll.  gather_tp8_m32 is TP=8, M=32, S=896; ctx and logits are the
     drafter's context-projection and lm_head shapes; m overrides the row count."""
     import dataclasses
@@ -650,7 +650,7 @@ def summarize_profiles(outdir):
                      "23 times, each launch after a 1 GiB read-only pass (torch's float32 sum) that evicts the "
                      "last-level cache", "arnorm_tp8_m4096_kernel_stats.md"),
             ("gather", "Gather at TP=8, S=896 words, cap=64, HIP-graph replay: 2000 gather_push_poll calls "
-                       "at M=32 (917504 B, within the 8 MiB one-launch limit, so one launch each), 2000 calls "
+                       "at M=32 (917504 B, within the 32 MiB one-launch limit, so one launch each), 2000 calls "
                        "of the pair gather_push of 8 slots + gather_poll with copy at M=32, then 2000 "
                        "one-launch gather_push_poll calls at M=4",
              "gather_tp8_m32_s896_kernel_stats.md"),
@@ -888,7 +888,7 @@ def main():
         },
         "gather": {
             "workload": "Gather TP=8 M=32 S=896 words cap=64: gather_push_poll with copy, HIP-graph replay "
-                        "(917504 B of gathered rows, within the 8 MiB one-launch limit, so every rank's push "
+                        "(917504 B of gathered rows, within the 32 MiB one-launch limit, so every rank's push "
                         "and the pollers run as one launch, as do all drafter_shapes entries); "
                         "two_launch_us_per_call is the pair gather_push + gather_poll",
             "us_per_call": round(gather_us, 3), "two_launch_us_per_call": round(gather_pair_us, 3),

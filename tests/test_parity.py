@@ -263,19 +263,20 @@ def test_drafter_gather_shapes(lib, name, m, tp):
 
 @pytest.mark.parametrize("name,m", [("gather_tp8_m32", 32), ("gather_tp8_m32", 16), ("gather_tp8_m32", 1),
                                     ("gather_tp8_m32", 54), ("gather_tp8_m32", 64), ("ctx", 64), ("logits", 4),
-                                    ("logits", 25), ("logits", 26),
+                                    ("logits", 25), ("logits", 26), ("logits", 102), ("logits", 103),
                                     ("logits", 2), ("logits", 1)])
 def test_gather_push_poll_one_call(lib, name, m):
-    """gather_push_poll (one launch for calls within 8 MiB, else the pair; the logits rows,
-    S=10240, fit 25 rows in it, not 26; its poll delay steps up above 2 and 4 MiB) against
-    the oracle's push of every rank followed by its poll: copy, then no-copy followed by a
-    copying poll."""
+    """gather_push_poll (one launch for calls within 32 MiB, else the pair; the logits rows,
+    S=10240, fit 102 rows in it, not 103; its poll delay steps at 2, 4 and 8 MiB, which
+    logits M=25 and 26 straddle) against the oracle's push of every rank followed by its
+    poll: copy, then no-copy followed by a copying poll."""
     import dataclasses
 
     import torch
 
     say(f"[parity] gather_push_poll {name} M={m}")
     cfg = dataclasses.replace(wl.CONFIGS[name], m=m)
+    cfg = dataclasses.replace(cfg, cap=max(cfg.cap, m))
     shards = wl.gather_shards(cfg) if name == "gather_tp8_m32" else wl.bf16_shards(cfg)
     gshape = (cfg.cap, cfg.tp * cfg.s)
     gbox_d, gbox_h = armed_box(gshape), oracle.arm(np.empty(gshape, dtype=np.uint32))

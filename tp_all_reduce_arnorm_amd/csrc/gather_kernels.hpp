@@ -157,7 +157,7 @@ struct GatherStepArgs {
 template <int TP, int U, int POL_PUSH, int POL_LD, int POL_ST, int POL_CP>
 __global__ void __launch_bounds__(256) gather_push_poll_kernel(GatherStepArgs a) {
   const uint32_t row_frags = TP * a.frags;
-  const uint32_t n = a.M * row_frags;  // the gathered range: the host keeps it within 8 MiB
+  const uint32_t n = a.M * row_frags;  // the gathered range: the host keeps it within 32 MiB
   if (blockIdx.x < a.producers) {
     const uint32_t i = blockIdx.x * 256u + threadIdx.x;
     if (i >= n) return;

@@ -236,7 +236,7 @@ std::atomic<int> g_poll_mode{0};   // Gather polls: 0 = automatic, 1 = re-read a
 #endif
 // gather_push_poll runs as one launch when the gathered rows total at most this many
 // bytes, its pollers waiting ARNORM_GATHER_STEP_POLL_DELAY s_sleep steps (8 more above 2
-// MiB, 16 more above 4 MiB) and then re-reading every pending fragment per pass, else as the pair
+// MiB, 16 more above 4 MiB, 8 more above 8 MiB) and then re-reading every pending fragment per pass, else as the pair
 // gather_push + gather_poll.  Measured on MI355X at TP=8 (HIP-graph replay, us per call,
 // medians of 2, the pair / one launch with delay 0 / 16 / 24 / 32): S=896 M=4 3.50 / 2.33-2.36
 // / 2.27-2.28 / 2.49 / 2.70, M=32 3.66-3.72 / 2.70-2.71 / 2.43 / 2.64-2.65 / 2.86, M=64 (1.84
@@ -246,9 +246,13 @@ std::atomic<int> g_poll_mode{0};   // Gather polls: 0 = automatic, 1 = re-read a
 // M=32 (10.5 MB) 8.50 / - / 8.32 / 8.49 / 8.60.  Finer, on two boxes (delay 10 / 12 / 14 /
 // 16): S=896 M=4 2.20 / 2.17-2.19 / 2.23 / 2.25-2.29, M=32 2.73 / 2.35-2.39 / 2.38-2.39 /
 // 2.43-2.44; logits M=4 2.74-2.75 / 2.43-2.48 / 2.51-2.52 / 2.55-2.57: 14 keeps a margin above
-// the cliff at 10.
+// the cliff at 10.  Above 8 MiB, medians of 3 on one box, the pair / one launch with 22 / 30
+// / 38 more steps: S=896 M=300 (8.6 MB) 7.86 / 6.59 / 6.65 / 6.72, M=400 9.89 / 8.71 / 8.84 /
+// 9.03, M=600 15.25 / 13.04 / 13.13 / 13.19, M=1000 22.76 / 22.55 / 22.68 / 22.83; logits M=26
+// 7.79 / 6.29 / 6.43 / 6.65, M=48 13.53 / 12.01 / 12.08 / 12.20, M=64 17.39 / 16.85 / 16.98 /
+// 17.10.
 #ifndef ARNORM_GATHER_STEP_MAX_BYTES
-#define ARNORM_GATHER_STEP_MAX_BYTES (8u << 20)
+#define ARNORM_GATHER_STEP_MAX_BYTES (32u << 20)
 #endif
 #ifndef ARNORM_GATHER_STEP_POLL_DELAY
 #define ARNORM_GATHER_STEP_POLL_DELAY 14
@@ -256,13 +260,15 @@ std::atomic<int> g_poll_mode{0};   // Gather polls: 0 = automatic, 1 = re-read a
 static_assert(ARNORM_GATHER_STEP_MAX_BYTES <= (1u << 30), "the one-launch Gather range is one buffer resource");
 // Steps of the one-launch Gather's poll delay for a gathered range of `bytes`.
 uint32_t gather_step_delay(uint64_t bytes) {
-  return bytes <= (2u << 20) ? ARNORM_GATHER_STEP_POLL_DELAY
-                             : bytes <= (4u << 20) ? ARNORM_GATHER_STEP_POLL_DELAY + 8 : ARNORM_GATHER_STEP_POLL_DELAY + 16;
+  return bytes <= (2u << 20)   ? ARNORM_GATHER_STEP_POLL_DELAY
+         : bytes <= (4u << 20) ? ARNORM_GATHER_STEP_POLL_DELAY + 8
+         : bytes <= (8u << 20) ? ARNORM_GATHER_STEP_POLL_DELAY + 16
+                               : ARNORM_GATHER_STEP_POLL_DELAY + 8;
 }
 // twoshot_push_reduce_read runs as one launch when the TP slots of rows < M total at
 // most this many bytes, its owners and readers waiting ARNORM_TWOSHOT_STEP_POLL_DELAY
-// s_sleep steps (6 more above 2 MiB of slots) and then re-reading every pending fragment
-// on each poll pass, else as its three launches.  Measured at TP=8, width 7168, with the re-arms of ARNORM_POL_REARM_STEP
+// s_sleep steps (6 more above 2 MiB of slots, 22 more above 8 MiB) and then re-reading every
+// pending fragment on each poll pass, else as its three launches.  Measured at TP=8, width 7168, with the re-arms of ARNORM_POL_REARM_STEP
 // (us per call, medians of 2, three launches / one launch with delay 0 / 16 / 24 / 32):
 // M=1 - / 4.04-4.06 / 3.86-3.87 / 4.07 / 4.27-4.29, M=4 6.22-6.29 / 4.44-4.45 / 4.05-4.06 /
 // 4.26-4.27 / 4.47-4.48, M=16 6.43-6.44 / 4.75 / 4.29-4.30 / 4.50-4.51 / 4.71-4.72, M=32
@@ -275,15 +281,21 @@ uint32_t gather_step_delay(uint64_t bytes) {
 // one box, delay 10 / 16 / 24: M=16 4.13 / 4.25 / 4.47, M=20 4.43 / 4.37 / 4.58, M=24 4.93 /
 // 4.50 / 4.70, M=28 5.43 / 4.67 / 4.84, M=32 5.74 / 4.82 / 4.97, M=40 6.01 / 5.33 / 5.44, M=48
 // 6.07 / 5.67 / 5.73, M=56 6.14 / 6.20 / 6.41, M=64 6.82 / 6.53 / 6.71, M=73 7.38 / 7.19 / 7.34.
+// Above 8 MiB, three launches / one launch with 16 / 24 / 32 steps: M=74 10.17 / 10.34 / 9.99
+// / 9.82, M=80 10.14 / 8.86 / 8.92 / 9.02, M=96 11.15 / 11.48 / 11.17 / 11.07, M=128 13.11 /
+// 13.41 / 13.22 / 13.15, M=192 19.25 / 17.93 / 17.97 / 18.05, M=256 23.65 / 22.36 / 22.43 /
+// 22.49.
 #ifndef ARNORM_TWOSHOT_STEP_MAX_BYTES
-#define ARNORM_TWOSHOT_STEP_MAX_BYTES (8u << 20)
+#define ARNORM_TWOSHOT_STEP_MAX_BYTES (32u << 20)
 #endif
 #ifndef ARNORM_TWOSHOT_STEP_POLL_DELAY
 #define ARNORM_TWOSHOT_STEP_POLL_DELAY 10
 #endif
 // Steps of the one-launch two-shot call's poll delay for TP slots of `bytes` (rows < M).
 uint32_t twoshot_step_delay(uint64_t bytes) {
-  return bytes <= (2u << 20) ? ARNORM_TWOSHOT_STEP_POLL_DELAY : ARNORM_TWOSHOT_STEP_POLL_DELAY + 6;
+  return bytes <= (2u << 20)   ? ARNORM_TWOSHOT_STEP_POLL_DELAY
+         : bytes <= (8u << 20) ? ARNORM_TWOSHOT_STEP_POLL_DELAY + 6
+                               : ARNORM_TWOSHOT_STEP_POLL_DELAY + 22;
 }
 // The one-launch two-shot call places an owner workgroup and the reader of the same
 // fragments on one XCD always, and their producers too from this many blocks of 256
