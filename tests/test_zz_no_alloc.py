@@ -1,8 +1,8 @@
 """arnorm_push_reduce_norm_static, the entry point that allocates nothing (its norm box is
 the library's static device array), against arnorm_push_reduce_norm with a norm box the
 caller allocated: the same inputs give the same bits, on calls in a row with fewer rows
-each time (M = 64: push + split consumer; M = 8 and 2: one launch), and the array's row
-limit is refused before anything is launched."""
+each time (M = 64, rows split 4 ways; M = 8 and 2, 7 ways; one launch each), and the
+array's row limit is refused before anything is launched."""
 
 import numpy as np
 import pytest
