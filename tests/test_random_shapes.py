@@ -56,9 +56,10 @@ def _draw_twoshot(rng, n):
 
 
 def _draw_arnorm_wide(rng, n):
-    """Larger caps (up to 300 rows: the 4-way split up to M=128 and the whole-row grid that
-    loops over rows above 128), the splits of 4 and 8 ways, and the call with the library's
-    own norm box (M <= 64)."""
+    """Larger caps (up to 300 rows: the pair's 4-way split up to M=128 and its whole-row grid
+    that loops over rows above 128; the one launch's 4-way rows up to M=256 and 2-way rows
+    above), the splits of 4 and 8 ways, and the call with the library's own norm box
+    (M <= 64)."""
     cases = []
     for i in range(n):
         tp = int(rng.integers(2, 9))
