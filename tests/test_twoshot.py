@@ -195,7 +195,7 @@ def test_one_call_workloads(lib, name, calls):
 def test_one_call_torture(lib, tp, m):
     """Torture rows through the one call, one launch where the TP slots of rows < M fit
     32 MiB (at TP=8 M=292 is the last row count within it, M=293 the first above; M=73 and
-    74 straddle the poll delay's step at 8 MiB), with the
+    74 straddle its former limit of 8 MiB), with the
     other parity published and left untouched.  The one launch pads its producer groups to
     multiples of 8 workgroups from 24 per slot: TP=2..5 at M=13 and TP=8 at M=7, 8 and 13
     take the padded layout, TP=8 at M=6 the largest unpadded one, and M=9 and 73 (32 and 256

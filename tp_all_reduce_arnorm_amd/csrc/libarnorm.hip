@@ -267,8 +267,8 @@ uint32_t gather_step_delay(uint64_t bytes) {
 }
 // twoshot_push_reduce_read runs as one launch when the TP slots of rows < M total at
 // most this many bytes, its owners and readers waiting ARNORM_TWOSHOT_STEP_POLL_DELAY
-// s_sleep steps (6 more above 2 MiB of slots, 22 more above 8 MiB) and then re-reading every
-// pending fragment on each poll pass, else as its three launches.  Measured at TP=8, width 7168, with the re-arms of ARNORM_POL_REARM_STEP
+// s_sleep steps (6 more above 2 MiB of slots) and then re-reading every pending fragment on
+// each poll pass, else as its three launches.  Measured at TP=8, width 7168, with the re-arms of ARNORM_POL_REARM_STEP
 // (us per call, medians of 2, three launches / one launch with delay 0 / 16 / 24 / 32):
 // M=1 - / 4.04-4.06 / 3.86-3.87 / 4.07 / 4.27-4.29, M=4 6.22-6.29 / 4.44-4.45 / 4.05-4.06 /
 // 4.26-4.27 / 4.47-4.48, M=16 6.43-6.44 / 4.75 / 4.29-4.30 / 4.50-4.51 / 4.71-4.72, M=32
@@ -281,10 +281,11 @@ uint32_t gather_step_delay(uint64_t bytes) {
 // one box, delay 10 / 16 / 24: M=16 4.13 / 4.25 / 4.47, M=20 4.43 / 4.37 / 4.58, M=24 4.93 /
 // 4.50 / 4.70, M=28 5.43 / 4.67 / 4.84, M=32 5.74 / 4.82 / 4.97, M=40 6.01 / 5.33 / 5.44, M=48
 // 6.07 / 5.67 / 5.73, M=56 6.14 / 6.20 / 6.41, M=64 6.82 / 6.53 / 6.71, M=73 7.38 / 7.19 / 7.34.
-// Above 8 MiB, three launches / one launch with 16 / 24 / 32 steps: M=74 10.17 / 10.34 / 9.99
-// / 9.82, M=80 10.14 / 8.86 / 8.92 / 9.02, M=96 11.15 / 11.48 / 11.17 / 11.07, M=128 13.11 /
-// 13.41 / 13.22 / 13.15, M=192 19.25 / 17.93 / 17.97 / 18.05, M=256 23.65 / 22.36 / 22.43 /
-// 22.49.
+// Above 8 MiB, with the producers' default-policy loads, three launches / one launch with
+// 16 / 24 / 32 steps: M=74 10.17 / 9.78 / 9.12 / 8.94, M=75 - / 7.86 / 8.01 / 8.23, M=80 10.14
+// / 8.18 / 8.37 / 8.61, M=96 11.15 / 9.48 / 9.63 / 9.85, M=128 13.11 / 12.22 / 12.39 / 12.60,
+// M=160 - / 15.12 / 15.00 / 15.12, M=224 - / 19.45 / 19.50 / 19.62, M=292 - / 23.54 / 23.59 /
+// 23.76 (M=74 is slower than its neighbours at every delay).
 #ifndef ARNORM_TWOSHOT_STEP_MAX_BYTES
 #define ARNORM_TWOSHOT_STEP_MAX_BYTES (32u << 20)
 #endif
@@ -293,9 +294,7 @@ uint32_t gather_step_delay(uint64_t bytes) {
 #endif
 // Steps of the one-launch two-shot call's poll delay for TP slots of `bytes` (rows < M).
 uint32_t twoshot_step_delay(uint64_t bytes) {
-  return bytes <= (2u << 20)   ? ARNORM_TWOSHOT_STEP_POLL_DELAY
-         : bytes <= (8u << 20) ? ARNORM_TWOSHOT_STEP_POLL_DELAY + 6
-                               : ARNORM_TWOSHOT_STEP_POLL_DELAY + 22;
+  return bytes <= (2u << 20) ? ARNORM_TWOSHOT_STEP_POLL_DELAY : ARNORM_TWOSHOT_STEP_POLL_DELAY + 6;
 }
 // The one-launch two-shot call places an owner workgroup and the reader of the same
 // fragments on one XCD always, and their producers too from this many blocks of 256
