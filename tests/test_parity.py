@@ -111,8 +111,8 @@ def test_split_rows(lib, name, split):
                                                 ("tp2_m1", True, 14), ("tp8_m4", True, 14), ("tp8_m4", True, 4),
                                                 ("tp8_m4", True, 8), ("tp8_m64", True, 4), ("tp8_m64", True, 8)])
 def test_push_reduce_norm_one_call(lib, name, with_box, split):
-    """arnorm_push_reduce_norm (one launch with a norm box where the TP slots of rows < M
-    fit 1 MiB, rows split 7 or 14 ways; else the pair of launches) against the oracle's
+    """arnorm_push_reduce_norm (with a norm box one launch, rows split the automatic 7 or 4
+    ways or the forced 4, 8 or 14; without one the pair of launches) against the oracle's
     push of every slot followed by its consumer."""
     cfg = wl.CONFIGS[name]
     say(f"[parity] push_reduce_norm {name} norm_box={with_box} split={split}")
