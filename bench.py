@@ -26,6 +26,8 @@ The same JSON line carries:
   gather        Gather calls (TP=8, M=32, S=896, and the drafter's shapes)
   twoshot       the two-shot stand-in call at M=4 and its kernels at M=4096
   drafter_step  a drafter decode step's collectives: 11 ArNorm calls and 2 Gathers
+  workloads     GPU µs per call at the named ArNorm configurations as stated: tp2_m1
+                (TP=2, M=1, residual), tp8_m4 and tp8_m64 (TP=8, M=64, residual)
   cpu_baseline  the CPU oracle on this host's cores, one thread: the same TP=8, M=4
                 call (the headline), and per workload tp2_m1, tp8_m4, tp8_m64,
                 gather_tp8_m32 and tp8_m4096
@@ -198,6 +200,47 @@ def time_latency(lib, torch, steps, warmup, chunk=200, one_launch=True, m=None):
     elapsed = gpu_span_us(torch, timed) * 1e-6
     assert lib.status() == lib.OK
     return elapsed
+
+
+def time_config(lib, torch, name, calls=2000, chunk=200):
+    """GPU µs per stand-in ArNorm call at one of the named workload configurations, as that
+    configuration states it (TP, M, residual, capacity, parities): one arnorm_push_reduce_norm
+    per call with a norm box, the residual an input of its own and residual_out another
+    buffer, graph-replayed and timed as time_latency."""
+    from tp_all_reduce_arnorm_amd import workloads as wl
+
+    cfg = wl.CONFIGS[name]
+    src = wl.ArNormInputs(cfg)
+    box = torch.empty((cfg.parities, cfg.tp, cfg.cap, HIDDEN // 2), dtype=torch.int32, device="cuda")
+    nbox = torch.empty((cfg.parities, cfg.cap, 256), dtype=torch.int32, device="cuda")
+    assert lib.lamport_arm(box) is True and lib.lamport_arm(nbox) is True
+    parts = [torch.from_numpy(src.partials().view(np.int16)).cuda() for _ in range(2)]
+    res = torch.from_numpy(src.residual().view(np.int16)).cuda() if cfg.residual else None
+    gamma = torch.from_numpy(src.gamma.view(np.int16)).cuda()
+    out = torch.empty((cfg.m, HIDDEN), dtype=torch.int16, device="cuda")
+    rout = torch.empty((cfg.m, HIDDEN), dtype=torch.int16, device="cuda")
+
+    def call(i):
+        assert lib.arnorm_push_reduce_norm(parts[i % 2], res, gamma, box, i % cfg.parities, EPS, out, rout,
+                                           norm_box=nbox) is True
+
+    for i in range(4):
+        call(i)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(chunk):
+            call(i)
+    for _ in range(3):  # a new graph's first replays run slower
+        g.replay()
+
+    def timed():
+        for _ in range(calls // chunk):
+            g.replay()
+
+    us = gpu_span_us(torch, timed) / (calls // chunk * chunk)
+    assert lib.status() == lib.OK
+    return cfg, us
 
 
 def time_drafter_step(lib, torch, steps=400, layers=11):
@@ -796,6 +839,13 @@ def main():
     _, gather_pair_us = time_gather(lib, torch, one_launch=False)
     ts = time_twoshot(lib, torch)
     step_us = time_drafter_step(lib, torch)
+    work = {}
+    for name in ("tp2_m1", "tp8_m4", "tp8_m64"):
+        c, us = time_config(lib, torch, name)
+        nb = push_bytes(c.tp, c.m) + reduce_bytes(c.tp, c.m, c.residual)
+        work[name] = {"tp": c.tp, "m": c.m, "residual": c.residual, "parities": c.parities, "cap": c.cap,
+                      "us_per_call": round(us, 3), "algorithmic_bytes": nb,
+                      "algorithmic_gbps": round(nb / (us * 1e-6) / 1e9, 1)}
     shapes = {}
     for name in ("ctx", "logits"):
         c, us = time_gather(lib, torch, name=name)
@@ -918,6 +968,13 @@ def main():
             "us_per_step": round(step_us, 2),
             "context": "the pages quote 6-9 us per stock one-shot all-reduce (11 per step) and 16-20 us per "
                        "stock all-gather (2 per step) on their NVLink hardware: another machine's figures",
+        },
+        "workloads": {
+            "note": "the named configurations as they are stated (TP, M, residual, capacity, parities), one "
+                    "arnorm_push_reduce_norm per call, graph-replayed, HIP events; algorithmic bytes are the "
+                    "push of every slot plus the consumer's, per call; the Gather configuration is `gather`, "
+                    "the M=4096 one `roofline` and `push`",
+            **work,
         },
         "cpu_baseline": cpu,
     }
