@@ -638,6 +638,10 @@ int push_reduce_norm_launch(const uint16_t *partials, const uint16_t *residual, 
                                      : 0);
   a.partials = reinterpret_cast<const u32x4 *>(partials);
   a.frags = (uint32_t)M * arn::kRowFrags;
+  // The residual rows are read with the default cache policy here (the layer before wrote
+  // them; non-temporal reads fetched them from HBM: TP=8 with a residual, M=64 6.09 against
+  // 5.77 us, M=128 13.44 / 11.77, M=256 24.89 / 21.08, M=512 44.73 / 38.71, M=1..16 and the
+  // drafter step the same); the pair and the M=4096 consumer keep kPolIn.
   const int U = ARNORM_STEP_PUSH_U;
   const uint32_t nt = arn::split_threads(K);
   // Workgroups of at most 128 threads (rows split 7 ways) come in an even number of
@@ -655,7 +659,7 @@ int push_reduce_norm_launch(const uint16_t *partials, const uint16_t *residual, 
   const bool res = residual != nullptr;
 #define ARNORM_STEP_LAUNCH_K(TPV, KV)                                                                              \
   return res ? launch(arn::push_reduce_kernel<TPV, true, KV, ARNORM_STEP_PUSH_U, kPolPush, kPolPoll, kPolRearmStep,  \
-                                              kPolIn, kPolIO>,                                                     \
+                                              arn::kPolPlain, kPolIO>,                                             \
                       grid, dim3(nt), stream, a)                                                                   \
              : launch(arn::push_reduce_kernel<TPV, false, KV, ARNORM_STEP_PUSH_U, kPolPush, kPolPoll, kPolRearmStep, \
                                               kPolIn, kPolIO>,                                                     \
