@@ -638,10 +638,13 @@ int push_reduce_norm_launch(const uint16_t *partials, const uint16_t *residual, 
                                      : 0);
   a.partials = reinterpret_cast<const u32x4 *>(partials);
   a.frags = (uint32_t)M * arn::kRowFrags;
-  // The residual rows are read with the default cache policy here (the layer before wrote
-  // them; non-temporal reads fetched them from HBM: TP=8 with a residual, M=64 6.09 against
-  // 5.77 us, M=128 13.44 / 11.77, M=256 24.89 / 21.08, M=512 44.73 / 38.71, M=1..16 and the
-  // drafter step the same); the pair and the M=4096 consumer keep kPolIn.
+  // The residual rows are read with the default cache policy here, so that a residual buffer
+  // read again unchanged stays in the last-level cache (with non-temporal reads it came from
+  // HBM on every call: TP=8, one residual buffer for every call, M=64 6.09 against 5.77 us,
+  // M=128 13.44 / 11.77, M=256 24.89 / 21.08, M=512 44.73 / 38.71; M=1..16 and the drafter
+  // step the same).  Rows that the previous call stored as its residual_out are still in
+  // that cache and read from it with either policy (calls chained that way, M=16..512, within
+  // 0.05 us).  The pair and the M=4096 consumer keep kPolIn.
   const int U = ARNORM_STEP_PUSH_U;
   const uint32_t nt = arn::split_threads(K);
   // Workgroups of at most 128 threads (rows split 7 ways) come in an even number of
