@@ -143,7 +143,7 @@ def time_latency(lib, torch, steps, warmup, chunk=200, one_launch=True, m=None):
     """GPU seconds for exactly `steps` stand-in calls at TP=8, M=4 (or M=m), no
     residual, graph-replayed (graphs of `chunk` calls and one of the remainder), timed
     by gpu_span_us.  one_launch: arnorm_push_reduce_norm (every rank's push and the
-    consumer in one launch within the library's one-launch limits, M <= 512 at TP=8, else
+    consumer in one launch within the library's one-launch limits, M <= 562 at TP=8, else
     the pair); else the pair arnorm_push + arnorm_reduce_norm."""
     import dataclasses
 

@@ -143,18 +143,22 @@ def test_push_reduce_norm_one_call(lib, name, with_box, split):
                                         (8, 8, 13), (8, 0, 3), (8, 0, 4), (8, 0, 5), (8, 0, 9), (4, 0, 7),
                                         (8, 0, 14), (8, 0, 31), (8, 0, 32), (8, 0, 33), (8, 0, 34), (8, 0, 64),
                                         (8, 0, 65), (8, 0, 128), (8, 0, 129), (8, 0, 256), (8, 0, 257),
-                                        (8, 0, 512), (8, 0, 513), (5, 0, 129), (4, 0, 200), (4, 0, 257),
-                                        (2, 0, 300)])
+                                        (8, 0, 512), (8, 0, 513), (8, 0, 562), (8, 0, 563), (5, 0, 129),
+                                        (4, 0, 200), (4, 0, 257), (4, 0, 936), (4, 0, 937), (6, 0, 704),
+                                        (6, 0, 705), (2, 0, 300), (2, 0, 1024), (2, 0, 1025)])
 def test_push_reduce_norm_torture(lib, tp, split, m):
     """Torture rows through arnorm_push_reduce_norm.  With the automatic split at TP=8 the
     one launch (a row's workgroups on one XCD, in blocks of 8 rows) takes 7 parts at M=3
     (one short block), 4, 5, 9 (a full block and one row), 13, 14 and 31 (an odd producer
     count per slot, rounded up to even: the extra producer has no fragments) and 32, and 4
     parts at M=33, 34, 64, 65, 128, 129 and 256 (from about M=100 the grid is larger than
-    what the GPU holds at once), and 2 parts at M=257 and 512 (the last row count in one
-    launch); forced splits of 4, 8 and 14 ways run at M=13; at M=513 the pair of launches
-    runs, one workgroup per row.  Below TP=8: 4 parts at TP=5 M=129 and TP=4 M=200, 2 parts
-    at TP=4 M=257 and TP=2 M=300, all one launch."""
+    what the GPU holds at once), and 2 parts at M=257, 512, 513 (past the split grid's cap
+    of 1024 workgroups) and 562 (the last row count whose grid, 10 M workgroups, fits the
+    one launch's 5632); forced splits of 4, 8 and 14 ways run at M=13; at M=563 the pair of
+    launches runs, one workgroup per row.  Below TP=8: 4 parts at TP=5 M=129 and TP=4 M=200,
+    2 parts at TP=4 M=257 and 936, TP=6 M=704 and TP=2 M=300 and 1024, all one launch, and
+    the pair at TP=4 M=937, TP=6 M=705 (one row past the grid limit) and TP=2
+    M=1025 (past the one launch's 1024 rows)."""
     say(f"[parity] push_reduce_norm torture tp={tp} split={split} m={m}")
     lib.set_reduce_split(split)
     rng = np.random.default_rng(170 + tp + 32 * m)

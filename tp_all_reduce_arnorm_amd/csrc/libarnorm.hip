@@ -174,7 +174,8 @@ std::atomic<int> g_poll_mode{0};   // Gather polls: 0 = automatic, 1 = re-read a
 #define ARNORM_POLL_ALL_MAX_BYTES (1u << 20)
 #endif
 // arnorm_push_reduce_norm runs as one launch (with a norm box) up to ARNORM_STEP_MAX_M rows
-// whose TP slots total at most ARNORM_STEP_MAX_BYTES, else as the pair.  Its consumers wait
+// whose TP slots total at most ARNORM_STEP_MAX_BYTES, in a grid of at most
+// ARNORM_STEP_MAX_GRID workgroups (the limit that binds at TP <= 8), else as the pair.  Its consumers wait
 // ARNORM_STEP_POLL_DELAY s_sleep steps of 64 cycles (ARNORM_STEP_POLL_DELAY_SPLIT4 and its ramp
 // for rows split 4 or 2 ways) before their first poll pass, about as long as the producers' stores take
 // to land: polling the lines while they are written slowed the stores.  Measured at TP=8,
@@ -204,23 +205,37 @@ std::atomic<int> g_poll_mode{0};   // Gather polls: 0 = automatic, 1 = re-read a
 // ARNORM_STEP_SPLIT4_MAX_M also above, where the pair takes whole rows (one launch / the
 // pair, medians of 3: M=129 11.32 / 12.79, M=144 12.60 / 13.63, M=160 14.05 / 15.02, M=192
 // 16.68 / 17.32, M=224 18.54 / 19.26, M=256 20.63 / 21.25; the pair with 4-way rows was
-// slower still, M=192 17.65), and then with rows split 2 ways (448-thread workgroups) up
-// to ARNORM_STEP_SPLIT2_MAX_M, where the split grid reaches its cap (one launch / the pair:
-// M=257 20.04 / 23.64, M=300 22.68 / 25.79, M=384 28.56 / 30.85, M=448 33.29 / 34.46, M=512
-// 38.02 / 38.65).  From about M=100 at TP=8 its grid is larger than what the GPU holds at
-// once, which the dispatch order allows (producers wait on nothing, and a row's consumers
-// come in one block).
+// slower still, M=192 17.65), and then with rows split 2 ways (448-thread workgroups)
+// (one launch / the pair: M=257 20.04 / 23.64, M=300 22.68 / 25.79, M=384 28.56 / 30.85,
+// M=448 33.29 / 34.46, M=512 38.02 / 38.65) while its grid holds at most
+// ARNORM_STEP_MAX_GRID workgroups (TP=8: M <= 562, TP=4: M <= 936, TP=2: M <= 1024).  Past
+// about 6000 workgroups the one launch fell behind the pair, by a margin that grew with M
+// and at a size that moved between boxes; below it, it won on every box (µs per call,
+// medians of 3, calls chained through residual_out, one launch / the pair; TP=8, 10 M
+// workgroups: M=513 39.06-39.36 / 42.14-42.19, M=544 41.56-42.10 / 43.92-44.02, M=560
+// 42.83-43.98 / 44.46-44.62, M=576 (5760) 44.01-44.14 / 45.42-45.66, M=600 50.12 / 46.85 and
+// M=608 46.06 / 47.75 on two boxes, M=640 53.2 / 49.6-49.9, M=1024 89.8-90.4 / 74.9-75.1;
+// TP=4, 6 M workgroups: M=513 22.21 / 25.17, M=768 31.20 / 33.42, M=896 (5376) 36.41-37.66 /
+// 38.61-38.64, M=1024 (6144) 47.79 / 42.96 and 41.98 / 42.71 on two boxes; TP=2, 4 M
+// workgroups: M=513 13.62 / 15.58, M=1024 24.52 / 26.12).  Consumers that watch one witness
+// per wave instead of re-reading every slot left that loss as it was (TP=8 M=640 53.24, M=1024
+// 90.62).  From about M=100 at TP=8 the grid is larger than what the GPU holds at once,
+// which the dispatch order allows (producers wait on nothing, and a row's consumers come in
+// one block).
 #ifndef ARNORM_STEP_MAX_BYTES
 #define ARNORM_STEP_MAX_BYTES (64u << 20)
 #endif
 #ifndef ARNORM_STEP_MAX_M
-#define ARNORM_STEP_MAX_M 512
+#define ARNORM_STEP_MAX_M 1024
+#endif
+#ifndef ARNORM_STEP_MAX_GRID
+#define ARNORM_STEP_MAX_GRID 5632
 #endif
 #ifndef ARNORM_STEP_SPLIT4_MAX_M
 #define ARNORM_STEP_SPLIT4_MAX_M 256
 #endif
 #ifndef ARNORM_STEP_SPLIT2_MAX_M
-#define ARNORM_STEP_SPLIT2_MAX_M 512
+#define ARNORM_STEP_SPLIT2_MAX_M 1024
 #endif
 #ifndef ARNORM_STEP_POLL_DELAY
 #define ARNORM_STEP_POLL_DELAY 22
@@ -599,15 +614,33 @@ int push_reduce_norm_launch(const uint16_t *partials, const uint16_t *residual, 
   int K = nbox != nullptr ? reduce_split(M, true) : 1;
   // the automatic split takes whole rows above ARNORM_SPLIT4_MAX_M (the pair's crossover);
   // the one launch keeps rows split 4 ways up to ARNORM_STEP_SPLIT4_MAX_M, then 2 ways up to
-  // ARNORM_STEP_SPLIT2_MAX_M
+  // ARNORM_STEP_SPLIT2_MAX_M.  Its 2-way rows may pass the split grid's cap, which leaves room
+  // for a producer on another stream: in one launch the producers come first and a row's
+  // workgroups in one block, so the dispatch order guarantees progress at any grid size.
   if (nbox != nullptr && K == 1 && g_reduce_split.load(std::memory_order_relaxed) == 0) {
     if (M <= ARNORM_STEP_SPLIT4_MAX_M && M * 4 <= kSplitMaxGrid)
       K = 4;
-    else if (M <= ARNORM_STEP_SPLIT2_MAX_M && M * 2 <= kSplitMaxGrid)
+    else if (M <= ARNORM_STEP_SPLIT2_MAX_M)
       K = 2;
   }
-  const bool one_launch =
-      K > 1 && M <= ARNORM_STEP_MAX_M && (uint64_t)tp * M * arn::kRowBytes <= ARNORM_STEP_MAX_BYTES;
+  const int U = ARNORM_STEP_PUSH_U;
+  const uint32_t nt = arn::split_threads(K);
+  // Workgroups of at most 128 threads (rows split 7 ways) come in an even number of
+  // producers per slot (an extra one finds no fragments and ends).  With an odd count, from
+  // M=14 the call paid most of a poll round trip more: TP=8, medians of 3 alternations, odd
+  // / rounded up to even, M=14 4.12 / 3.99, M=15 4.16 / 3.98, M=18 4.32 / 4.07, M=22 4.66 /
+  // 4.17, M=23 4.71 / 4.15, M=26 4.75 / 4.24, M=27 4.77 / 4.23, M=30 5.02 / 4.40, M=31 5.17 /
+  // 4.48 (two more boxes: M=30 5.08, 4.81 / 4.39, 4.47), the other row counts within 0.02.
+  // Rows split 4 ways (256 threads) keep the count: there rounding moved the slow row counts
+  // about (M=39 4.87 / 5.41, M=47 5.09 / 5.74, M=61 6.31 / 6.07, measured while the producers
+  // read their rows with non-temporal loads).
+  const uint64_t frags = (uint64_t)M * arn::kRowFrags;
+  uint64_t per_slot = (frags + nt * U - 1) / (nt * U);
+  if (nt <= 128) per_slot += per_slot & 1u;
+  const uint64_t grid_wgs = tp * per_slot + (uint64_t)(M + 7) / 8 * 8 * K;
+  const bool one_launch = K > 1 && M <= ARNORM_STEP_MAX_M &&
+                          (uint64_t)tp * M * arn::kRowBytes <= ARNORM_STEP_MAX_BYTES &&
+                          grid_wgs <= ARNORM_STEP_MAX_GRID;
   if (!one_launch) {
     // the same call as two launches: every rank's push, then the consumer
     const int rc = arnorm_push(partials, mailbox, parities, tp, cap, parity, 0, tp, M, stream);
@@ -637,7 +670,7 @@ int push_reduce_norm_launch(const uint16_t *partials, const uint16_t *residual, 
                                         ARNORM_STEP_POLL_DELAY_RAMP_M + 1) / 2
                                      : 0);
   a.partials = reinterpret_cast<const u32x4 *>(partials);
-  a.frags = (uint32_t)M * arn::kRowFrags;
+  a.frags = (uint32_t)frags;
   // The residual rows are read with the default cache policy here, so that a residual buffer
   // read again unchanged stays in the last-level cache (with non-temporal reads it came from
   // HBM on every call: TP=8, one residual buffer for every call, M=64 6.09 against 5.77 us,
@@ -645,20 +678,8 @@ int push_reduce_norm_launch(const uint16_t *partials, const uint16_t *residual, 
   // step the same).  Rows that the previous call stored as its residual_out are still in
   // that cache and read from it with either policy (calls chained that way, M=16..512, within
   // 0.05 us).  The pair and the M=4096 consumer keep kPolIn.
-  const int U = ARNORM_STEP_PUSH_U;
-  const uint32_t nt = arn::split_threads(K);
-  // Workgroups of at most 128 threads (rows split 7 ways) come in an even number of
-  // producers per slot (an extra one finds no fragments and ends).  With an odd count, from
-  // M=14 the call paid most of a poll round trip more: TP=8, medians of 3 alternations, odd
-  // / rounded up to even, M=14 4.12 / 3.99, M=15 4.16 / 3.98, M=18 4.32 / 4.07, M=22 4.66 /
-  // 4.17, M=23 4.71 / 4.15, M=26 4.75 / 4.24, M=27 4.77 / 4.23, M=30 5.02 / 4.40, M=31 5.17 /
-  // 4.48 (two more boxes: M=30 5.08, 4.81 / 4.39, 4.47), the other row counts within 0.02.
-  // Rows split 4 ways (256 threads) keep the count: there rounding moved the slow row counts
-  // about (M=39 4.87 / 5.41, M=47 5.09 / 5.74, M=61 6.31 / 6.07, measured while the producers
-  // read their rows with non-temporal loads).
-  a.per_slot = (a.frags + nt * U - 1) / (nt * U);
-  if (nt <= 128) a.per_slot += a.per_slot & 1u;
-  const dim3 grid(tp * a.per_slot + (M + 7) / 8 * 8 * K);
+  a.per_slot = (uint32_t)per_slot;
+  const dim3 grid((uint32_t)grid_wgs);
   const bool res = residual != nullptr;
 #define ARNORM_STEP_LAUNCH_K(TPV, KV)                                                                              \
   return res ? launch(arn::push_reduce_kernel<TPV, true, KV, ARNORM_STEP_PUSH_U, kPolPush, kPolPoll, kPolRearmStep,  \
