@@ -265,7 +265,12 @@ std::atomic<int> g_poll_mode{0};   // Gather polls: 0 = automatic, 1 = re-read a
 // / 38 more steps: S=896 M=300 (8.6 MB) 7.86 / 6.59 / 6.65 / 6.72, M=400 9.89 / 8.71 / 8.84 /
 // 9.03, M=600 15.25 / 13.04 / 13.13 / 13.19, M=1000 22.76 / 22.55 / 22.68 / 22.83; logits M=26
 // 7.79 / 6.29 / 6.43 / 6.65, M=48 13.53 / 12.01 / 12.08 / 12.20, M=64 17.39 / 16.85 / 16.98 /
-// 17.10.
+// 17.10.  Above 32 MiB, with the producers' default-policy loads (the pair / one launch,
+// medians of 3): S=896 M=1200 (34.4 MB) 26.99 / 25.21, M=1600 34.73 / 34.25, M=2340 51.20 /
+// 50.37, M=3600 (103 MB) 77.00 / 83.09, but the drafter's logits rows (S=10240) gain nothing
+// there: M=103 25.47 / 24.53, M=128 30.87 / 31.51, M=160 39.18 / 39.38, M=192 47.35 / 46.95,
+// M=204 50.10-50.19 / 51.97-52.23 on two boxes.  (At S=896 the pair's push leaves 32 of each
+// 256 lanes idle, 224 fragments to a row.)  So the limit stays at 32 MiB.
 #ifndef ARNORM_GATHER_STEP_MAX_BYTES
 #define ARNORM_GATHER_STEP_MAX_BYTES (32u << 20)
 #endif
@@ -300,9 +305,12 @@ uint32_t gather_step_delay(uint64_t bytes) {
 // 16 / 24 / 32 steps: M=74 10.17 / 9.78 / 9.12 / 8.94, M=75 - / 7.86 / 8.01 / 8.23, M=80 10.14
 // / 8.18 / 8.37 / 8.61, M=96 11.15 / 9.48 / 9.63 / 9.85, M=128 13.11 / 12.22 / 12.39 / 12.60,
 // M=160 - / 15.12 / 15.00 / 15.12, M=224 - / 19.45 / 19.50 / 19.62, M=292 - / 23.54 / 23.59 /
-// 23.76 (M=74 is slower than its neighbours at every delay).
+// 23.76 (M=74 is slower than its neighbours at every delay).  Above 32 MiB (M=293), three
+// launches / one launch with 16 steps, medians of 3: M=300 27.19 / 24.32, M=400 33.92 /
+// 30.53, M=600 (68.8 MB) 49.06 / 45.79, M=1000 (115 MB) 75.97 / 78.02; the limit sits at 64
+// MiB (M=585 at TP=8), below that loss.
 #ifndef ARNORM_TWOSHOT_STEP_MAX_BYTES
-#define ARNORM_TWOSHOT_STEP_MAX_BYTES (32u << 20)
+#define ARNORM_TWOSHOT_STEP_MAX_BYTES (64u << 20)
 #endif
 #ifndef ARNORM_TWOSHOT_STEP_POLL_DELAY
 #define ARNORM_TWOSHOT_STEP_POLL_DELAY 10
