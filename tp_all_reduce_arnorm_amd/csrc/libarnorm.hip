@@ -830,11 +830,11 @@ int gather_push(const int32_t *shard, int32_t *mailbox, int tp, int cap, int S, 
   if (rank < 0 || nslots < 1 || rank + nslots > tp) return ARNORM_BAD_ARG;
   if (!aligned16(shard) || !aligned16(mailbox)) return ARNORM_BAD_ARG;
   const uint32_t frags = (uint32_t)S / 4;
-  const uint32_t chunks = (frags + 255) / 256;
-  if ((uint64_t)chunks * M * nslots >= (uint64_t(1) << 31)) return ARNORM_NOT_SERVED;
-  return launch(arn::gather_push_kernel<kPolPush>, dim3(chunks * (unsigned)M * (unsigned)nslots), dim3(256), stream,
-                reinterpret_cast<const u32x4 *>(shard), reinterpret_cast<uint8_t *>(mailbox), frags, (uint32_t)M,
-                (uint32_t)tp * S * 4u, (uint32_t)rank * S * 4u, chunks);
+  const uint64_t n = (uint64_t)M * frags;  // one slot's fragments
+  if (n > 0xFFFFFF00u) return ARNORM_NOT_SERVED;  // a grid row of at most 2^32 - 256 threads
+  return launch(arn::gather_push_kernel<kPolPush>, dim3((uint32_t)((n + 255) / 256), (uint32_t)nslots), dim3(256),
+                stream, reinterpret_cast<const u32x4 *>(shard), reinterpret_cast<uint8_t *>(mailbox), frags,
+                (uint32_t)n, (uint32_t)tp * S * 4u, (uint32_t)rank * S * 4u);
 }
 
 int gather_poll(int32_t *mailbox, int32_t *out, int tp, int cap, int S, int M, int copy, hipStream_t stream) {
