@@ -150,6 +150,8 @@ def test_gather_checks(L):
     assert L.gather_push(FAKE, FAKE, 8, 64, 896, 0, 1, 65, None) == 1
     assert L.gather_push(FAKE, FAKE, 8, 64, 896, 7, 2, 32, None) == 2
     assert L.gather_push(MIS, FAKE, 8, 64, 896, 0, 1, 32, None) == 2
+    # one slot's shard rows above 2^32 - 256 fragments (2^24 + 1 rows of 256): refused before any launch
+    assert L.gather_push(FAKE, FAKE, 2, (1 << 24) + 1, 1024, 0, 1, (1 << 24) + 1, None) == 1
     assert L.gather_poll(FAKE, None, 8, 64, 896, 32, 1, None) == 2  # copy needs out
     assert L.gather_poll(FAKE, FAKE, 8, 64, 896, 32, 1, None) == 2  # out aliases mailbox
     assert L.gather_poll(FAKE, None, 8, 64, 896, 0, 0, None) == 1
