@@ -219,7 +219,8 @@ std::atomic<int> g_poll_mode{0};   // Gather polls: 0 = automatic, 1 = re-read a
 // 38.61-38.64, M=1024 (6144) 47.79 / 42.96 and 41.98 / 42.71 on two boxes; TP=2, 4 M
 // workgroups: M=513 13.62 / 15.58, M=1024 24.52 / 26.12).  Consumers that watch one witness
 // per wave instead of re-reading every slot left that loss as it was (TP=8 M=640 53.24, M=1024
-// 90.62).  From about M=100 at TP=8 the grid is larger than what the GPU holds at once,
+// 90.62).  The workgroup count stands in for an edge it does not cause: producers of 4
+// fragments per thread (TP=8: 6 M workgroups) lost from the same M=640 (54.09 against 49.82).  From about M=100 at TP=8 the grid is larger than what the GPU holds at once,
 // which the dispatch order allows (producers wait on nothing, and a row's consumers come in
 // one block).
 #ifndef ARNORM_STEP_MAX_BYTES
@@ -618,7 +619,7 @@ int push_reduce_norm_launch(const uint16_t *partials, const uint16_t *residual, 
                             int tp, int cap, int parity, int M, float eps, hipStream_t stream) {
   // One launch where its consumers, re-reading every slot on each poll pass after the
   // delay below, beat the pair (see ARNORM_STEP_MAX_BYTES).  Rows split 7 ways beat 14 (M=4:
-  // 4.8 against 5.3 us) and one workgroup per row (6.5 us).
+  // 3.80-3.82 against 3.96 us) and one workgroup per row (4.98 us, 4.70 at M=1 against 3.71).
   int K = nbox != nullptr ? reduce_split(M, true) : 1;
   // the automatic split takes whole rows above ARNORM_SPLIT4_MAX_M (the pair's crossover);
   // the one launch keeps rows split 4 ways up to ARNORM_STEP_SPLIT4_MAX_M, then 2 ways up to
