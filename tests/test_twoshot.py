@@ -192,11 +192,12 @@ def test_one_call_workloads(lib, name, calls):
 
 @pytest.mark.parametrize("tp,m", [(2, 13), (3, 13), (4, 13), (5, 13), (6, 9), (7, 9), (8, 9), (8, 13), (8, 1),
                                   (8, 6), (8, 7), (8, 8), (8, 73), (8, 74), (8, 292), (8, 293),
-                                  (8, 585), (8, 586)])
+                                  (8, 585), (8, 586), (4, 1170), (4, 1171), (2, 2340), (2, 2341)])
 def test_one_call_torture(lib, tp, m):
     """Torture rows through the one call, one launch where the TP slots of rows < M fit
-    64 MiB (at TP=8 M=585 is the last row count within it, M=586 the first above; M=292 and
-    293 straddle its former limit of 32 MiB, M=73 and 74 the one of 8 MiB), with the
+    64 MiB (at TP=8 M=585 is the last row count within it, M=586 the first above, at TP=4
+    1170 / 1171, at TP=2 2340 / 2341; M=292 and 293 straddle its former limit of 32 MiB, M=73
+    and 74 the one of 8 MiB), with the
     other parity published and left untouched.  The one launch pads its producer groups to
     multiples of 8 workgroups from 24 per slot: TP=2..5 at M=13 and TP=8 at M=7, 8 and 13
     take the padded layout, TP=8 at M=6 the largest unpadded one, and M=9 and 73 (32 and 256
